@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Throughput of one zero-bubble pipeline stage's hot path on one MI355X.
+
+A step is one whole schedule: every emulated stage's F, B and W passes for
+every microbatch (ZB-H1 order by default), run through zb_run_schedule on one
+stream, then the step boundary (zb_grad_flush) of every stage.  Inputs,
+weights and gradient buffers are resident in HBM before timing starts.
+
+Reported value: stage F+B+W TFLOP/s = algorithmic GEMM (+ attention) FLOPs of
+the step / wall time.  Also reported: % of the bf16 dense MFMA peak, the
+split-backward overhead against the same step in 1F1B order with unsplit
+backwards, the dominant kernel's roofline and the fp64 CPU oracle's rate on a
+bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--order zbh1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def gpu_step_flops(w) -> float:
+    per_mb_stage = 3 * w.gemm_flops_per_pass() + w.attn_flops_fwd() + w.attn_flops_bwd()
+    return float(per_mb_stage) * w.n_micro * w.n_stages
+
+
+def cpu_baseline(w, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle (as it stands) on a bounded sample: whole F+B+W units of
+    one stage and one microbatch at full size, repeated until budget_s elapses."""
+    import numpy as np
+    import synthetic_inputs as si
+    from oracle import stage as ost
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    ws = ost.to64(si.stage_weights(w, 0))
+    x = si.stage_input(w, 0).astype(np.float64)
+    dy = si.last_stage_grad(w, 0).astype(np.float64)
+    units = 0
+    t0 = time.perf_counter()
+    while True:
+        _, saved = ost.stage_forward(w, ws, x)
+        _, grads = ost.stage_backward_input(w, ws, saved, dy)
+        ost.stage_backward_weight(w, saved, grads)
+        units += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or units >= 8:
+            break
+    flops = units * (3 * w.gemm_flops_per_pass() + w.attn_flops_fwd() + w.attn_flops_bwd())
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{units} x (F+B+W of one stage, one microbatch, {w.n_layers} layers) at full size, fp64 numpy, "
+                      f"{el:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gpt_mlp_h2048")
+    ap.add_argument("--order", default=None)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-fused", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py: this build measures one GPU's share of the pipeline only; --gpus {a.gpus} is not "
+              f"supported (stages are emulated on one device).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import split_backward_gemms_amd as zb
+    import synthetic_inputs as si
+    from split_backward_gemms_amd.pipeline import EmulatedPipeline, upload
+
+    w = si.WORKLOADS[a.workload]
+    order = a.order or w.order
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"workload {w.name}: P={w.n_stages} m={w.n_micro} layers={w.n_layers} h={w.hidden} T={w.tokens} {order}")
+    t0 = time.perf_counter()
+    ws = [si.stage_weights(w, s) for s in range(w.n_stages)]
+    xs = [si.stage_input(w, j) for j in range(w.n_micro)]
+    dys = [si.last_stage_grad(w, j) for j in range(w.n_micro)]
+    log(f"inputs drawn in {time.perf_counter() - t0:.1f} s")
+
+    ops, sim = zb.zb_schedule_build(order, w.n_stages, w.n_micro)
+    ops_fused, sim_fused = zb.zb_schedule_build("1f1b", w.n_stages, w.n_micro)
+    pipe = EmulatedPipeline(w, ws, ops=None, device=dev)
+    del ws
+    X = [upload(x, w.dtype, dev) for x in xs]
+    DY = [upload(d, w.dtype, dev) for d in dys]
+    y, dx = pipe.io_buffers()
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"device ready: workspace {pipe.workspace_bytes() / 2**30:.2f} GiB")
+
+    def step(o):
+        pipe.run(o, X, DY, y, dx)
+
+    for _ in range(a.warmup):
+        step(ops)
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step(ops)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1000.0 * wall / a.steps
+    flops = gpu_step_flops(w)
+    tflops = flops / (ms_per_step / 1000.0) / 1e12
+    log(f"{order}: {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s")
+
+    # per-pass device times (hipEvent pair per pass) of one more step in each order
+    tr, _ = pipe.run(ops, X, DY, y, dx, trace=True)
+    t_split = {k: sum(ms for (op, ms, _) in tr if op[1] == k) for k in "FBW"}
+    fused = {}
+    if not a.no_fused:
+        for _ in range(a.warmup):
+            step(ops_fused)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(a.steps):
+            step(ops_fused)
+        torch.cuda.synchronize()
+        fused_ms = 1000.0 * (time.perf_counter() - t0) / a.steps
+        trf, _ = pipe.run(ops_fused, X, DY, y, dx, trace=True)
+        t_f = {k: sum(ms for (op, ms, _) in trf if op[1] == k) for k in "FU"}
+        fused = {"ms_per_step_1f1b_unsplit": fused_ms,
+                 "split_overhead_pass": (t_split["B"] + t_split["W"]) / t_f["U"] - 1.0,
+                 "split_overhead_wall": ms_per_step / fused_ms - 1.0,
+                 "pass_ms_1f1b": {"F": t_f["F"], "U": t_f["U"]}}
+        log(f"1f1b unsplit: {fused_ms:.3f} ms/step; split overhead (B+W vs U) "
+            f"{100 * fused['split_overhead_pass']:.2f}%")
+
+    # kernel-level timing over one more profiled step of the measured order
+    zb.zb_prof_reset()
+    zb.zb_prof_enable(True)
+    prof_steps = max(1, min(a.steps, 3))
+    for _ in range(prof_steps):
+        step(ops)
+    torch.cuda.synchronize()
+    zb.zb_prof_enable(False)
+    kern = zb.zb_prof_read()
+    zb.zb_prof_reset()
+    kern.sort(key=lambda r: -r["total_ms"])
+    for r in kern[:8]:
+        log(f"  {r['name']:<28} {r['launches']:6d} launches {r['total_ms'] / prof_steps:8.3f} ms/step "
+            f"{r['flops'] / r['total_ms'] / 1e9:8.1f} TFLOP/s")
+    gemm_ms = sum(r["total_ms"] for r in kern if r["name"].startswith("gemm")) / prof_steps
+    gemm_flops = sum(r["flops"] for r in kern if r["name"].startswith("gemm")) / prof_steps
+    top = kern[0]
+    avg_ms = top["total_ms"] / top["launches"]
+    per_launch_flops = top["flops"] / top["launches"]
+    achieved = per_launch_flops / (avg_ms / 1e3) / 1e12
+    roofline = {"bound": "mfma", "kernel": top["name"], "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "avg_launch_us": avg_ms * 1e3, "flops_per_launch": per_launch_flops}
+
+    pipe.close()
+    out = {
+        "metric": "stage F+B+W TFLOP/s",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "stages_emulated": w.n_stages, "n_micro": w.n_micro,
+                   "layers_per_stage": w.n_layers, "hidden": w.hidden, "ffn": w.ffn, "seq": w.seq,
+                   "micro_batch": w.micro_batch, "order": order, "flops_per_step": flops},
+        "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "gemm_only_tflops": gemm_flops / (gemm_ms / 1e3) / 1e12 if gemm_ms > 0 else None,
+        "pass_ms": t_split,
+        "sim_bubble_unit_times": {order: sim["bubble"], "1f1b": sim_fused["bubble"]},
+        "roofline": roofline,
+    }
+    out.update(fused)
+    if not a.no_cpu:
+        log("timing the CPU oracle sample ...")
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

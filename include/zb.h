@@ -1,0 +1,342 @@
+/*
+ * zb.h -- C ABI of one zero-bubble pipeline stage on an MI355X (gfx950).
+ *
+ * One pipeline stage holds n_layers layers.  Its three passes follow the split
+ * of the backward pass in "Zero Bubble Pipeline Parallelism" (structured summary
+ * of arXiv 2401.10241), section 3, "The Backward Pass Decomposition: B and W",
+ * and the tutorial "Pipeline Schedules: GPipe, 1F1B and Zero Bubble", section
+ * "Zero bubble: split the backward pass":
+ *
+ *   F  forward:          Y  = X . W        per linear (+ GeLU, attention, residual)
+ *   B  input gradient:   dX = dY . W^T     per linear, layers in reverse
+ *   W  weight gradient:  dW += X^T . dY    per linear, fp32, summed over microbatches
+ *
+ * B of stage s for microbatch j needs F(s,j) and B(s+1,j); W(s,j) needs only
+ * B(s,j); the optimizer step needs every W of the step ("Zero-Bubble Pipeline
+ * Parallelism, Proven", section "Draw the event graph before the Gantt").
+ *
+ * Conventions
+ *  - Every tensor is row-major.  Activations are [T, width] with T = seq *
+ *    micro_batch tokens; weight W of a linear K -> N is [K, N] (Y = X . W).
+ *    Its gradient buffer dW is fp32 [K, N].
+ *  - bf16 mode stores weights and activations as bfloat16 and accumulates in
+ *    fp32; fp32 mode stores fp32.  Weight gradients are always fp32.
+ *  - Linears of one layer, in order: TINY_MLP {up, down}; MLP_LINEARS and
+ *    FULL {qkv, proj, up, down} with qkv: h -> 3h (Q | K | V column blocks,
+ *    head-major inside each), proj: h -> h, up: h -> ffn, down: ffn -> h.
+ *  - Device pointers are plain device addresses (hipMalloc'd or torch
+ *    tensors); host pointers are marked "host".  The caller owns every
+ *    buffer it passes: weights, gradient buffers, inputs, outputs and the
+ *    workspace.  The library never allocates device memory.
+ *  - Work is enqueued asynchronously on the stream given at creation, in call
+ *    order.  Inputs must stay valid until the work that reads them has run on
+ *    that stream.
+ *  - On any error the call changes no state and enqueues no work; the text of
+ *    the last error of the calling thread is returned by zb_last_error().
+ *    Device faults surface as ZB_E_HIP at the next call that synchronises.
+ *  - Shapes: hidden, ffn and seq*micro_batch must be multiples of 8; FULL needs
+ *    hidden / n_heads == 128.
+ */
+#ifndef ZB_H
+#define ZB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ZB_OK = 0,
+  ZB_E_ARG = 1,            /* bad argument (null pointer, bad size, bad kind)      */
+  ZB_E_STATE = 2,          /* pass called out of F -> B -> W order for (stage, mb) */
+  ZB_E_DUPLICATE = 3,      /* a pass repeated in a schedule / duplicate event id   */
+  ZB_E_INVALID_STAGE = 4,  /* stage index outside [0, P)                           */
+  ZB_E_INVALID_MB = 5,     /* microbatch index outside [0, m)                      */
+  ZB_E_MISSING = 6,        /* flush before every W ran / pass or dependency absent */
+  ZB_E_DEPENDENCY = 7,     /* a pass placed before one it depends on               */
+  ZB_E_BUDGET = 8,         /* workspace too small for the planned live tensors     */
+  ZB_E_HIP = 9,            /* HIP runtime error                                    */
+  ZB_E_UNSUPPORTED = 10,   /* shape or mode this build does not implement          */
+  ZB_E_DEADLOCK = 11,      /* per-stage orders that can never all complete        */
+  ZB_E_INTERVAL = 12,      /* timed event with end <= start or start < 0           */
+  ZB_E_OVERLAP = 13        /* two timed events of one stage overlap                */
+} zb_status;
+
+enum { ZB_KIND_TINY_MLP = 0, ZB_KIND_MLP_LINEARS = 1, ZB_KIND_FULL = 2 };
+enum { ZB_DTYPE_BF16 = 0, ZB_DTYPE_FP32 = 1 };
+enum { ZB_GELU_ERF = 0, ZB_GELU_TANH = 1 };
+enum { ZB_ORDER_GPIPE = 0, ZB_ORDER_1F1B = 1, ZB_ORDER_ZBH1 = 2, ZB_ORDER_ZBH2 = 3,
+       ZB_ORDER_WLAST = 4 };
+
+/* Shape of one stage.  MLP_LINEARS routes the V columns of qkv straight to
+ * proj (attention replaced by the identity); FULL uses causal softmax attention
+ * and residual adds around the attention and MLP blocks. */
+typedef struct {
+  int kind;         /* ZB_KIND_*                                   */
+  int dtype;        /* ZB_DTYPE_*                                  */
+  int n_layers;
+  int hidden;       /* h                                           */
+  int ffn;          /* f (4h in the GPT shapes)                    */
+  int n_heads;      /* FULL only                                   */
+  int seq;          /* tokens per sequence                         */
+  int micro_batch;  /* sequences per microbatch                    */
+  int n_micro;      /* m, microbatches per step                    */
+  int gelu;         /* ZB_GELU_*                                   */
+} zb_stage_desc;
+
+/* One pass of a schedule.  kind: 'F', 'B', 'W', or 'U' = unsplit backward
+ * (B and W of (stage, mb) as one pass, the conventional backward). */
+typedef struct {
+  int32_t stage;
+  int32_t mb;
+  char kind;
+  char pad_[3];
+} zb_op;
+
+/* ------------------------------------------------------------------------
+ * Schedule layer (host only, no GPU needed).
+ * Zero Bubble Pipeline Parallelism, section 3: handcrafted ZB-H1 / ZB-H2,
+ * "The Memory Model", ILP appendix Eq. 3-7; tutorial sections "1F1B" and
+ * "Interleaved stages"; audit section "Validate the schedule as data".
+ * ---------------------------------------------------------------------- */
+
+/* Statistics of a simulated schedule (integer time units). */
+typedef struct {
+  int64_t makespan;  /* max over stages of (end of last pass - start of first pass), Eq. 3 */
+  int64_t span;      /* latest end over all passes (all stages start at t = 0)            */
+  int64_t busy;      /* sum of pass durations                                             */
+  int64_t ideal;     /* m * (T_F + T_B + T_W) per stage                                   */
+  int64_t bubble;    /* makespan - ideal                                                  */
+} zb_sim_stats;
+
+/* Pass order of stage `stage` (0-indexed) of P under ZB_ORDER_*.  Writes at most
+ * `cap` ops to out (host) and their count to *n_out (host).  GPIPE and 1F1B emit
+ * unsplit 'U' backwards; ZBH1, ZBH2 and WLAST emit split 'B' and 'W' with the W's
+ * of a stage in ascending microbatch order.  ZBH2 needs m >= 2P - 1.
+ * Errors: ZB_E_ARG (P < 1, m < 1, bad order, cap too small), ZB_E_INVALID_STAGE. */
+zb_status zb_schedule_stage_order(int order, int P, int m, int stage,
+                                  zb_op* out, int cap, int* n_out);
+
+/* As-soon-as-possible simulation of per-stage orders.  `ops` (host, n_ops) holds
+ * the passes of every stage; the passes of one stage run in the order they
+ * appear.  times[3] (host) = {T_F, T_B, T_W} >= 1; an unsplit pass lasts
+ * T_B + T_W.  A pass starts once its stage is free and its producers have
+ * ended (+ t_comm across stages).  Outputs (host, may be NULL): linear_out[n_ops]
+ * the one-device order (by simulated start, ties to the lower stage, then the
+ * stage's own order), start_out/end_out[n_ops] aligned with linear_out, stats.
+ * Errors: ZB_E_ARG, ZB_E_INVALID_STAGE, ZB_E_INVALID_MB, ZB_E_DEADLOCK. */
+zb_status zb_schedule_simulate(int P, int m, const zb_op* ops, int n_ops,
+                               const int64_t* times, int64_t t_comm,
+                               zb_op* linear_out, int64_t* start_out, int64_t* end_out,
+                               zb_sim_stats* stats);
+
+/* Generate every stage's order, simulate it and linearize it in one call.
+ * linear_out (host) needs cap >= 3*P*m (2*P*m for GPIPE / 1F1B). */
+zb_status zb_schedule_build(int order, int P, int m, const int64_t* times, int64_t t_comm,
+                            zb_op* linear_out, int cap, int* n_out, zb_sim_stats* stats);
+
+/* Interleaved pipeline with v chunks per device (simulation only): forwards
+ * group by group of P microbatches over chunks 0..v-1, unsplit backwards over
+ * chunks v-1..0.  times are per chunk.  Needs m % P == 0. */
+zb_status zb_schedule_simulate_interleaved(int P, int m, int v, const int64_t* times,
+                                           zb_sim_stats* stats);
+
+/* Validate a one-device execution order (host ops).  Pass by pass, first
+ * failure wins: kind not F/B/W/U -> ZB_E_ARG; stage outside [0,P) ->
+ * ZB_E_INVALID_STAGE; mb outside [0,m) -> ZB_E_INVALID_MB; repeated pass, or
+ * U mixed with B/W of the same (stage, mb) -> ZB_E_DUPLICATE; F(s,j) before
+ * F(s-1,j), B|U(s,j) before F(s,j) or before B|U(s+1,j), W(s,j) before B(s,j)
+ * -> ZB_E_DEPENDENCY.  Then every (s,j) must have F and B+W or U, else
+ * ZB_E_MISSING with *bad_index = n_ops.  *bad_index (host) = -1 on success. */
+zb_status zb_schedule_validate(int P, int m, const zb_op* ops, int n_ops, int* bad_index);
+
+/* Running activation memory of stage `stage` in `ops` (host): F adds m_b, B adds
+ * m_w - m_b, W adds -m_w, U adds -m_b, each at the start of its pass ("The
+ * Memory Model").  *peak (host) = the maximum level (>= 0). */
+zb_status zb_schedule_peak_memory(const zb_op* ops, int n_ops, int stage,
+                                  int64_t m_b, int64_t m_w, int64_t* peak);
+
+/* Timed event of a schedule, for zb_events_inspect (the audit's checker). */
+typedef struct {
+  int32_t id;
+  int32_t stage;
+  int32_t micro;
+  char kind;            /* 'F', 'B', 'W' (others allowed, ignored by the live count) */
+  char pad_[3];
+  double start;
+  double end;
+  int32_t n_deps;
+  const int32_t* deps;  /* host array of n_deps event ids */
+} zb_event;
+
+typedef struct {
+  double span;               /* latest end                                   */
+  double busy;               /* sum of (end - start)                         */
+  double bubble_ratio;       /* 1 - busy / (stage_count * span)              */
+  int64_t unfinished_activations;  /* per microbatch: F count minus released by B */
+} zb_event_report;
+
+/* Checks timed events (host).  Rejects in this order: stage_count < 2 ->
+ * ZB_E_ARG; a repeated id -> ZB_E_DUPLICATE; then event by event: stage
+ * outside [0, stage_count) -> ZB_E_INVALID_STAGE, start < 0 or end <= start
+ * -> ZB_E_INTERVAL, a dependency id absent -> ZB_E_MISSING, a dependency
+ * ending after the event starts -> ZB_E_DEPENDENCY; then two events of one
+ * stage that overlap -> ZB_E_OVERLAP.  *bad_index (host, may be NULL) names
+ * the offending event (-1 if none). */
+zb_status zb_events_inspect(const zb_event* events, int n, int stage_count,
+                            zb_event_report* report, int* bad_index);
+
+/* ------------------------------------------------------------------------
+ * Stage objects (GPU).
+ * ---------------------------------------------------------------------- */
+
+typedef struct zb_stage zb_stage;
+
+/* Create stage number `stage_index` (0-indexed; used to match schedule ops).
+ * weights (host array of n_layers * n_linears device pointers, [layer][linear])
+ * point at bf16 or fp32 [K, N] weights; dw (host array, same count) at fp32
+ * [K, N] gradient buffers.  Both stay owned by the caller and must outlive the
+ * stage.  stream: a hipStream_t (NULL = default stream).
+ * Errors: ZB_E_ARG, ZB_E_UNSUPPORTED (shape not a multiple of 8, FULL with
+ * head_dim != 128, fp32 with FULL). */
+zb_status zb_stage_create(const zb_stage_desc* desc, int stage_index,
+                          const void* const* weights, float* const* dw,
+                          void* stream, zb_stage** out);
+
+/* Bytes of the per-microbatch tensor classes of a stage (host outputs):
+ * fw = live from F to W (layer inputs and what W reads), fb = live from F to B
+ * (what only B reads), bw = live from B to W (every linear's output gradient).
+ * fw + fb is this build's M_B, fw + bw its M_W. */
+zb_status zb_stage_class_bytes(const zb_stage* st, size_t* fw, size_t* fb, size_t* bw);
+
+/* Workspace the stage needs to run `ops` (host, the whole one-device order of
+ * all stages; NULL = every microbatch live at once).  Slots of each class are
+ * counted by replaying allocations: the input of F(s,j) is claimed when
+ * F(s-1,j) runs (or F(s,j) itself on the first stage), freed by W|U(s,j); the
+ * F->B tensors live from F(s,j) to B|U(s,j); the gradient entering B(s,j) is
+ * claimed when B(s+1,j) runs (or B|U(s,j) on the last stage), freed by
+ * W|U(s,j).  The plan is remembered by the stage for zb_stage_bind_workspace.
+ * *bytes (host) receives the size. */
+zb_status zb_stage_workspace_bytes(zb_stage* st, const zb_op* ops, int n_ops, size_t* bytes);
+
+/* Hand the stage a device buffer of at least the planned size (256-byte
+ * aligned).  The stage sub-allocates its stash from it; the caller keeps
+ * ownership.  Only allowed while no microbatch is live.
+ * Errors: ZB_E_ARG (null, misaligned), ZB_E_BUDGET (too small), ZB_E_STATE. */
+zb_status zb_stage_bind_workspace(zb_stage* st, void* dev_ptr, size_t bytes);
+
+/* Device address of the stage's input slot for microbatch mb (claimed on
+ * first use): writing stage input there makes zb_forward's copy a no-op. */
+zb_status zb_stage_input_slot(zb_stage* st, int mb, void** dev_ptr);
+/* Device address of the slot holding the gradient that enters B(mb). */
+zb_status zb_stage_grad_slot(zb_stage* st, int mb, void** dev_ptr);
+
+/* F of microbatch mb: x (device, [T, h]) is copied into the input slot (unless
+ * it is that slot), the layers run, y (device, [T, h]) receives the stage
+ * output.  Needs mb not yet forwarded this step.  Errors: ZB_E_INVALID_MB,
+ * ZB_E_STATE, ZB_E_BUDGET (no free slot), ZB_E_HIP. */
+zb_status zb_forward(zb_stage* st, int mb, const void* x, void* y);
+
+/* B of microbatch mb: dy (device, [T, h]) is the gradient of the stage output
+ * (copied into the gradient slot unless it is that slot); dx (device, [T, h])
+ * receives the gradient of the stage input -- the value handed upstream.
+ * Frees the F->B tensors and keeps every linear's output gradient for W.
+ * Needs F(mb) done and B(mb) not.  Errors as zb_forward. */
+zb_status zb_backward_input(zb_stage* st, int mb, const void* dy, void* dx);
+
+/* W of microbatch mb: dW += X^T . dY for every linear, accumulated in fp32 in
+ * the caller's gradient buffers.  The first W of a step overwrites dW instead
+ * of adding (the buffers need no zeroing).  Frees the microbatch's tensors.
+ * Needs B(mb) done.  Errors: ZB_E_INVALID_MB, ZB_E_STATE, ZB_E_HIP. */
+zb_status zb_backward_weight(zb_stage* st, int mb);
+
+/* Unsplit backward (B and W of mb as one pass, each linear's input gradient
+ * and weight gradient back to back): the fused baseline.  Same kernels and
+ * the same bits as B followed by W. */
+zb_status zb_backward_unsplit(zb_stage* st, int mb, const void* dy, void* dx);
+
+/* Step boundary (the optimizer dependency): requires W (or U) of every
+ * microbatch of the step, else ZB_E_MISSING.  If nonfinite_out (host) is not
+ * NULL, synchronises the stream and stores 1 if any dW holds a NaN or Inf, else
+ * 0.  Afterwards the gradient buffers hold the step's full sum until the first
+ * W of the next step overwrites them, and every microbatch may be forwarded
+ * again. */
+zb_status zb_grad_flush(zb_stage* st, int* nonfinite_out);
+
+/* Per-pass record filled by zb_run_schedule when trace != NULL. */
+typedef struct {
+  zb_op op;
+  float ms;      /* device time of the pass (hipEvent pair)          */
+  float t0_ms;   /* start, relative to the first pass's start event  */
+} zb_trace_rec;
+
+/* Run a one-device order over P stages (host array stages[P], all on one
+ * stream, stage_index p at stages[p]).  The whole list is validated
+ * (zb_schedule_validate rules) and every stage's workspace plan checked before
+ * anything is launched.  x0[mb], dy_last[mb], y_last[mb], dx0[mb] (host arrays
+ * of m device pointers, [T, h] each) are the first stage's inputs, the last
+ * stage's output gradients, the last stage's outputs and the first stage's
+ * input gradients.  Stage s's output is written straight into stage s+1's
+ * input slot and stage s+1's dx into stage s's gradient slot.  trace (host,
+ * n_ops records, may be NULL) receives per-pass device times, which
+ * synchronises the stream at the end.  Does not flush. */
+zb_status zb_run_schedule(zb_stage* const* stages, int P, const zb_op* ops, int n_ops,
+                          const void* const* x0, const void* const* dy_last,
+                          void* const* y_last, void* const* dx0, zb_trace_rec* trace);
+
+/* Text of the calling thread's last error ("" if none); names the first
+ * violating op index for schedule errors. */
+const char* zb_last_error(void);
+
+/* Release the stage object (not the caller's buffers).  Enqueued work must have
+ * finished. */
+void zb_stage_destroy(zb_stage* st);
+
+/* ------------------------------------------------------------------------
+ * One linear layer's three passes, the per-linear definitions of the tutorial
+ * "Pipeline Schedules: GPipe, 1F1B and Zero Bubble", section "Zero bubble:
+ * split the backward pass", run by the same kernels the stage uses.
+ * x, dy, y, dx, w (device) are row-major bf16 (dtype ZB_DTYPE_BF16) or fp32;
+ * dw (device) is fp32 [K, N].  Asynchronous on stream (hipStream_t or NULL).
+ * Errors: ZB_E_ARG (null pointer, negative size), ZB_E_UNSUPPORTED (bf16
+ * with K, N or T not a multiple of 8, or a pointer not 16-byte aligned).
+ * ---------------------------------------------------------------------- */
+
+/* F: y[T, N] = x[T, K] . w[K, N] */
+zb_status zb_linear_forward(int dtype, int T, int K, int N, const void* x, const void* w, void* y,
+                            void* stream);
+/* B: dx[T, K] = dy[T, N] . w[K, N]^T */
+zb_status zb_linear_backward_input(int dtype, int T, int K, int N, const void* dy, const void* w, void* dx,
+                                   void* stream);
+/* W: dw[K, N] = (accumulate ? dw : 0) + x[T, K]^T . dy[T, N], the fp32 sum
+ * continuing from the buffer's value inside the same accumulation chain. */
+zb_status zb_linear_backward_weight(int dtype, int T, int K, int N, const void* x, const void* dy, float* dw,
+                                    int accumulate, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Kernel-level timing (measurement).  When enabled, every kernel the library
+ * launches is bracketed by a hipEvent pair on its stream; zb_prof_read
+ * synchronises and returns per-kernel totals.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  char name[48];      /* kernel family and tile, e.g. "gemm_w_256x256"   */
+  int64_t launches;
+  double total_ms;
+  double flops;       /* algorithmic FLOPs summed over launches          */
+  double bytes;       /* algorithmic HBM bytes summed over launches      */
+} zb_prof_rec;
+
+void zb_prof_enable(int on);
+void zb_prof_reset(void);
+/* Writes up to cap records (host) and the number of distinct kernels to *n. */
+zb_status zb_prof_read(zb_prof_rec* out, int cap, int* n);
+
+/* Version string of the library build. */
+const char* zb_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZB_H */

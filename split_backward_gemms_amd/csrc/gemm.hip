@@ -1,0 +1,542 @@
+// Dense contractions of a stage: the F, B and W GEMMs with fused epilogues.
+//
+//   F  Y[T,N]  = X[T,K] . W[K,N]            A k-contiguous, B n-contiguous
+//   B  dX[T,K] = dY[T,N] . W[K,N]^T         A and B k-contiguous
+//   W  dW[K,N] += X[T,K]^T . dY[T,N]        A m-contiguous, B n-contiguous (reduce over T)
+//
+// (B/W split of the backward pass: "Zero Bubble Pipeline Parallelism",
+// section 3, "The Backward Pass Decomposition"; the three products as the
+// tutorial "Pipeline Schedules: GPipe, 1F1B and Zero Bubble" writes them in
+// "Zero bubble: split the backward pass".)
+//
+// bf16 path: 256 threads = 4 waves of 64 in a 2x2 grid; each wave owns a
+// (BM/2)x(BN/2) block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, fp32
+// accumulators).  K advances 64 at a time through two LDS buffers: the next
+// tile is fetched into registers while the current one feeds the MFMAs.  In
+// LDS every tile is stored k-contiguous ([row][64]) with its 16-byte chunks
+// XOR-swizzled by (row ^ row>>3) & 7, so both the MFMA operand reads and the
+// transposing writes of m/n-contiguous operands are free of bank conflicts.
+// m/n-contiguous operands (W's X and dY, F's weight) are loaded as 8x8 (or
+// 4x8) bf16 blocks with 16-byte global loads and transposed in registers.
+//
+// The W epilogue is fused: the accumulators start from the fp32 gradient
+// buffer (or from zero for the first W of a step) and the MFMA chain simply
+// continues, so W of microbatches j, j+1, ... run in any slot give the same
+// bits as long as they are applied in the same order.  No split-K, no atomics.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+
+#include "zb_internal.h"
+
+namespace zb {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int BKT = 64;   // K per LDS tile
+constexpr int NT = 256;   // threads per workgroup
+constexpr int XCDS = 8;   // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
+
+struct Params {
+  int M, N, K;
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  void* C;
+  int64_t ldc;
+  const void* R;
+  int64_t ldr;
+  void* Z;
+  int64_t ldz;
+  int beta;
+  int gelu;
+  int nbm, nbn;
+};
+
+// ------------------------------------------------------------- elementwise math
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // keep NaN quiet
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);                 // nearest even
+}
+
+__device__ __forceinline__ float gelu_f(float z, int kind) {
+  if (kind == ZB_GELU_TANH) {
+    const float c = 0.7978845608028654f;  // sqrt(2/pi)
+    float u = c * (z + 0.044715f * z * z * z);
+    return 0.5f * z * (1.0f + tanhf(u));
+  }
+  return 0.5f * z * (1.0f + erff(z * 0.7071067811865476f));
+}
+
+__device__ __forceinline__ float gelu_grad_f(float z, int kind) {
+  if (kind == ZB_GELU_TANH) {
+    const float c = 0.7978845608028654f;
+    float u = c * (z + 0.044715f * z * z * z);
+    float t = tanhf(u);
+    return 0.5f * (1.0f + t) + 0.5f * z * (1.0f - t * t) * c * (1.0f + 3.0f * 0.044715f * z * z);
+  }
+  float cdf = 0.5f * (1.0f + erff(z * 0.7071067811865476f));
+  float pdf = 0.3989422804014327f * __expf(-0.5f * z * z);
+  return cdf + z * pdf;
+}
+
+template <typename T>
+__device__ __forceinline__ float ld_elem(const void* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld_elem<uint16_t>(const void* p, int64_t i) {
+  return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+template <>
+__device__ __forceinline__ float ld_elem<float>(const void* p, int64_t i) {
+  return static_cast<const float*>(p)[i];
+}
+template <typename T>
+__device__ __forceinline__ void st_elem(void* p, int64_t i, float v);
+template <>
+__device__ __forceinline__ void st_elem<uint16_t>(void* p, int64_t i, float v) {
+  static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+}
+template <>
+__device__ __forceinline__ void st_elem<float>(void* p, int64_t i, float v) {
+  static_cast<float*>(p)[i] = v;
+}
+
+// Output element (m, n) of the product with value v: the fused epilogue.
+template <typename T, int EPI>
+__device__ __forceinline__ void epi_store(const Params& p, int m, int n, float v) {
+  if constexpr (EPI == EPI_ACC) {
+    static_cast<float*>(p.C)[(int64_t)m * p.ldc + n] = v;
+  } else {
+    if constexpr (EPI == EPI_RESID) v += ld_elem<T>(p.R, (int64_t)m * p.ldr + n);
+    if constexpr (EPI == EPI_GELU) {
+      st_elem<T>(p.Z, (int64_t)m * p.ldz + n, v);
+      v = gelu_f(v, p.gelu);
+    }
+    if constexpr (EPI == EPI_DGELU) v *= gelu_grad_f(ld_elem<T>(p.R, (int64_t)m * p.ldr + n), p.gelu);
+    st_elem<T>(p.C, (int64_t)m * p.ldc + n, v);
+  }
+}
+
+// Workgroup -> output tile.  Consecutive logical tiles share an XCD (its own
+// L2); within the logical order, tiles go in groups of 8 tile-rows so that
+// neighbours reuse A rows and B columns.
+__device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
+  const int nblk = p.nbm * p.nbn;
+  int b = blockIdx.x;
+  if (nblk % XCDS == 0) b = (b % XCDS) * (nblk / XCDS) + b / XCDS;
+  const int G = 8;
+  const int per_group = G * p.nbn;
+  const int group = b / per_group;
+  const int first_m = group * G;
+  const int gsz = min(p.nbm - first_m, G);
+  const int r = b - group * per_group;
+  tm = first_m + r % gsz;
+  tn = r / gsz;
+}
+
+// ------------------------------------------------------------- bf16 MFMA GEMM
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+__device__ __forceinline__ uint32_t half_of(const u32x4& v, int e) {
+  uint32_t w = v[e >> 1];
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// One operand tile of ROWS x 64 (rows = m or n, columns = k) moved global -> regs -> LDS.
+// KCONTIG: element (row, k) at base[row * ld + k]; otherwise at base[k * ld + row].
+// The per-thread base pointer and row validity are fixed at construction; a
+// tile load only adds the k offset.  Rows past rows_lim read as zero; columns
+// past K read as zero only in loads made with CHECK_K (the last, partial tile).
+template <int ROWS, bool KCONTIG>
+struct TileLoader {
+  static constexpr int NREG = ROWS / 32;  // 16-byte registers per thread
+  static constexpr int KR = NREG;         // m/n-contiguous: k rows per thread (8 or 4)
+  static constexpr int MCH = ROWS / 64;   // m/n-contiguous: 64-wide column groups
+  u32x4 r[NREG];
+  const uint16_t* ptr;  // this thread's first element
+  int64_t ld;
+  uint32_t row_ok;      // bit i: register i's row (KCONTIG) / the column block is in range
+  int kofs;             // k of this thread's first element within a tile
+
+  __device__ __forceinline__ TileLoader(const uint16_t* base, int64_t ld_, int row0, int rows_lim, int tid) : ld(ld_) {
+    row_ok = 0;
+    if constexpr (KCONTIG) {
+      const int row = tid >> 3;
+      kofs = (tid & 7) * 8;
+      ptr = base + (int64_t)(row0 + row) * ld + kofs;
+#pragma unroll
+      for (int i = 0; i < NREG; ++i)
+        if (row0 + row + i * (NT / 8) < rows_lim) row_ok |= 1u << i;
+    } else {
+      const int mc = (tid & 7) + 8 * ((tid >> 6) % MCH);
+      const int kg = ((tid >> 3) & 7) + 8 * ((tid >> 6) / MCH);
+      kofs = kg * KR;
+      ptr = base + (int64_t)kofs * ld + row0 + mc * 8;
+      row_ok = (row0 + mc * 8 < rows_lim) ? 0xffffffffu : 0u;
+    }
+  }
+
+  template <bool CHECK_K>
+  __device__ __forceinline__ void load(int k0, int K) {
+    if constexpr (KCONTIG) {
+      const uint16_t* q = ptr + k0;
+#pragma unroll
+      for (int i = 0; i < NREG; ++i) {
+        bool ok = (row_ok >> i) & 1u;
+        if constexpr (CHECK_K) ok = ok && (k0 + kofs < K);
+        r[i] = ok ? *reinterpret_cast<const u32x4*>(q + (int64_t)i * (NT / 8) * ld) : u32x4{0u, 0u, 0u, 0u};
+      }
+    } else {
+      const uint16_t* q = ptr + (int64_t)k0 * ld;
+#pragma unroll
+      for (int i = 0; i < KR; ++i) {
+        bool ok = row_ok & 1u;
+        if constexpr (CHECK_K) ok = ok && (k0 + kofs + i < K);
+        r[i] = ok ? *reinterpret_cast<const u32x4*>(q + (int64_t)i * ld) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint16_t* s, int tid) const {
+    if constexpr (KCONTIG) {
+#pragma unroll
+      for (int i = 0; i < NREG; ++i) {
+        const int row = (tid >> 3) + i * (NT / 8), c = tid & 7;
+        *reinterpret_cast<u32x4*>(s + row * BKT + ((c ^ swz(row)) << 3)) = r[i];
+      }
+    } else {
+      const int mc = (tid & 7) + 8 * ((tid >> 6) % MCH);
+      const int kg = ((tid >> 3) & 7) + 8 * ((tid >> 6) / MCH);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = mc * 8 + e;
+        if constexpr (KR == 8) {
+          u32x4 v;
+          v[0] = half_of(r[0], e) | (half_of(r[1], e) << 16);
+          v[1] = half_of(r[2], e) | (half_of(r[3], e) << 16);
+          v[2] = half_of(r[4], e) | (half_of(r[5], e) << 16);
+          v[3] = half_of(r[6], e) | (half_of(r[7], e) << 16);
+          *reinterpret_cast<u32x4*>(s + row * BKT + ((kg ^ swz(row)) << 3)) = v;
+        } else {
+          u32x2 v;
+          v[0] = half_of(r[0], e) | (half_of(r[1], e) << 16);
+          v[1] = half_of(r[2], e) | (half_of(r[3], e) << 16);
+          *reinterpret_cast<u32x2*>(s + row * BKT + (((kg >> 1) ^ swz(row)) << 3) + 4 * (kg & 1)) = v;
+        }
+      }
+    }
+  }
+};
+
+template <int BM, int BN, bool AK, bool BKC, int EPI>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
+gemm_bf16_mfma(Params p) {
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * BKT];
+
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const uint16_t* __restrict__ Ap = static_cast<const uint16_t*>(p.A);
+  const uint16_t* __restrict__ Bp = static_cast<const uint16_t*>(p.B);
+
+  // Lane (l) of the 32x32 MFMA result holds column l%32 and rows
+  // 8*(r/4) + 4*(l/32) + r%4 for its 16 values r.
+  const int lrow = m0 + wm * WTM + (lane >> 5) * 4;
+  const int lcol = n0 + wn * WTN + (lane & 31);
+  const bool full = (m0 + BM <= p.M) && (n0 + BN <= p.N);
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  if constexpr (EPI == EPI_ACC) {
+    if (p.beta) {
+      const float* Cp = static_cast<const float*>(p.C);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = lrow + i * 32 + (r >> 2) * 8 + (r & 3);
+          const float* row = Cp + (int64_t)m * p.ldc + lcol;
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            if (full || (m < p.M && lcol + j * 32 < p.N)) acc[i][j][r] = row[j * 32];
+        }
+    }
+  }
+
+  TileLoader<BM, AK> la(Ap, p.lda, m0, p.M, tid);
+  TileLoader<BN, BKC> lb(Bp, p.ldb, n0, p.N, tid);
+  const int nk = (p.K + BKT - 1) / BKT;
+  const bool k_ragged = (p.K % BKT) != 0;
+  if (nk > 0) {  // K == 0: empty sum, the epilogue sees the initial accumulators
+    if (nk == 1 && k_ragged) {
+      la.template load<true>(0, p.K);
+      lb.template load<true>(0, p.K);
+    } else {
+      la.template load<false>(0, p.K);
+      lb.template load<false>(0, p.K);
+    }
+    la.store(smem, tid);
+    lb.store(smem + BM * BKT, tid);
+    __syncthreads();
+  }
+
+  for (int kt = 0; kt < nk; ++kt) {
+    uint16_t* cur = smem + (kt & 1) * (BM + BN) * BKT;
+    uint16_t* nxt = smem + ((kt + 1) & 1) * (BM + BN) * BKT;
+    if (kt + 1 < nk) {
+      if (kt + 2 == nk && k_ragged) {
+        la.template load<true>((kt + 1) * BKT, p.K);
+        lb.template load<true>((kt + 1) * BKT, p.K);
+      } else {
+        la.template load<false>((kt + 1) * BKT, p.K);
+        lb.template load<false>((kt + 1) * BKT, p.K);
+      }
+    }
+    const uint16_t* sa = cur;
+    const uint16_t* sb = cur + BM * BKT;
+#pragma unroll
+    for (int kk = 0; kk < BKT / 16; ++kk) {
+      const int chunk = kk * 2 + (lane >> 5);
+      bf16x8 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * WTM + i * 32 + (lane & 31);
+        af[i] = *reinterpret_cast<const bf16x8*>(sa + row * BKT + ((chunk ^ swz(row)) << 3));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int row = wn * WTN + j * 32 + (lane & 31);
+        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + row * BKT + ((chunk ^ swz(row)) << 3));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      la.store(nxt, tid);
+      lb.store(nxt + BM * BKT, tid);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = lrow + i * 32 + (r >> 2) * 8 + (r & 3);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = lcol + j * 32;
+        if (full || (m < p.M && n < p.N)) epi_store<uint16_t, EPI>(p, m, n, acc[i][j][r]);
+      }
+    }
+}
+
+// ------------------------------------------------- fp32 storage (plain FMA tiles)
+
+template <typename T, int EPI>
+__global__ void __launch_bounds__(256) gemm_simt(Params p, int ak, int bk) {
+  constexpr int TB = 64, KB = 16;
+  __shared__ float sA[KB][TB + 1], sB[KB][TB + 1];
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int m0 = tm * TB, n0 = tn * TB;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const T* A = static_cast<const T*>(p.A);
+  const T* B = static_cast<const T*>(p.B);
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v = 0.0f;
+      if constexpr (EPI == EPI_ACC) {
+        const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
+        if (p.beta && m < p.M && n < p.N) v = static_cast<const float*>(p.C)[(int64_t)m * p.ldc + n];
+      }
+      acc[i][j] = v;
+    }
+  for (int k0 = 0; k0 < p.K; k0 += KB) {
+    for (int idx = tid; idx < KB * TB; idx += 256) {
+      const int kk = idx / TB, mm = idx % TB;
+      const int gk = k0 + kk, gm = m0 + mm, gn = n0 + mm;
+      float a = 0.0f, b = 0.0f;
+      if (gk < p.K && gm < p.M) a = ld_elem<T>(A, ak ? (int64_t)gm * p.lda + gk : (int64_t)gk * p.lda + gm);
+      if (gk < p.K && gn < p.N) b = ld_elem<T>(B, bk ? (int64_t)gn * p.ldb + gk : (int64_t)gk * p.ldb + gn);
+      sA[kk][mm] = a;
+      sB[kk][mm] = b;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sA[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = sB[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
+      if (m < p.M && n < p.N) epi_store<T, EPI>(p, m, n, acc[i][j]);
+    }
+}
+
+// ------------------------------------------------------------------- dispatch
+
+struct TileCfg {
+  int bm, bn;
+  float eff;  // relative per-CU throughput of the tile shape
+};
+constexpr TileCfg kTiles[] = {{256, 256, 1.0f}, {256, 128, 0.85f}, {128, 128, 0.7f}};
+constexpr int kCUs = 256;
+
+// first_tile = 1 skips 256x256 (the W layout needs too many registers for it).
+int pick_tile(int M, int N, int first_tile) {
+  int best = first_tile;
+  double best_cost = 1e300;
+  for (int t = first_tile; t < 3; ++t) {
+    const int nb = ((M + kTiles[t].bm - 1) / kTiles[t].bm) * ((N + kTiles[t].bn - 1) / kTiles[t].bn);
+    const int waves = (nb + kCUs - 1) / kCUs;
+    const double cost = (double)waves * kTiles[t].bm * kTiles[t].bn / kTiles[t].eff;
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = t;
+    }
+  }
+  return best;
+}
+
+template <int BM, int BN, bool AK, bool BKC, int EPI>
+void launch_mfma(Params p, hipStream_t s) {
+  p.nbm = (p.M + BM - 1) / BM;
+  p.nbn = (p.N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_bf16_mfma<BM, BN, AK, BKC, EPI>), dim3(p.nbm * p.nbn), dim3(NT), 0, s, p);
+}
+
+template <bool AK, bool BKC, int EPI>
+void launch_tile(int t, const Params& p, hipStream_t s) {
+  switch (t) {
+    case 0:
+      if constexpr (AK || BKC) launch_mfma<256, 256, AK, BKC, EPI>(p, s);
+      break;
+    case 1: launch_mfma<256, 128, AK, BKC, EPI>(p, s); break;
+    default: launch_mfma<128, 128, AK, BKC, EPI>(p, s); break;
+  }
+}
+
+template <typename T, int EPI>
+void launch_simt(Params p, bool ak, bool bk, hipStream_t s) {
+  p.nbm = (p.M + 63) / 64;
+  p.nbn = (p.N + 63) / 64;
+  hipLaunchKernelGGL((gemm_simt<T, EPI>), dim3(p.nbm * p.nbn), dim3(256), 0, s, p, (int)ak, (int)bk);
+}
+
+template <typename T>
+void launch_simt_epi(int epi, const Params& p, bool ak, bool bk, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE: launch_simt<T, EPI_STORE>(p, ak, bk, s); break;
+    case EPI_RESID: launch_simt<T, EPI_RESID>(p, ak, bk, s); break;
+    case EPI_GELU: launch_simt<T, EPI_GELU>(p, ak, bk, s); break;
+    case EPI_DGELU: launch_simt<T, EPI_DGELU>(p, ak, bk, s); break;
+    default: launch_simt<T, EPI_ACC>(p, ak, bk, s); break;
+  }
+}
+
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
+
+}  // namespace
+
+zb_status launch_gemm(const GemmDesc& g, hipStream_t s) {
+  if (g.M < 0 || g.N < 0 || g.K < 0) return set_error(ZB_E_ARG, "gemm: negative size");
+  if (g.M == 0 || g.N == 0) return ZB_OK;
+  if (!g.A || !g.B || !g.C) return set_error(ZB_E_ARG, "gemm: null operand");
+  if ((g.epi == EPI_RESID || g.epi == EPI_DGELU) && !g.R) return set_error(ZB_E_ARG, "gemm: null R");
+  if (g.epi == EPI_GELU && !g.Z) return set_error(ZB_E_ARG, "gemm: null Z");
+  Params p{};
+  p.M = g.M; p.N = g.N; p.K = g.K;
+  p.A = g.A; p.lda = g.lda; p.B = g.B; p.ldb = g.ldb; p.C = g.C; p.ldc = g.ldc;
+  p.R = g.R; p.ldr = g.ldr; p.Z = g.Z; p.ldz = g.ldz; p.beta = g.beta; p.gelu = g.gelu;
+
+  const double flops = 2.0 * g.M * g.N * (double)g.K;
+  const size_t es = g.dtype == ZB_DTYPE_BF16 ? 2 : 4;
+  double bytes = es * ((double)g.M * g.K + (double)g.K * g.N);
+  if (g.epi == EPI_ACC) bytes += (g.beta ? 8.0 : 4.0) * g.M * g.N;
+  else bytes += es * (double)g.M * g.N * ((g.epi == EPI_STORE) ? 1 : 2);
+
+  if (g.dtype == ZB_DTYPE_FP32) {
+    char name[48];
+    snprintf(name, sizeof name, "gemm_%s_simt64", g.tag);
+    ProfScope ps(name, flops, bytes, s);
+    launch_simt_epi<float>(g.epi, p, g.a_kcontig, g.b_kcontig, s);
+    ZB_HIP_CHECK(hipGetLastError());
+    return ZB_OK;
+  }
+  // bf16 MFMA path: 16-byte vectors along every contiguous dimension.
+  const int a_contig = g.a_kcontig ? g.K : g.M;
+  const int b_contig = g.b_kcontig ? g.K : g.N;
+  if (a_contig % 8 || b_contig % 8 || g.lda % 8 || g.ldb % 8 || !aligned16(g.A) || !aligned16(g.B))
+    return set_error(ZB_E_UNSUPPORTED, "gemm: contiguous extents and leading dims must be multiples of 8 "
+                                       "(M=%d N=%d K=%d lda=%lld ldb=%lld)", g.M, g.N, g.K,
+                     (long long)g.lda, (long long)g.ldb);
+  const bool w_layout = !g.a_kcontig && !g.b_kcontig;
+  const int t = pick_tile(g.M, g.N, w_layout ? 1 : 0);
+  char name[48];
+  snprintf(name, sizeof name, "gemm_%s_%dx%d", g.tag, kTiles[t].bm, kTiles[t].bn);
+  ProfScope ps(name, flops, bytes, s);
+  const bool ak = g.a_kcontig, bk = g.b_kcontig;
+  if (ak && !bk) {  // F
+    switch (g.epi) {
+      case EPI_STORE: launch_tile<true, false, EPI_STORE>(t, p, s); break;
+      case EPI_RESID: launch_tile<true, false, EPI_RESID>(t, p, s); break;
+      case EPI_GELU: launch_tile<true, false, EPI_GELU>(t, p, s); break;
+      default: return set_error(ZB_E_UNSUPPORTED, "gemm: epilogue %d with F layout", g.epi);
+    }
+  } else if (ak && bk) {  // B
+    switch (g.epi) {
+      case EPI_STORE: launch_tile<true, true, EPI_STORE>(t, p, s); break;
+      case EPI_RESID: launch_tile<true, true, EPI_RESID>(t, p, s); break;
+      case EPI_DGELU: launch_tile<true, true, EPI_DGELU>(t, p, s); break;
+      default: return set_error(ZB_E_UNSUPPORTED, "gemm: epilogue %d with B layout", g.epi);
+    }
+  } else if (!ak && !bk) {  // W
+    if (g.epi != EPI_ACC) return set_error(ZB_E_UNSUPPORTED, "gemm: W layout needs the fp32 accumulate epilogue");
+    launch_tile<false, false, EPI_ACC>(t, p, s);
+  } else {
+    return set_error(ZB_E_UNSUPPORTED, "gemm: layout (A m-contiguous, B k-contiguous) not built");
+  }
+  ZB_HIP_CHECK(hipGetLastError());
+  return ZB_OK;
+}
+
+}  // namespace zb

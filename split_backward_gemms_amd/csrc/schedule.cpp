@@ -1,0 +1,459 @@
+// Schedule layer: per-stage pass orders, ASAP simulation, one-device
+// linearization, order validation, the activation-memory ledger and the
+// timed-event inspector.  Host code only.
+//
+// Sources: "Zero Bubble Pipeline Parallelism" section 3 (ZB-H1, ZB-H2, the
+// memory model, ILP appendix Eq. 3-7) and section 5 (bubble rate); the
+// tutorial "Pipeline Schedules: GPipe, 1F1B and Zero Bubble" (1F1B warm-up
+// P-1-p, interleaved stages); the audit "Zero-Bubble Pipeline Parallelism,
+// Proven", section "Validate the schedule as data".
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "zb_internal.h"
+
+namespace zb {
+
+namespace {
+
+// Pass kinds packed as small integers for table lookups.
+enum { KF = 0, KB = 1, KW = 2, KU = 3, KBAD = 4 };
+
+int kind_index(char k) {
+  switch (k) {
+    case 'F': return KF;
+    case 'B': return KB;
+    case 'W': return KW;
+    case 'U': return KU;
+    default: return KBAD;
+  }
+}
+
+zb_op mk(int s, int j, char k) {
+  zb_op o;
+  o.stage = s;
+  o.mb = j;
+  o.kind = k;
+  o.pad_[0] = o.pad_[1] = o.pad_[2] = 0;
+  return o;
+}
+
+// Builds the op sequence of one stage.  The three split orders share one
+// shape: a warm-up of forwards, then one steady-state round per B, then the
+// W's still held back.  They differ in the warm-up length, in where a round
+// puts its forward, and in how many W's a stage holds back.
+std::vector<zb_op> stage_order(int order, int P, int m, int s) {
+  std::vector<zb_op> v;
+  if (order == ZB_ORDER_GPIPE) {
+    for (int j = 0; j < m; ++j) v.push_back(mk(s, j, 'F'));
+    for (int j = 0; j < m; ++j) v.push_back(mk(s, j, 'U'));
+    return v;
+  }
+  int warm, held;
+  bool f_first;  // round = F,B(,W) if true; B(,W),F if false
+  switch (order) {
+    case ZB_ORDER_1F1B:
+    case ZB_ORDER_ZBH1:
+    case ZB_ORDER_WLAST:
+      warm = P - 1 - s;       // tutorial: stage p warms up with P-1-p forwards
+      held = s;               // ZB-H1: stage s keeps s W's back
+      f_first = true;
+      break;
+    case ZB_ORDER_ZBH2:
+      warm = 2 * (P - s) - 1; // 2P-1 forwards on the first stage
+      held = 2 * s;
+      f_first = false;
+      break;
+    default:
+      return v;
+  }
+  warm = std::min(warm, m);
+  int nf = 0, nw = 0;
+  for (; nf < warm; ++nf) v.push_back(mk(s, nf, 'F'));
+  for (int b = 0; b < m; ++b) {
+    if (f_first && nf < m) v.push_back(mk(s, nf++, 'F'));
+    if (order == ZB_ORDER_1F1B) {
+      v.push_back(mk(s, b, 'U'));
+    } else {
+      v.push_back(mk(s, b, 'B'));
+      if (order != ZB_ORDER_WLAST && b >= held) v.push_back(mk(s, nw++, 'W'));
+    }
+    if (!f_first && nf < m) v.push_back(mk(s, nf++, 'F'));
+  }
+  if (order != ZB_ORDER_1F1B)
+    for (; nw < m; ++nw) v.push_back(mk(s, nw, 'W'));
+  return v;
+}
+
+int64_t duration(int k, const int64_t* t) { return k == KU ? t[1] + t[2] : t[k]; }
+
+}  // namespace
+
+zb_status schedule_stage_order(int order, int P, int m, int stage, std::vector<zb_op>& out) {
+  if (P < 1 || m < 1) return set_error(ZB_E_ARG, "P and m must be >= 1");
+  if (order < ZB_ORDER_GPIPE || order > ZB_ORDER_WLAST) return set_error(ZB_E_ARG, "unknown order");
+  if (stage < 0 || stage >= P) return set_error(ZB_E_INVALID_STAGE, "stage outside [0, P)");
+  if (order == ZB_ORDER_ZBH2 && m < 2 * P - 1)
+    return set_error(ZB_E_ARG, "ZB-H2 needs m >= 2P-1");
+  out = stage_order(order, P, m, stage);
+  return ZB_OK;
+}
+
+zb_status schedule_simulate(int P, int m, const zb_op* ops, int n_ops, const int64_t* t,
+                            int64_t t_comm, std::vector<SimPass>& passes, zb_sim_stats* stats) {
+  if (P < 1 || m < 1 || n_ops < 0 || (n_ops > 0 && !ops) || !t)
+    return set_error(ZB_E_ARG, "bad simulate arguments");
+  for (int i = 0; i < 3; ++i)
+    if (t[i] < 1) return set_error(ZB_E_ARG, "pass times must be >= 1");
+  if (t_comm < 0) return set_error(ZB_E_ARG, "t_comm must be >= 0");
+  std::vector<std::vector<int>> per(P);
+  for (int i = 0; i < n_ops; ++i) {
+    const zb_op& o = ops[i];
+    if (o.stage < 0 || o.stage >= P) return set_error(ZB_E_INVALID_STAGE, "op %d: stage %d", i, o.stage);
+    if (o.mb < 0 || o.mb >= m) return set_error(ZB_E_INVALID_MB, "op %d: mb %d", i, o.mb);
+    if (kind_index(o.kind) == KBAD) return set_error(ZB_E_ARG, "op %d: kind", i);
+    per[o.stage].push_back(i);
+  }
+  // end time per (stage, mb, kind); -1 = not yet run
+  const int64_t NONE = -1;
+  std::vector<int64_t> endt((size_t)P * m * 4, NONE), backend((size_t)P * m, NONE);
+  auto E = [&](int s, int j, int k) -> int64_t& { return endt[((size_t)s * m + j) * 4 + k]; };
+  std::vector<size_t> pos(P, 0);
+  std::vector<int64_t> freet(P, 0);
+  passes.assign(n_ops, SimPass{});
+  int remaining = n_ops;
+  while (remaining > 0) {
+    bool progressed = false;
+    for (int s = 0; s < P; ++s) {
+      while (pos[s] < per[s].size()) {
+        int idx = per[s][pos[s]];
+        const zb_op& o = ops[idx];
+        int k = kind_index(o.kind), j = o.mb;
+        int64_t ready = freet[s];
+        bool ok = true;
+        if (k == KF) {
+          if (s > 0) {
+            if (E(s - 1, j, KF) == NONE) ok = false;
+            else ready = std::max(ready, E(s - 1, j, KF) + t_comm);
+          }
+        } else if (k == KB || k == KU) {
+          if (E(s, j, KF) == NONE) ok = false;
+          else ready = std::max(ready, E(s, j, KF));
+          if (ok && s < P - 1) {
+            int64_t be = backend[(size_t)(s + 1) * m + j];
+            if (be == NONE) ok = false;
+            else ready = std::max(ready, be + t_comm);
+          }
+        } else {  // W
+          if (E(s, j, KB) == NONE) ok = false;
+          else ready = std::max(ready, E(s, j, KB));
+        }
+        if (!ok) break;
+        int64_t d = duration(k, t);
+        passes[idx] = SimPass{idx, s, ready, ready + d};
+        E(s, j, k) = ready + d;
+        if (k == KB || k == KU) backend[(size_t)s * m + j] = ready + d;
+        freet[s] = ready + d;
+        ++pos[s];
+        --remaining;
+        progressed = true;
+      }
+    }
+    if (!progressed) {
+      for (int s = 0; s < P; ++s)
+        if (pos[s] < per[s].size())
+          return set_error(ZB_E_DEADLOCK, "deadlock: op %d (stage %d) can never start",
+                           per[s][pos[s]], s);
+    }
+  }
+  if (stats) {
+    int64_t makespan = 0, span = 0, busy = 0;
+    for (int s = 0; s < P; ++s) {
+      if (per[s].empty()) continue;
+      int64_t c = passes[per[s].back()].end - passes[per[s].front()].start;
+      makespan = std::max(makespan, c);
+    }
+    for (const SimPass& p : passes) {
+      span = std::max(span, p.end);
+      busy += p.end - p.start;
+    }
+    stats->makespan = makespan;
+    stats->span = span;
+    stats->busy = busy;
+    stats->ideal = (int64_t)m * (t[0] + t[1] + t[2]);
+    stats->bubble = makespan - stats->ideal;
+  }
+  return ZB_OK;
+}
+
+void schedule_linearize(const std::vector<SimPass>& passes, std::vector<int>& order) {
+  order.resize(passes.size());
+  for (size_t i = 0; i < passes.size(); ++i) order[i] = (int)i;
+  // Ties: lower stage first, then the stage's own order (which is the input index order).
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    if (passes[a].start != passes[b].start) return passes[a].start < passes[b].start;
+    if (passes[a].stage != passes[b].stage) return passes[a].stage < passes[b].stage;
+    return a < b;
+  });
+}
+
+zb_status schedule_validate(int P, int m, const zb_op* ops, int n_ops, int* bad) {
+  if (bad) *bad = -1;
+  if (P < 1 || m < 1 || n_ops < 0 || (n_ops > 0 && !ops)) return set_error(ZB_E_ARG, "bad validate arguments");
+  std::vector<uint8_t> done((size_t)P * m * 4, 0);
+  auto D = [&](int s, int j, int k) -> uint8_t& { return done[((size_t)s * m + j) * 4 + k]; };
+  for (int i = 0; i < n_ops; ++i) {
+    const zb_op& o = ops[i];
+    int k = kind_index(o.kind), s = o.stage, j = o.mb;
+    auto fail = [&](zb_status st, const char* why) {
+      if (bad) *bad = i;
+      return set_error(st, "op %d (stage %d, mb %d, kind %c): %s", i, s, j,
+                       (o.kind >= 32 && o.kind < 127) ? o.kind : '?', why);
+    };
+    if (k == KBAD) return fail(ZB_E_ARG, "kind must be F, B, W or U");
+    if (s < 0 || s >= P) return fail(ZB_E_INVALID_STAGE, "stage outside [0, P)");
+    if (j < 0 || j >= m) return fail(ZB_E_INVALID_MB, "microbatch outside [0, m)");
+    if (D(s, j, k)) return fail(ZB_E_DUPLICATE, "pass repeated");
+    if (k == KU && (D(s, j, KB) || D(s, j, KW))) return fail(ZB_E_DUPLICATE, "unsplit pass after split B/W");
+    if ((k == KB || k == KW) && D(s, j, KU)) return fail(ZB_E_DUPLICATE, "split pass after unsplit backward");
+    if (k == KF) {
+      if (s > 0 && !D(s - 1, j, KF)) return fail(ZB_E_DEPENDENCY, "forward before the previous stage's forward");
+    } else if (k == KB || k == KU) {
+      if (!D(s, j, KF)) return fail(ZB_E_DEPENDENCY, "backward before its own forward");
+      if (s < P - 1 && !D(s + 1, j, KB) && !D(s + 1, j, KU))
+        return fail(ZB_E_DEPENDENCY, "backward before the next stage's backward");
+    } else {
+      if (!D(s, j, KB)) return fail(ZB_E_DEPENDENCY, "weight gradient before its B");
+    }
+    D(s, j, k) = 1;
+  }
+  for (int s = 0; s < P; ++s)
+    for (int j = 0; j < m; ++j) {
+      bool f = D(s, j, KF), split = D(s, j, KB) && D(s, j, KW), un = D(s, j, KU);
+      if (!f || !(split || un)) {
+        if (bad) *bad = n_ops;
+        return set_error(ZB_E_MISSING, "stage %d mb %d: %s missing before the step boundary", s, j,
+                         !f ? "F" : (D(s, j, KB) ? "W" : "backward"));
+      }
+    }
+  return ZB_OK;
+}
+
+}  // namespace zb
+
+using namespace zb;
+
+extern "C" zb_status zb_schedule_stage_order(int order, int P, int m, int stage, zb_op* out, int cap,
+                                             int* n_out) {
+  clear_error();
+  if (!out || !n_out) return set_error(ZB_E_ARG, "null output");
+  std::vector<zb_op> v;
+  zb_status st = schedule_stage_order(order, P, m, stage, v);
+  if (st != ZB_OK) return st;
+  if ((int)v.size() > cap) return set_error(ZB_E_ARG, "cap %d < %zu ops", cap, v.size());
+  std::copy(v.begin(), v.end(), out);
+  *n_out = (int)v.size();
+  return ZB_OK;
+}
+
+extern "C" zb_status zb_schedule_simulate(int P, int m, const zb_op* ops, int n_ops, const int64_t* times,
+                                          int64_t t_comm, zb_op* linear_out, int64_t* start_out,
+                                          int64_t* end_out, zb_sim_stats* stats) {
+  clear_error();
+  std::vector<SimPass> passes;
+  zb_status st = schedule_simulate(P, m, ops, n_ops, times, t_comm, passes, stats);
+  if (st != ZB_OK) return st;
+  std::vector<int> lin;
+  schedule_linearize(passes, lin);
+  for (int i = 0; i < n_ops; ++i) {
+    const SimPass& p = passes[lin[i]];
+    if (linear_out) linear_out[i] = ops[lin[i]];
+    if (start_out) start_out[i] = p.start;
+    if (end_out) end_out[i] = p.end;
+  }
+  return ZB_OK;
+}
+
+extern "C" zb_status zb_schedule_build(int order, int P, int m, const int64_t* times, int64_t t_comm,
+                                       zb_op* linear_out, int cap, int* n_out, zb_sim_stats* stats) {
+  clear_error();
+  if (!linear_out || !n_out) return set_error(ZB_E_ARG, "null output");
+  if (P < 1 || m < 1) return set_error(ZB_E_ARG, "P and m must be >= 1");
+  std::vector<zb_op> all;
+  for (int s = 0; s < P; ++s) {
+    std::vector<zb_op> v;
+    zb_status st = schedule_stage_order(order, P, m, s, v);
+    if (st != ZB_OK) return st;
+    all.insert(all.end(), v.begin(), v.end());
+  }
+  if ((int)all.size() > cap) return set_error(ZB_E_ARG, "cap %d < %zu ops", cap, all.size());
+  std::vector<SimPass> passes;
+  zb_status st = schedule_simulate(P, m, all.data(), (int)all.size(), times, t_comm, passes, stats);
+  if (st != ZB_OK) return st;
+  std::vector<int> lin;
+  schedule_linearize(passes, lin);
+  for (size_t i = 0; i < lin.size(); ++i) linear_out[i] = all[lin[i]];
+  *n_out = (int)all.size();
+  return ZB_OK;
+}
+
+extern "C" zb_status zb_schedule_simulate_interleaved(int P, int m, int v, const int64_t* t,
+                                                      zb_sim_stats* stats) {
+  clear_error();
+  if (P < 1 || m < 1 || v < 1 || !t || !stats) return set_error(ZB_E_ARG, "bad arguments");
+  if (m % P) return set_error(ZB_E_ARG, "interleaved order needs m %% P == 0");
+  for (int i = 0; i < 3; ++i)
+    if (t[i] < 1) return set_error(ZB_E_ARG, "pass times must be >= 1");
+  // Virtual stage k = c*P + d lives on device d; dependencies run along k.
+  const int V = v * P;
+  struct VOp { int k, kind, j; };
+  std::vector<std::vector<VOp>> dev(P);
+  for (int d = 0; d < P; ++d) {
+    for (int g = 0; g < m; g += P)
+      for (int c = 0; c < v; ++c)
+        for (int j = g; j < g + P; ++j) dev[d].push_back({c * P + d, KF, j});
+    for (int g = 0; g < m; g += P)
+      for (int c = v - 1; c >= 0; --c)
+        for (int j = g; j < g + P; ++j) dev[d].push_back({c * P + d, KU, j});
+  }
+  const int64_t NONE = -1;
+  std::vector<int64_t> fend((size_t)V * m, NONE), uend((size_t)V * m, NONE);
+  std::vector<int64_t> first_start(P, NONE), last_end(P, 0), freet(P, 0);
+  std::vector<size_t> pos(P, 0);
+  size_t remaining = 0;
+  for (auto& q : dev) remaining += q.size();
+  int64_t busy = 0, span = 0;
+  while (remaining) {
+    bool progressed = false;
+    for (int d = 0; d < P; ++d) {
+      while (pos[d] < dev[d].size()) {
+        const VOp& o = dev[d][pos[d]];
+        int64_t ready = freet[d];
+        if (o.kind == KF) {
+          if (o.k > 0) {
+            int64_t e = fend[(size_t)(o.k - 1) * m + o.j];
+            if (e == NONE) break;
+            ready = std::max(ready, e);
+          }
+        } else {
+          int64_t fe = fend[(size_t)o.k * m + o.j];
+          if (fe == NONE) break;
+          ready = std::max(ready, fe);
+          if (o.k < V - 1) {
+            int64_t e = uend[(size_t)(o.k + 1) * m + o.j];
+            if (e == NONE) break;
+            ready = std::max(ready, e);
+          }
+        }
+        int64_t dur = duration(o.kind, t);
+        if (o.kind == KF) fend[(size_t)o.k * m + o.j] = ready + dur;
+        else uend[(size_t)o.k * m + o.j] = ready + dur;
+        if (first_start[d] == NONE) first_start[d] = ready;
+        last_end[d] = ready + dur;
+        freet[d] = ready + dur;
+        busy += dur;
+        span = std::max(span, ready + dur);
+        ++pos[d];
+        --remaining;
+        progressed = true;
+      }
+    }
+    if (!progressed) return set_error(ZB_E_DEADLOCK, "interleaved order deadlocked");
+  }
+  int64_t makespan = 0;
+  for (int d = 0; d < P; ++d) makespan = std::max(makespan, last_end[d] - first_start[d]);
+  stats->makespan = makespan;
+  stats->span = span;
+  stats->busy = busy;
+  stats->ideal = (int64_t)m * v * (t[0] + t[1] + t[2]);
+  stats->bubble = makespan - stats->ideal;
+  return ZB_OK;
+}
+
+extern "C" zb_status zb_schedule_validate(int P, int m, const zb_op* ops, int n_ops, int* bad_index) {
+  clear_error();
+  return schedule_validate(P, m, ops, n_ops, bad_index);
+}
+
+extern "C" zb_status zb_schedule_peak_memory(const zb_op* ops, int n_ops, int stage, int64_t m_b,
+                                             int64_t m_w, int64_t* peak) {
+  clear_error();
+  if (!peak || n_ops < 0 || (n_ops > 0 && !ops)) return set_error(ZB_E_ARG, "bad arguments");
+  int64_t level = 0, best = 0;
+  for (int i = 0; i < n_ops; ++i) {
+    if (ops[i].stage != stage) continue;
+    switch (kind_index(ops[i].kind)) {
+      case KF: level += m_b; break;
+      case KB: level += m_w - m_b; break;
+      case KW: level -= m_w; break;
+      case KU: level -= m_b; break;
+      default: return set_error(ZB_E_ARG, "op %d: kind", i);
+    }
+    best = std::max(best, level);
+  }
+  *peak = best;
+  return ZB_OK;
+}
+
+extern "C" zb_status zb_events_inspect(const zb_event* ev, int n, int stage_count, zb_event_report* rep,
+                                       int* bad_index) {
+  clear_error();
+  if (bad_index) *bad_index = -1;
+  if (n < 1 || !ev || !rep) return set_error(ZB_E_ARG, "need at least one event");
+  if (stage_count < 2) return set_error(ZB_E_ARG, "invalid_stage_count");
+  std::unordered_map<int32_t, int> by_id;
+  for (int i = 0; i < n; ++i) by_id[ev[i].id] = i;
+  if ((int)by_id.size() != n) {
+    std::unordered_map<int32_t, int> seen;
+    for (int i = 0; i < n; ++i)
+      if (!seen.emplace(ev[i].id, i).second) {
+        if (bad_index) *bad_index = i;
+        break;
+      }
+    return set_error(ZB_E_DUPLICATE, "duplicate_task");
+  }
+  for (int i = 0; i < n; ++i) {
+    const zb_event& e = ev[i];
+    auto fail = [&](zb_status st, const char* why) {
+      if (bad_index) *bad_index = i;
+      return set_error(st, "event %d (id %d): %s", i, e.id, why);
+    };
+    if (e.stage < 0 || e.stage >= stage_count) return fail(ZB_E_INVALID_STAGE, "invalid_stage");
+    if (!(e.start >= 0 && e.end > e.start)) return fail(ZB_E_INTERVAL, "invalid_interval");
+    for (int d = 0; d < e.n_deps; ++d) {
+      auto it = by_id.find(e.deps[d]);
+      if (it == by_id.end()) return fail(ZB_E_MISSING, "missing_dependency");
+      if (ev[it->second].end > e.start) return fail(ZB_E_DEPENDENCY, "dependency_violation");
+    }
+  }
+  for (int s = 0; s < stage_count; ++s) {
+    std::vector<int> idx;
+    for (int i = 0; i < n; ++i)
+      if (ev[i].stage == s) idx.push_back(i);
+    std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return ev[a].start < ev[b].start; });
+    for (size_t q = 1; q < idx.size(); ++q)
+      if (ev[idx[q - 1]].end > ev[idx[q]].start) {
+        if (bad_index) *bad_index = idx[q];
+        return set_error(ZB_E_OVERLAP, "stage_overlap on stage %d", s);
+      }
+  }
+  double span = ev[0].end, busy = 0;
+  std::unordered_map<int32_t, int64_t> live;
+  for (int i = 0; i < n; ++i) {
+    span = std::max(span, ev[i].end);
+    busy += ev[i].end - ev[i].start;
+    if (ev[i].kind == 'F') live[ev[i].micro] += 1;
+    else if (ev[i].kind == 'B') live[ev[i].micro] = std::max<int64_t>(0, live[ev[i].micro] - 1);
+  }
+  int64_t unfinished = 0;
+  for (auto& kv : live) unfinished += kv.second;
+  rep->span = span;
+  rep->busy = busy;
+  rep->bubble_ratio = 1.0 - busy / (stage_count * span);
+  rep->unfinished_activations = unfinished;
+  return ZB_OK;
+}

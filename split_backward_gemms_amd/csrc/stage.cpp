@@ -1,0 +1,877 @@
+// Stage object, saved-tensor lifetime manager and schedule executor.
+//
+// A stage keeps, per live microbatch, three classes of tensors in slots of a
+// caller-provided workspace (the pages' activation memory M_B / M_W, "Zero
+// Bubble Pipeline Parallelism", section 3, "The Memory Model"):
+//   FW  from F to W:  each layer's input and what its W passes read
+//   FB  from F to B:  what only B reads (pre-activations, attention inputs, LSE)
+//   BW  from B to W:  every linear's output gradient
+// The F -> B -> W order per microbatch and the optimizer dependency at the
+// step boundary follow section 3's dependency rules and the audit's "Draw the
+// event graph before the Gantt".
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "zb_internal.h"
+
+// ================================================================ errors
+namespace zb {
+namespace {
+thread_local std::string g_err;
+}
+
+zb_status set_error(zb_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+void clear_error() { g_err.clear(); }
+
+// ========================================================== kernel timing
+namespace {
+struct ProfEvent {
+  std::string name;
+  double flops, bytes;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof = false;
+std::vector<ProfEvent> g_prof_ev;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pool_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+bool prof_on() { return g_prof; }
+
+ProfScope::ProfScope(const char* name, double flops, double bytes, hipStream_t s) : stream(s) {
+  if (!g_prof) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  hipEvent_t a = pool_event(), b = pool_event();
+  if (!a || !b) return;
+  g_prof_ev.push_back(ProfEvent{name, flops, bytes, a, b});
+  slot = (int)g_prof_ev.size() - 1;
+  (void)hipEventRecord(a, s);
+}
+
+ProfScope::~ProfScope() {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  (void)hipEventRecord(g_prof_ev[slot].b, stream);
+}
+
+}  // namespace zb
+
+using namespace zb;
+
+extern "C" const char* zb_last_error(void) { return g_err.c_str(); }
+
+extern "C" const char* zb_version(void) { return "zb-stage gfx950 0.1"; }
+
+extern "C" void zb_prof_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof = on != 0;
+}
+
+extern "C" void zb_prof_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& e : g_prof_ev) {
+    (void)hipEventSynchronize(e.b);
+    g_event_pool.push_back(e.a);
+    g_event_pool.push_back(e.b);
+  }
+  g_prof_ev.clear();
+}
+
+extern "C" zb_status zb_prof_read(zb_prof_rec* out, int cap, int* n) {
+  clear_error();
+  if (!n || (cap > 0 && !out)) return set_error(ZB_E_ARG, "null output");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  std::map<std::string, zb_prof_rec> agg;
+  for (auto& e : g_prof_ev) {
+    ZB_HIP_CHECK(hipEventSynchronize(e.b));
+    float ms = 0.f;
+    ZB_HIP_CHECK(hipEventElapsedTime(&ms, e.a, e.b));
+    zb_prof_rec& r = agg[e.name];
+    if (r.launches == 0) {
+      memset(&r, 0, sizeof r);
+      snprintf(r.name, sizeof r.name, "%s", e.name.c_str());
+    }
+    r.launches += 1;
+    r.total_ms += ms;
+    r.flops += e.flops;
+    r.bytes += e.bytes;
+  }
+  int i = 0;
+  for (auto& kv : agg) {
+    if (i < cap) out[i] = kv.second;
+    ++i;
+  }
+  *n = i;
+  return ZB_OK;
+}
+
+// ============================================================ stage object
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Slots of one tensor class.
+struct Pool {
+  size_t bytes = 0;  // per slot
+  int n = 0;
+  char* base = nullptr;
+  std::vector<int> free_list;
+  void reset(char* b, int count) {
+    base = b;
+    n = count;
+    free_list.clear();
+    for (int i = count - 1; i >= 0; --i) free_list.push_back(i);
+  }
+  int acquire() {
+    if (free_list.empty()) return -1;
+    int s = free_list.back();
+    free_list.pop_back();
+    return s;
+  }
+  void release(int s) {
+    if (s >= 0) free_list.push_back(s);
+  }
+  char* at(int s) const { return base + (size_t)s * bytes; }
+};
+
+struct LayerOff {
+  // FW
+  size_t x = 0, qkv_fw = 0, o = 0, xup = 0, a = 0;
+  // FB
+  size_t z = 0, qkv_fb = 0, lse = 0;
+  // BW
+  size_t dy = 0, dz = 0, dp = 0, dqkv = 0;
+};
+
+enum MbState { MB_IDLE = 0, MB_F = 1, MB_B = 2, MB_DONE = 3 };
+
+int linears_per_layer(int kind) { return kind == ZB_KIND_TINY_MLP ? 2 : 4; }
+
+}  // namespace
+
+struct zb_stage {
+  zb_stage_desc d{};
+  int index = 0;
+  int T = 0, h = 0, f = 0, L = 0, nlin = 0;
+  size_t es = 2;
+  std::vector<const void*> w;
+  std::vector<float*> dw;
+  std::vector<int64_t> wK, wN;  // per linear
+  hipStream_t stream = nullptr;
+  std::vector<LayerOff> off;
+  size_t fw_bytes = 0, fb_bytes = 0, bw_bytes = 0, scratch_bytes = 0;
+  size_t scratch_do = 0, scratch_flag = 0;
+  // plan
+  bool planned = false;
+  int plan_fw = 0, plan_fb = 0, plan_bw = 0;
+  // workspace
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  char* scratch = nullptr;
+  Pool fw, fb, bw;
+  bool bound = false;
+  // per microbatch
+  std::vector<int> st, s_fw, s_fb, s_bw;
+  int w_count = 0;
+};
+
+namespace {
+
+enum { LIN_QKV = 0, LIN_PROJ = 1, LIN_UP = 2, LIN_DOWN = 3 };
+
+int lin_index(const zb_stage* S, int layer, int which) {
+  if (S->d.kind == ZB_KIND_TINY_MLP) return layer * 2 + (which == LIN_UP ? 0 : 1);
+  return layer * 4 + which;
+}
+
+void compute_layout(zb_stage* S) {
+  const size_t T = S->T, h = S->h, f = S->f, es = S->es;
+  const size_t a = S->d.n_heads;
+  size_t fw = 0, fb = 0, bw = 0;
+  S->off.assign(S->L, LayerOff{});
+  for (int l = 0; l < S->L; ++l) {
+    LayerOff& o = S->off[l];
+    o.x = fw; fw += align_up(T * h * es);
+    if (S->d.kind == ZB_KIND_MLP_LINEARS) {
+      o.qkv_fw = fw; fw += align_up(T * 3 * h * es);
+      o.xup = fw; fw += align_up(T * h * es);
+    } else if (S->d.kind == ZB_KIND_FULL) {
+      o.o = fw; fw += align_up(T * h * es);
+      o.xup = fw; fw += align_up(T * h * es);
+    }
+    o.a = fw; fw += align_up(T * f * es);
+
+    o.z = fb; fb += align_up(T * f * es);
+    if (S->d.kind == ZB_KIND_FULL) {
+      o.qkv_fb = fb; fb += align_up(T * 3 * h * es);
+      o.lse = fb; fb += align_up(a * T * 4);
+    }
+
+    o.dy = bw; bw += align_up(T * h * es);
+    o.dz = bw; bw += align_up(T * f * es);
+    if (S->d.kind != ZB_KIND_TINY_MLP) {
+      o.dp = bw; bw += align_up(T * h * es);
+      o.dqkv = bw; bw += align_up(T * 3 * h * es);
+    }
+  }
+  S->fw_bytes = fw;
+  S->fb_bytes = fb;
+  S->bw_bytes = bw;
+  size_t sc = 0;
+  S->scratch_flag = sc; sc += kAlign;
+  S->scratch_do = sc;
+  if (S->d.kind == ZB_KIND_FULL) sc += align_up(T * h * es);
+  S->scratch_bytes = sc;
+  S->fw.bytes = fw;
+  S->fb.bytes = fb;
+  S->bw.bytes = bw;
+}
+
+// Replays slot claims and releases of stage `idx` over a one-device order.
+void plan_counts(int idx, int m, const zb_op* ops, int n, int& nfw, int& nfb, int& nbw) {
+  if (!ops) {
+    nfw = nfb = nbw = m;
+    return;
+  }
+  std::vector<char> hfw(m, 0), hfb(m, 0), hbw(m, 0);
+  int cfw = 0, cfb = 0, cbw = 0;
+  nfw = nfb = nbw = 0;
+  auto take = [&](std::vector<char>& held, int j, int& c, int& mx) {
+    if (j < 0 || j >= m || held[j]) return;
+    held[j] = 1;
+    mx = std::max(mx, ++c);
+  };
+  auto drop = [&](std::vector<char>& held, int j, int& c) {
+    if (j < 0 || j >= m || !held[j]) return;
+    held[j] = 0;
+    --c;
+  };
+  for (int i = 0; i < n; ++i) {
+    const zb_op& o = ops[i];
+    const int j = o.mb;
+    if (o.stage == idx - 1 && o.kind == 'F') take(hfw, j, cfw, nfw);
+    if (o.stage == idx + 1 && (o.kind == 'B' || o.kind == 'U')) take(hbw, j, cbw, nbw);
+    if (o.stage != idx) continue;
+    switch (o.kind) {
+      case 'F':
+        take(hfw, j, cfw, nfw);
+        take(hfb, j, cfb, nfb);
+        break;
+      case 'B':
+        take(hbw, j, cbw, nbw);
+        drop(hfb, j, cfb);
+        break;
+      case 'W':
+        drop(hfw, j, cfw);
+        drop(hbw, j, cbw);
+        break;
+      case 'U':
+        take(hbw, j, cbw, nbw);
+        drop(hfb, j, cfb);
+        drop(hfw, j, cfw);
+        drop(hbw, j, cbw);
+        break;
+      default:
+        break;
+    }
+  }
+}
+
+size_t ws_size(const zb_stage* S, int nfw, int nfb, int nbw) {
+  return S->scratch_bytes + (size_t)nfw * S->fw_bytes + (size_t)nfb * S->fb_bytes + (size_t)nbw * S->bw_bytes;
+}
+
+// ------------------------------------------------------------- GEMM calls
+
+zb_status gemm_f(zb_stage* S, const void* X, int64_t ldx, int lin, void* Y, int64_t ldy, int epi,
+                 const void* R = nullptr, int64_t ldr = 0, void* Z = nullptr, int64_t ldz = 0) {
+  GemmDesc g;
+  g.M = S->T; g.N = (int)S->wN[lin]; g.K = (int)S->wK[lin];
+  g.A = X; g.lda = ldx; g.a_kcontig = true;
+  g.B = S->w[lin]; g.ldb = S->wN[lin]; g.b_kcontig = false;
+  g.C = Y; g.ldc = ldy; g.R = R; g.ldr = ldr; g.Z = Z; g.ldz = ldz;
+  g.epi = epi; g.dtype = S->d.dtype; g.gelu = S->d.gelu; g.tag = "f";
+  return launch_gemm(g, S->stream);
+}
+
+// dX[T, K_in] = dY[T, N_out] . W^T
+zb_status gemm_b(zb_stage* S, const void* dY, int64_t lddy, int lin, void* dX, int64_t lddx, int epi,
+                 const void* R = nullptr, int64_t ldr = 0) {
+  GemmDesc g;
+  g.M = S->T; g.N = (int)S->wK[lin]; g.K = (int)S->wN[lin];
+  g.A = dY; g.lda = lddy; g.a_kcontig = true;
+  g.B = S->w[lin]; g.ldb = S->wN[lin]; g.b_kcontig = true;
+  g.C = dX; g.ldc = lddx; g.R = R; g.ldr = ldr;
+  g.epi = epi; g.dtype = S->d.dtype; g.gelu = S->d.gelu; g.tag = "b";
+  return launch_gemm(g, S->stream);
+}
+
+// dW[K_in, N_out] (+)= X^T . dY
+zb_status gemm_w(zb_stage* S, const void* X, int64_t ldx, const void* dY, int64_t lddy, int lin, int beta) {
+  GemmDesc g;
+  g.M = (int)S->wK[lin]; g.N = (int)S->wN[lin]; g.K = S->T;
+  g.A = X; g.lda = ldx; g.a_kcontig = false;
+  g.B = dY; g.ldb = lddy; g.b_kcontig = false;
+  g.C = S->dw[lin]; g.ldc = S->wN[lin];
+  g.epi = EPI_ACC; g.beta = beta; g.dtype = S->d.dtype; g.tag = "w";
+  return launch_gemm(g, S->stream);
+}
+
+#define ZB_TRY(expr)                   \
+  do {                                 \
+    zb_status s_ = (expr);             \
+    if (s_ != ZB_OK) return s_;        \
+  } while (0)
+
+char* elem(char* base, size_t off, int64_t col, size_t es) { return base + off + (size_t)col * es; }
+
+// ---------------------------------------------------------------- passes
+
+zb_status run_forward(zb_stage* S, int mb, void* y) {
+  char* fwb = S->fw.at(S->s_fw[mb]);
+  char* fbb = S->fb.at(S->s_fb[mb]);
+  const int64_t h = S->h, f = S->f;
+  const size_t es = S->es;
+  for (int l = 0; l < S->L; ++l) {
+    const LayerOff& o = S->off[l];
+    void* out = (l + 1 < S->L) ? (void*)(fwb + S->off[l + 1].x) : y;
+    char* X = fwb + o.x;
+    switch (S->d.kind) {
+      case ZB_KIND_TINY_MLP:
+        ZB_TRY(gemm_f(S, X, h, lin_index(S, l, LIN_UP), fwb + o.a, f, EPI_GELU, nullptr, 0, fbb + o.z, f));
+        ZB_TRY(gemm_f(S, fwb + o.a, f, lin_index(S, l, LIN_DOWN), out, h, EPI_STORE));
+        break;
+      case ZB_KIND_MLP_LINEARS: {
+        char* qkv = fwb + o.qkv_fw;
+        ZB_TRY(gemm_f(S, X, h, lin_index(S, l, LIN_QKV), qkv, 3 * h, EPI_STORE));
+        // identity attention: proj reads the V columns of qkv in place
+        ZB_TRY(gemm_f(S, elem(fwb, o.qkv_fw, 2 * h, es), 3 * h, lin_index(S, l, LIN_PROJ), fwb + o.xup, h,
+                      EPI_STORE));
+        ZB_TRY(gemm_f(S, fwb + o.xup, h, lin_index(S, l, LIN_UP), fwb + o.a, f, EPI_GELU, nullptr, 0, fbb + o.z, f));
+        ZB_TRY(gemm_f(S, fwb + o.a, f, lin_index(S, l, LIN_DOWN), out, h, EPI_STORE));
+        break;
+      }
+      default:
+        return set_error(ZB_E_UNSUPPORTED, "FULL layers need the attention kernels");
+    }
+  }
+  return ZB_OK;
+}
+
+// Input-gradient pass; with `unsplit`, each linear's weight gradient follows its B GEMM.
+zb_status run_backward(zb_stage* S, int mb, void* dx, bool unsplit, int beta) {
+  char* fwb = S->fw.at(S->s_fw[mb]);
+  char* fbb = S->fb.at(S->s_fb[mb]);
+  char* bwb = S->bw.at(S->s_bw[mb]);
+  const int64_t h = S->h, f = S->f;
+  const size_t es = S->es;
+  for (int l = S->L - 1; l >= 0; --l) {
+    const LayerOff& o = S->off[l];
+    void* out = (l > 0) ? (void*)(bwb + S->off[l - 1].dy) : dx;
+    char* dY = bwb + o.dy;
+    switch (S->d.kind) {
+      case ZB_KIND_TINY_MLP: {
+        const int up = lin_index(S, l, LIN_UP), down = lin_index(S, l, LIN_DOWN);
+        ZB_TRY(gemm_b(S, dY, h, down, bwb + o.dz, f, EPI_DGELU, fbb + o.z, f));
+        if (unsplit) ZB_TRY(gemm_w(S, fwb + o.a, f, dY, h, down, beta));
+        ZB_TRY(gemm_b(S, bwb + o.dz, f, up, out, h, EPI_STORE));
+        if (unsplit) ZB_TRY(gemm_w(S, fwb + o.x, h, bwb + o.dz, f, up, beta));
+        break;
+      }
+      case ZB_KIND_MLP_LINEARS: {
+        const int qkv = lin_index(S, l, LIN_QKV), proj = lin_index(S, l, LIN_PROJ);
+        const int up = lin_index(S, l, LIN_UP), down = lin_index(S, l, LIN_DOWN);
+        ZB_TRY(gemm_b(S, dY, h, down, bwb + o.dz, f, EPI_DGELU, fbb + o.z, f));
+        if (unsplit) ZB_TRY(gemm_w(S, fwb + o.a, f, dY, h, down, beta));
+        ZB_TRY(gemm_b(S, bwb + o.dz, f, up, bwb + o.dp, h, EPI_STORE));
+        if (unsplit) ZB_TRY(gemm_w(S, fwb + o.xup, h, bwb + o.dz, f, up, beta));
+        // identity attention backward: dV = dO, dQ = dK = 0
+        ZB_TRY(launch_zero2d(bwb + o.dqkv, S->T, 2 * h, 3 * h, (int)es, S->stream));
+        ZB_TRY(gemm_b(S, bwb + o.dp, h, proj, elem(bwb, o.dqkv, 2 * h, es), 3 * h, EPI_STORE));
+        if (unsplit) ZB_TRY(gemm_w(S, elem(fwb, o.qkv_fw, 2 * h, es), 3 * h, bwb + o.dp, h, proj, beta));
+        ZB_TRY(gemm_b(S, bwb + o.dqkv, 3 * h, qkv, out, h, EPI_STORE));
+        if (unsplit) ZB_TRY(gemm_w(S, fwb + o.x, h, bwb + o.dqkv, 3 * h, qkv, beta));
+        break;
+      }
+      default:
+        return set_error(ZB_E_UNSUPPORTED, "FULL layers need the attention kernels");
+    }
+  }
+  return ZB_OK;
+}
+
+zb_status run_weight(zb_stage* S, int mb, int beta) {
+  char* fwb = S->fw.at(S->s_fw[mb]);
+  char* bwb = S->bw.at(S->s_bw[mb]);
+  const int64_t h = S->h, f = S->f;
+  const size_t es = S->es;
+  for (int l = 0; l < S->L; ++l) {
+    const LayerOff& o = S->off[l];
+    switch (S->d.kind) {
+      case ZB_KIND_TINY_MLP:
+        ZB_TRY(gemm_w(S, fwb + o.x, h, bwb + o.dz, f, lin_index(S, l, LIN_UP), beta));
+        ZB_TRY(gemm_w(S, fwb + o.a, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
+        break;
+      case ZB_KIND_MLP_LINEARS:
+        ZB_TRY(gemm_w(S, fwb + o.x, h, bwb + o.dqkv, 3 * h, lin_index(S, l, LIN_QKV), beta));
+        ZB_TRY(gemm_w(S, elem(fwb, o.qkv_fw, 2 * h, es), 3 * h, bwb + o.dp, h, lin_index(S, l, LIN_PROJ), beta));
+        ZB_TRY(gemm_w(S, fwb + o.xup, h, bwb + o.dz, f, lin_index(S, l, LIN_UP), beta));
+        ZB_TRY(gemm_w(S, fwb + o.a, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
+        break;
+      default:
+        return set_error(ZB_E_UNSUPPORTED, "FULL layers need the attention kernels");
+    }
+  }
+  return ZB_OK;
+}
+
+zb_status copy_in(zb_stage* S, void* dst, const void* src) {
+  if (dst == src) return ZB_OK;
+  const size_t bytes = (size_t)S->T * S->h * S->es;
+  ZB_HIP_CHECK(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, S->stream));
+  return ZB_OK;
+}
+
+zb_status check_mb(const zb_stage* S, int mb) {
+  if (!S) return set_error(ZB_E_ARG, "null stage");
+  if (!S->bound) return set_error(ZB_E_STATE, "stage %d has no workspace bound", S->index);
+  if (mb < 0 || mb >= S->d.n_micro) return set_error(ZB_E_INVALID_MB, "mb %d outside [0, %d)", mb, S->d.n_micro);
+  return ZB_OK;
+}
+
+// Claims (if not yet held) the input slot of mb.
+zb_status claim_fw(zb_stage* S, int mb) {
+  if (S->s_fw[mb] >= 0) return ZB_OK;
+  int s = S->fw.acquire();
+  if (s < 0) return set_error(ZB_E_BUDGET, "stage %d: no free F->W slot for mb %d (workspace planned for %d)",
+                              S->index, mb, S->fw.n);
+  S->s_fw[mb] = s;
+  return ZB_OK;
+}
+
+zb_status claim_bw(zb_stage* S, int mb) {
+  if (S->s_bw[mb] >= 0) return ZB_OK;
+  int s = S->bw.acquire();
+  if (s < 0) return set_error(ZB_E_BUDGET, "stage %d: no free B->W slot for mb %d (workspace planned for %d)",
+                              S->index, mb, S->bw.n);
+  S->s_bw[mb] = s;
+  return ZB_OK;
+}
+
+void release_all(zb_stage* S, int mb) {
+  S->fw.release(S->s_fw[mb]);
+  S->fb.release(S->s_fb[mb]);
+  S->bw.release(S->s_bw[mb]);
+  S->s_fw[mb] = S->s_fb[mb] = S->s_bw[mb] = -1;
+}
+
+zb_status do_forward(zb_stage* S, int mb, const void* x, void* y) {
+  ZB_TRY(check_mb(S, mb));
+  if (!x || !y) return set_error(ZB_E_ARG, "null x or y");
+  if (S->st[mb] != MB_IDLE) return set_error(ZB_E_STATE, "stage %d mb %d already forwarded this step", S->index, mb);
+  const bool had_fw = S->s_fw[mb] >= 0;
+  ZB_TRY(claim_fw(S, mb));
+  int sfb = S->fb.acquire();
+  if (sfb < 0) {
+    if (!had_fw) {
+      S->fw.release(S->s_fw[mb]);
+      S->s_fw[mb] = -1;
+    }
+    return set_error(ZB_E_BUDGET, "stage %d: no free F->B slot for mb %d", S->index, mb);
+  }
+  S->s_fb[mb] = sfb;
+  ZB_TRY(copy_in(S, S->fw.at(S->s_fw[mb]) + S->off[0].x, x));
+  ZB_TRY(run_forward(S, mb, y));
+  S->st[mb] = MB_F;
+  return ZB_OK;
+}
+
+zb_status do_backward(zb_stage* S, int mb, const void* dy, void* dx, bool unsplit) {
+  ZB_TRY(check_mb(S, mb));
+  if (!dy || !dx) return set_error(ZB_E_ARG, "null dy or dx");
+  if (S->st[mb] != MB_F)
+    return set_error(ZB_E_STATE, "stage %d mb %d: backward needs a finished forward and no earlier backward",
+                     S->index, mb);
+  ZB_TRY(claim_bw(S, mb));
+  const int beta = S->w_count > 0 ? 1 : 0;
+  ZB_TRY(copy_in(S, S->bw.at(S->s_bw[mb]) + S->off[S->L - 1].dy, dy));
+  ZB_TRY(run_backward(S, mb, dx, unsplit, beta));
+  S->fb.release(S->s_fb[mb]);
+  S->s_fb[mb] = -1;
+  if (unsplit) {
+    release_all(S, mb);
+    S->st[mb] = MB_DONE;
+    S->w_count += 1;
+  } else {
+    S->st[mb] = MB_B;
+  }
+  return ZB_OK;
+}
+
+zb_status do_weight(zb_stage* S, int mb) {
+  ZB_TRY(check_mb(S, mb));
+  if (S->st[mb] != MB_B)
+    return set_error(ZB_E_STATE, "stage %d mb %d: W needs its B first (and runs once)", S->index, mb);
+  ZB_TRY(run_weight(S, mb, S->w_count > 0 ? 1 : 0));
+  release_all(S, mb);
+  S->st[mb] = MB_DONE;
+  S->w_count += 1;
+  return ZB_OK;
+}
+
+}  // namespace
+
+// ================================================================== ABI
+
+extern "C" zb_status zb_stage_create(const zb_stage_desc* d, int stage_index, const void* const* weights,
+                                     float* const* dw, void* stream, zb_stage** out) {
+  clear_error();
+  if (!d || !weights || !dw || !out) return set_error(ZB_E_ARG, "null argument");
+  *out = nullptr;
+  if (d->kind < ZB_KIND_TINY_MLP || d->kind > ZB_KIND_FULL) return set_error(ZB_E_ARG, "kind");
+  if (d->dtype != ZB_DTYPE_BF16 && d->dtype != ZB_DTYPE_FP32) return set_error(ZB_E_ARG, "dtype");
+  if (d->gelu != ZB_GELU_ERF && d->gelu != ZB_GELU_TANH) return set_error(ZB_E_ARG, "gelu");
+  if (d->n_layers < 1 || d->hidden < 1 || d->ffn < 1 || d->seq < 1 || d->micro_batch < 1 || d->n_micro < 1)
+    return set_error(ZB_E_ARG, "sizes must be >= 1");
+  if (stage_index < 0) return set_error(ZB_E_ARG, "stage_index must be >= 0");
+  const int64_t T = (int64_t)d->seq * d->micro_batch;
+  if (T > (1 << 30) || (int64_t)d->hidden * 3 > (1 << 30) || d->ffn > (1 << 30)) return set_error(ZB_E_ARG, "too large");
+  if (d->hidden % 8 || d->ffn % 8 || T % 8)
+    return set_error(ZB_E_UNSUPPORTED, "hidden, ffn and seq*micro_batch must be multiples of 8");
+  if (d->kind == ZB_KIND_FULL) {
+    if (d->n_heads < 1 || d->hidden % d->n_heads || d->hidden / d->n_heads != 128)
+      return set_error(ZB_E_UNSUPPORTED, "FULL needs hidden / n_heads == 128");
+    if (d->dtype != ZB_DTYPE_BF16) return set_error(ZB_E_UNSUPPORTED, "FULL is bf16 only");
+    return set_error(ZB_E_UNSUPPORTED, "FULL layers need the attention kernels");
+  }
+  zb_stage* S = new zb_stage();
+  S->d = *d;
+  S->index = stage_index;
+  S->T = (int)T;
+  S->h = d->hidden;
+  S->f = d->ffn;
+  S->L = d->n_layers;
+  S->nlin = linears_per_layer(d->kind);
+  S->es = d->dtype == ZB_DTYPE_BF16 ? 2 : 4;
+  S->stream = static_cast<hipStream_t>(stream);
+  const int nw = S->L * S->nlin;
+  for (int i = 0; i < nw; ++i) {
+    if (!weights[i] || !dw[i]) {
+      delete S;
+      return set_error(ZB_E_ARG, "null weight or gradient pointer %d", i);
+    }
+    if ((reinterpret_cast<uintptr_t>(weights[i]) & 15) || (reinterpret_cast<uintptr_t>(dw[i]) & 15)) {
+      delete S;
+      return set_error(ZB_E_ARG, "weight / gradient %d not 16-byte aligned", i);
+    }
+    S->w.push_back(weights[i]);
+    S->dw.push_back(dw[i]);
+    const int which = S->d.kind == ZB_KIND_TINY_MLP ? (i % 2 == 0 ? LIN_UP : LIN_DOWN) : i % 4;
+    int64_t K = 0, N = 0;
+    switch (which) {
+      case LIN_QKV: K = S->h; N = 3LL * S->h; break;
+      case LIN_PROJ: K = S->h; N = S->h; break;
+      case LIN_UP: K = S->h; N = S->f; break;
+      default: K = S->f; N = S->h; break;
+    }
+    S->wK.push_back(K);
+    S->wN.push_back(N);
+  }
+  compute_layout(S);
+  const int m = d->n_micro;
+  S->st.assign(m, MB_IDLE);
+  S->s_fw.assign(m, -1);
+  S->s_fb.assign(m, -1);
+  S->s_bw.assign(m, -1);
+  *out = S;
+  return ZB_OK;
+}
+
+extern "C" zb_status zb_stage_class_bytes(const zb_stage* S, size_t* fw, size_t* fb, size_t* bw) {
+  clear_error();
+  if (!S || !fw || !fb || !bw) return set_error(ZB_E_ARG, "null argument");
+  *fw = S->fw_bytes;
+  *fb = S->fb_bytes;
+  *bw = S->bw_bytes;
+  return ZB_OK;
+}
+
+extern "C" zb_status zb_stage_workspace_bytes(zb_stage* S, const zb_op* ops, int n_ops, size_t* bytes) {
+  clear_error();
+  if (!S || !bytes || n_ops < 0 || (n_ops > 0 && !ops)) return set_error(ZB_E_ARG, "bad arguments");
+  int a, b, c;
+  plan_counts(S->index, S->d.n_micro, ops, n_ops, a, b, c);
+  S->plan_fw = a;
+  S->plan_fb = b;
+  S->plan_bw = c;
+  S->planned = true;
+  *bytes = ws_size(S, a, b, c);
+  return ZB_OK;
+}
+
+extern "C" zb_status zb_stage_bind_workspace(zb_stage* S, void* p, size_t bytes) {
+  clear_error();
+  if (!S || !p) return set_error(ZB_E_ARG, "null argument");
+  if (reinterpret_cast<uintptr_t>(p) % kAlign) return set_error(ZB_E_ARG, "workspace must be 256-byte aligned");
+  for (int j = 0; j < S->d.n_micro; ++j)
+    if (S->st[j] != MB_IDLE && S->st[j] != MB_DONE)
+      return set_error(ZB_E_STATE, "stage %d: microbatch %d is live", S->index, j);
+  if (!S->planned) {
+    S->plan_fw = S->plan_fb = S->plan_bw = S->d.n_micro;
+    S->planned = true;
+  }
+  const size_t need = ws_size(S, S->plan_fw, S->plan_fb, S->plan_bw);
+  if (bytes < need) return set_error(ZB_E_BUDGET, "workspace %zu bytes < planned %zu", bytes, need);
+  char* base = static_cast<char*>(p);
+  S->ws = base;
+  S->ws_bytes = bytes;
+  S->scratch = base;
+  char* q = base + S->scratch_bytes;
+  S->fw.reset(q, S->plan_fw);
+  q += (size_t)S->plan_fw * S->fw_bytes;
+  S->fb.reset(q, S->plan_fb);
+  q += (size_t)S->plan_fb * S->fb_bytes;
+  S->bw.reset(q, S->plan_bw);
+  std::fill(S->s_fw.begin(), S->s_fw.end(), -1);
+  std::fill(S->s_fb.begin(), S->s_fb.end(), -1);
+  std::fill(S->s_bw.begin(), S->s_bw.end(), -1);
+  S->bound = true;
+  return ZB_OK;
+}
+
+extern "C" zb_status zb_stage_input_slot(zb_stage* S, int mb, void** p) {
+  clear_error();
+  if (!p) return set_error(ZB_E_ARG, "null output");
+  ZB_TRY(check_mb(S, mb));
+  if (S->st[mb] != MB_IDLE) return set_error(ZB_E_STATE, "stage %d mb %d already forwarded", S->index, mb);
+  ZB_TRY(claim_fw(S, mb));
+  *p = S->fw.at(S->s_fw[mb]) + S->off[0].x;
+  return ZB_OK;
+}
+
+extern "C" zb_status zb_stage_grad_slot(zb_stage* S, int mb, void** p) {
+  clear_error();
+  if (!p) return set_error(ZB_E_ARG, "null output");
+  ZB_TRY(check_mb(S, mb));
+  if (S->st[mb] != MB_IDLE && S->st[mb] != MB_F)
+    return set_error(ZB_E_STATE, "stage %d mb %d already past its B", S->index, mb);
+  ZB_TRY(claim_bw(S, mb));
+  *p = S->bw.at(S->s_bw[mb]) + S->off[S->L - 1].dy;
+  return ZB_OK;
+}
+
+extern "C" zb_status zb_forward(zb_stage* S, int mb, const void* x, void* y) {
+  clear_error();
+  return do_forward(S, mb, x, y);
+}
+
+extern "C" zb_status zb_backward_input(zb_stage* S, int mb, const void* dy, void* dx) {
+  clear_error();
+  return do_backward(S, mb, dy, dx, false);
+}
+
+extern "C" zb_status zb_backward_unsplit(zb_stage* S, int mb, const void* dy, void* dx) {
+  clear_error();
+  return do_backward(S, mb, dy, dx, true);
+}
+
+extern "C" zb_status zb_backward_weight(zb_stage* S, int mb) {
+  clear_error();
+  return do_weight(S, mb);
+}
+
+extern "C" zb_status zb_grad_flush(zb_stage* S, int* nonfinite_out) {
+  clear_error();
+  if (!S) return set_error(ZB_E_ARG, "null stage");
+  for (int j = 0; j < S->d.n_micro; ++j)
+    if (S->st[j] != MB_DONE)
+      return set_error(ZB_E_MISSING, "stage %d: microbatch %d has no W yet; the optimizer step needs all of them",
+                       S->index, j);
+  if (nonfinite_out) {
+    if (!S->bound) return set_error(ZB_E_STATE, "no workspace");
+    int* flag = reinterpret_cast<int*>(S->scratch + S->scratch_flag);
+    ZB_TRY(launch_zero_int(flag, S->stream));
+    for (size_t i = 0; i < S->dw.size(); ++i)
+      ZB_TRY(launch_nonfinite(S->dw[i], S->wK[i] * S->wN[i], flag, S->stream));
+    int host = 0;
+    ZB_HIP_CHECK(hipMemcpyAsync(&host, flag, sizeof(int), hipMemcpyDeviceToHost, S->stream));
+    ZB_HIP_CHECK(hipStreamSynchronize(S->stream));
+    *nonfinite_out = host;
+  }
+  std::fill(S->st.begin(), S->st.end(), (int)MB_IDLE);
+  S->w_count = 0;
+  return ZB_OK;
+}
+
+extern "C" zb_status zb_run_schedule(zb_stage* const* stages, int P, const zb_op* ops, int n_ops,
+                                     const void* const* x0, const void* const* dy_last, void* const* y_last,
+                                     void* const* dx0, zb_trace_rec* trace) {
+  clear_error();
+  if (!stages || P < 1 || !ops || n_ops < 1 || !x0 || !dy_last || !y_last || !dx0)
+    return set_error(ZB_E_ARG, "null argument");
+  for (int p = 0; p < P; ++p) {
+    const zb_stage* S = stages[p];
+    if (!S) return set_error(ZB_E_ARG, "stages[%d] is null", p);
+    if (S->index != p) return set_error(ZB_E_ARG, "stages[%d] was created as stage %d", p, S->index);
+    if (S->stream != stages[0]->stream) return set_error(ZB_E_ARG, "stages must share one stream");
+    if (S->d.n_micro != stages[0]->d.n_micro || S->T != stages[0]->T || S->h != stages[0]->h ||
+        S->d.dtype != stages[0]->d.dtype)
+      return set_error(ZB_E_ARG, "stage %d: microbatch count, tokens, hidden or dtype differ", p);
+    if (!S->bound) return set_error(ZB_E_STATE, "stage %d has no workspace bound", p);
+    for (int j = 0; j < S->d.n_micro; ++j)
+      if (S->st[j] != MB_IDLE || S->s_fw[j] >= 0 || S->s_bw[j] >= 0)
+        return set_error(ZB_E_STATE, "stage %d mb %d is live (flush the previous step first)", p, j);
+  }
+  const int m = stages[0]->d.n_micro;
+  for (int j = 0; j < m; ++j)
+    if (!x0[j] || !dy_last[j] || !y_last[j] || !dx0[j]) return set_error(ZB_E_ARG, "null buffer for mb %d", j);
+  int bad = -1;
+  ZB_TRY(schedule_validate(P, m, ops, n_ops, &bad));
+  for (int p = 0; p < P; ++p) {
+    int a, b, c;
+    plan_counts(p, m, ops, n_ops, a, b, c);
+    const zb_stage* S = stages[p];
+    if (a > S->fw.n || b > S->fb.n || c > S->bw.n)
+      return set_error(ZB_E_BUDGET, "stage %d: order needs %d/%d/%d slots (F->W, F->B, B->W), workspace has %d/%d/%d",
+                       p, a, b, c, S->fw.n, S->fb.n, S->bw.n);
+  }
+  hipStream_t s = stages[0]->stream;
+  std::vector<hipEvent_t> ev;
+  if (trace) {
+    ev.resize(2 * (size_t)n_ops, nullptr);
+    for (auto& e : ev) ZB_HIP_CHECK(hipEventCreate(&e));
+  }
+  zb_status rc = ZB_OK;
+  for (int i = 0; i < n_ops && rc == ZB_OK; ++i) {
+    const zb_op& o = ops[i];
+    zb_stage* S = stages[o.stage];
+    const int j = o.mb;
+    if (trace) (void)hipEventRecord(ev[2 * i], s);
+    switch (o.kind) {
+      case 'F': {
+        void* y = y_last[j];
+        if (o.stage + 1 < P) {
+          rc = zb_stage_input_slot(stages[o.stage + 1], j, &y);
+          if (rc != ZB_OK) break;
+        }
+        const void* x = x0[j];
+        if (o.stage > 0) x = S->fw.at(S->s_fw[j]) + S->off[0].x;
+        rc = do_forward(S, j, x, y);
+        break;
+      }
+      case 'B':
+      case 'U': {
+        void* dx = dx0[j];
+        if (o.stage > 0) {
+          rc = zb_stage_grad_slot(stages[o.stage - 1], j, &dx);
+          if (rc != ZB_OK) break;
+        }
+        const void* dy = dy_last[j];
+        if (o.stage + 1 < P) dy = S->bw.at(S->s_bw[j]) + S->off[S->L - 1].dy;
+        rc = do_backward(S, j, dy, dx, o.kind == 'U');
+        break;
+      }
+      case 'W':
+        rc = do_weight(S, j);
+        break;
+      default:
+        rc = set_error(ZB_E_ARG, "op %d kind", i);
+    }
+    if (trace) (void)hipEventRecord(ev[2 * i + 1], s);
+  }
+  if (rc != ZB_OK) {
+    for (auto& e : ev) (void)hipEventDestroy(e);
+    return rc;
+  }
+  if (trace) {
+    ZB_HIP_CHECK(hipEventSynchronize(ev.back()));
+    for (int i = 0; i < n_ops; ++i) {
+      trace[i].op = ops[i];
+      float ms = 0.f, t0 = 0.f;
+      (void)hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]);
+      (void)hipEventElapsedTime(&t0, ev[0], ev[2 * i]);
+      trace[i].ms = ms;
+      trace[i].t0_ms = t0;
+    }
+    for (auto& e : ev) (void)hipEventDestroy(e);
+  }
+  return ZB_OK;
+}
+
+extern "C" void zb_stage_destroy(zb_stage* S) { delete S; }
+
+// ========================================================== single linears
+
+namespace {
+zb_status linear_args(int dtype, int T, int K, int N, const void* a, const void* b, const void* c) {
+  if (dtype != ZB_DTYPE_BF16 && dtype != ZB_DTYPE_FP32) return set_error(ZB_E_ARG, "dtype");
+  if (T < 0 || K < 0 || N < 0) return set_error(ZB_E_ARG, "negative size");
+  if ((T > 0 && K > 0 && N > 0) && (!a || !b || !c)) return set_error(ZB_E_ARG, "null pointer");
+  return ZB_OK;
+}
+}  // namespace
+
+extern "C" zb_status zb_linear_forward(int dtype, int T, int K, int N, const void* x, const void* w, void* y,
+                                       void* stream) {
+  clear_error();
+  ZB_TRY(linear_args(dtype, T, K, N, x, w, y));
+  GemmDesc g;
+  g.M = T; g.N = N; g.K = K;
+  g.A = x; g.lda = K; g.a_kcontig = true;
+  g.B = w; g.ldb = N; g.b_kcontig = false;
+  g.C = y; g.ldc = N; g.epi = EPI_STORE; g.dtype = dtype; g.tag = "f";
+  return launch_gemm(g, static_cast<hipStream_t>(stream));
+}
+
+extern "C" zb_status zb_linear_backward_input(int dtype, int T, int K, int N, const void* dy, const void* w,
+                                              void* dx, void* stream) {
+  clear_error();
+  ZB_TRY(linear_args(dtype, T, K, N, dy, w, dx));
+  GemmDesc g;
+  g.M = T; g.N = K; g.K = N;
+  g.A = dy; g.lda = N; g.a_kcontig = true;
+  g.B = w; g.ldb = N; g.b_kcontig = true;
+  g.C = dx; g.ldc = K; g.epi = EPI_STORE; g.dtype = dtype; g.tag = "b";
+  return launch_gemm(g, static_cast<hipStream_t>(stream));
+}
+
+extern "C" zb_status zb_linear_backward_weight(int dtype, int T, int K, int N, const void* x, const void* dy,
+                                               float* dw, int accumulate, void* stream) {
+  clear_error();
+  ZB_TRY(linear_args(dtype, T, K, N, x, dy, dw));
+  GemmDesc g;
+  g.M = K; g.N = N; g.K = T;
+  g.A = x; g.lda = K; g.a_kcontig = false;
+  g.B = dy; g.ldb = N; g.b_kcontig = false;
+  g.C = dw; g.ldc = N; g.epi = EPI_ACC; g.beta = accumulate ? 1 : 0; g.dtype = dtype; g.tag = "w";
+  return launch_gemm(g, static_cast<hipStream_t>(stream));
+}

@@ -1,0 +1,89 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/zb.h"
+
+namespace zb {
+
+// ---------------------------------------------------------------- errors
+zb_status set_error(zb_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+#define ZB_HIP_CHECK(expr)                                                           \
+  do {                                                                               \
+    hipError_t e_ = (expr);                                                          \
+    if (e_ != hipSuccess)                                                            \
+      return ::zb::set_error(ZB_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// -------------------------------------------------------------- schedule
+struct SimPass {
+  int op;         // index into the input op list
+  int stage;
+  int64_t start;
+  int64_t end;
+};
+
+zb_status schedule_stage_order(int order, int P, int m, int stage, std::vector<zb_op>& out);
+zb_status schedule_simulate(int P, int m, const zb_op* ops, int n_ops, const int64_t* t,
+                            int64_t t_comm, std::vector<SimPass>& passes, zb_sim_stats* stats);
+void schedule_linearize(const std::vector<SimPass>& passes, std::vector<int>& order);
+zb_status schedule_validate(int P, int m, const zb_op* ops, int n_ops, int* bad);
+
+// ----------------------------------------------------------------- kernels
+enum Epilogue {
+  EPI_STORE = 0,   // C = acc
+  EPI_RESID = 1,   // C = acc + R
+  EPI_GELU = 2,    // Z = acc; C = gelu(acc)
+  EPI_DGELU = 3,   // C = acc * gelu'(R)          (R = saved pre-activation)
+  EPI_ACC = 4      // C(fp32) = (beta ? C : 0) + acc, accumulated in the MFMA chain
+};
+
+// C[M,N] = sum_k A(m,k) B(k,n) with
+//   A(m,k) = A[m*lda + k] if a_kcontig else A[k*lda + m]
+//   B(k,n) = B[n*ldb + k] if b_kcontig else B[k*ldb + n]
+struct GemmDesc {
+  int M = 0, N = 0, K = 0;
+  const void* A = nullptr;
+  int64_t lda = 0;
+  bool a_kcontig = true;
+  const void* B = nullptr;
+  int64_t ldb = 0;
+  bool b_kcontig = true;
+  void* C = nullptr;
+  int64_t ldc = 0;
+  const void* R = nullptr;   // residual (EPI_RESID) or pre-activation (EPI_DGELU)
+  int64_t ldr = 0;
+  void* Z = nullptr;         // pre-activation output (EPI_GELU)
+  int64_t ldz = 0;
+  int epi = EPI_STORE;
+  int beta = 0;              // EPI_ACC: add into C
+  int dtype = ZB_DTYPE_BF16; // storage type of A, B, R, Z and (non-ACC) C
+  int gelu = ZB_GELU_ERF;
+  const char* tag = "gemm";  // pass name for kernel timing ("f", "b", "w")
+};
+
+zb_status launch_gemm(const GemmDesc& g, hipStream_t s);
+
+// Fill rows x cols elements (row stride ld, 2 or 4 bytes each) with zero.
+zb_status launch_zero2d(void* p, int64_t rows, int64_t cols, int64_t ld, int elem_bytes, hipStream_t s);
+// Sets *flag (device int) to 1 if any of n fp32 values is NaN/Inf (flag must be pre-zeroed).
+zb_status launch_nonfinite(const float* p, int64_t n, int* flag, hipStream_t s);
+zb_status launch_zero_int(int* flag, hipStream_t s);
+
+// --------------------------------------------------------- kernel timing
+bool prof_on();
+struct ProfScope {
+  // Brackets one kernel launch with a hipEvent pair when timing is enabled.
+  ProfScope(const char* name, double flops, double bytes, hipStream_t s);
+  ~ProfScope();
+  int slot = -1;
+  hipStream_t stream;
+};
+
+}  // namespace zb

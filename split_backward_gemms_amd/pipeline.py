@@ -1,0 +1,108 @@
+"""Device-memory plumbing for P emulated stages on one GPU.
+
+Allocates, with torch, the weights, fp32 gradient buffers, per-stage
+workspaces and microbatch I/O buffers, and calls the C ABI.  It performs no
+arithmetic of the method itself.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+import split_backward_gemms_amd as zb
+
+KIND_OF = {0: zb.ZB_KIND_TINY_MLP, 1: zb.ZB_KIND_MLP_LINEARS, 2: zb.ZB_KIND_FULL}
+
+
+def torch_dtype(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def desc_of(w) -> "zb.zb_stage_desc":
+    """Stage descriptor of a synthetic_inputs.Workload."""
+    return zb.make_desc(KIND_OF[w.kind], zb.ZB_DTYPE_BF16 if w.dtype == "bf16" else zb.ZB_DTYPE_FP32,
+                        w.n_layers, w.hidden, w.ffn, max(w.n_heads, 0), w.seq, w.micro_batch, w.n_micro)
+
+
+def upload(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """fp32 array holding bf16-exact values -> device tensor (exact conversion)."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device).to(torch_dtype(dtype))
+
+
+class EmulatedPipeline:
+    """P stages of one workload, each with its own weights, on one device and one stream."""
+
+    def __init__(self, w, weights: Sequence[Sequence[Dict[str, np.ndarray]]], ops: Optional[Sequence] = None,
+                 device: str = "cuda", stream: Optional[torch.cuda.Stream] = None):
+        self.w = w
+        self.device = torch.device(device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        self.P = w.n_stages
+        self.handles: List[int] = []
+        self.weights: List[List[torch.Tensor]] = []
+        self.grads: List[List[torch.Tensor]] = []
+        self.workspaces: List[torch.Tensor] = []
+        desc = desc_of(w)
+        names = [nm for nm, _, _ in w.linears()]
+        shapes = {nm: (k, n) for nm, k, n in w.linears()}
+        for s in range(self.P):
+            wt = [upload(weights[s][l][nm], w.dtype, self.device) for l in range(w.n_layers) for nm in names]
+            gr = [torch.empty(shapes[nm], dtype=torch.float32, device=self.device)
+                  for _ in range(w.n_layers) for nm in names]
+            h = zb.zb_stage_create(desc, s, wt, gr, self.stream.cuda_stream)
+            self.handles.append(h)
+            self.weights.append(wt)
+            self.grads.append(gr)
+        self.plan(ops)
+
+    def plan(self, ops: Optional[Sequence]) -> None:
+        """(Re)size and bind every stage's workspace for the given order (None = all m live)."""
+        self.workspaces = []
+        for h in self.handles:
+            nbytes = zb.zb_stage_workspace_bytes(h, ops)
+            buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+            off = (-buf.data_ptr()) % 256
+            zb.zb_stage_bind_workspace(h, buf.data_ptr() + off, nbytes)
+            self.workspaces.append(buf)
+
+    def workspace_bytes(self) -> int:
+        return sum(int(b.numel()) for b in self.workspaces)
+
+    def io_buffers(self):
+        w = self.w
+        shape = (w.tokens, w.hidden)
+        dt = torch_dtype(w.dtype)
+        y = [torch.empty(shape, dtype=dt, device=self.device) for _ in range(w.n_micro)]
+        dx = [torch.empty(shape, dtype=dt, device=self.device) for _ in range(w.n_micro)]
+        return y, dx
+
+    def run(self, ops, xs: Sequence[torch.Tensor], dys: Sequence[torch.Tensor], y_last, dx0, trace: bool = False,
+            flush: bool = True, check_finite: bool = False):
+        tr = zb.zb_run_schedule(self.handles, ops, xs, dys, y_last, dx0, trace=trace)
+        flags = None
+        if flush:
+            flags = [zb.zb_grad_flush(h, check_finite) for h in self.handles]
+        return tr, flags
+
+    def grads_host(self) -> List[List[Dict[str, np.ndarray]]]:
+        names = [nm for nm, _, _ in self.w.linears()]
+        out = []
+        for s in range(self.P):
+            per = []
+            for l in range(self.w.n_layers):
+                per.append({nm: self.grads[s][l * len(names) + i].cpu().numpy() for i, nm in enumerate(names)})
+            out.append(per)
+        return out
+
+    def close(self) -> None:
+        for h in self.handles:
+            zb.zb_stage_destroy(h)
+        self.handles = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,292 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+* Each GEMM layout (F, B, W) on small-integer inputs: the fp32 accumulators
+  hold exact integers, so F/B outputs must equal the bf16 rounding of the exact
+  result bit for bit and W must be exact; shapes span several tiles, every tile
+  configuration and ragged M/N/K tails.
+* Whole pipelines (P emulated stages, m microbatches) in several orders against
+  oracle.stage.pipeline: |gpu - ref| <= 2e-2 * max|ref| per tensor.
+* Deferred W: flushed fp32 gradients are bit-identical across 1F1B, ZB-H1,
+  ZB-H2 and W-last orders, and across steps.
+"""
+import numpy as np
+import pytest
+import torch
+
+import split_backward_gemms_amd as zb
+import synthetic_inputs as si
+from oracle import stage as ost
+from oracle import schedules as sch
+from split_backward_gemms_amd.pipeline import EmulatedPipeline, upload
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
+    scale = float(np.max(np.abs(ref)))
+    return float(np.max(np.abs(gpu.astype(np.float64) - ref))) / (scale if scale > 0 else 1.0)
+
+
+def _host(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy()
+
+
+# --------------------------------------------------------------- linears
+
+INT_SHAPES = [
+    (64, 64, 64),          # one partial tile
+    (200, 136, 328),       # ragged M, N, K against every tile size
+    (520, 264, 392),       # several tiles + ragged tails
+    (1024, 2048, 1024),    # 128x128 / 256x128 tiles
+    (4096, 4096, 256),     # B picks 256x256 tiles
+    (4096, 256, 4096),     # F picks 256x256 tiles
+    (8, 8, 8),             # smallest legal shape
+]
+
+
+@pytest.mark.parametrize("T,K,N", INT_SHAPES)
+def test_linear_passes_exact_on_integers(T, K, N):
+    print(f"linear exact T={T} K={K} N={N}", flush=True)
+    x = si.integer_valued((T, K), -2, 2, seed=T + 1)
+    w = si.integer_valued((K, N), -2, 2, seed=K + 2)
+    dy = si.integer_valued((T, N), -2, 2, seed=N + 3)
+    dw0 = si.integer_valued((K, N), -100, 100, seed=4)
+    X, Wt, DY = (upload(a, "bf16", "cuda") for a in (x, w, dy))
+    Y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    DX = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    DW = torch.from_numpy(dw0).cuda()
+    zb.zb_linear_forward(X, Wt, Y, _stream())
+    zb.zb_linear_backward_input(DY, Wt, DX, _stream())
+    zb.zb_linear_backward_weight(X, DY, DW, True, _stream())
+    torch.cuda.synchronize()
+    y_ref = ost.linear_forward(x.astype(np.float64), w.astype(np.float64))
+    dx_ref = ost.linear_backward_input(dy.astype(np.float64), w.astype(np.float64))
+    dw_ref = dw0 + ost.linear_backward_weight(x.astype(np.float64), dy.astype(np.float64))
+    y_bits = Y.view(torch.int16).cpu().numpy().view(np.uint16)
+    dx_bits = DX.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(y_bits, si.to_bf16_bits(y_ref.astype(np.float32)))
+    assert np.array_equal(dx_bits, si.to_bf16_bits(dx_ref.astype(np.float32)))
+    assert np.array_equal(DW.cpu().numpy(), dw_ref.astype(np.float32))
+    # overwrite mode ignores the buffer's old contents
+    zb.zb_linear_backward_weight(X, DY, DW, False, _stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(DW.cpu().numpy(), (dw_ref - dw0).astype(np.float32))
+
+
+@pytest.mark.parametrize("T,K,N", [(520, 264, 392), (1024, 2048, 1024)])
+def test_linear_passes_random_within_tolerance(T, K, N):
+    rng = np.random.default_rng(5)
+    x = si.round_bf16(rng.standard_normal((T, K)).astype(np.float32))
+    w = si.round_bf16((0.02 * rng.standard_normal((K, N))).astype(np.float32))
+    dy = si.round_bf16(rng.standard_normal((T, N)).astype(np.float32))
+    X, Wt, DY = (upload(a, "bf16", "cuda") for a in (x, w, dy))
+    Y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    DX = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    DW = torch.empty((K, N), dtype=torch.float32, device="cuda")
+    zb.zb_linear_forward(X, Wt, Y, _stream())
+    zb.zb_linear_backward_input(DY, Wt, DX, _stream())
+    zb.zb_linear_backward_weight(X, DY, DW, False, _stream())
+    torch.cuda.synchronize()
+    x64, w64, dy64 = x.astype(np.float64), w.astype(np.float64), dy.astype(np.float64)
+    assert _rel_err(_host(Y), ost.linear_forward(x64, w64)) < 1e-2
+    assert _rel_err(_host(DX), ost.linear_backward_input(dy64, w64)) < 1e-2
+    assert _rel_err(DW.cpu().numpy(), ost.linear_backward_weight(x64, dy64)) < 1e-5
+
+
+def test_linear_fp32_mode_exact_on_integers():
+    T, K, N = 200, 136, 328
+    x = si.integer_valued((T, K), -3, 3, seed=11)
+    w = si.integer_valued((K, N), -3, 3, seed=12)
+    dy = si.integer_valued((T, N), -3, 3, seed=13)
+    X, Wt, DY = (torch.from_numpy(a).cuda() for a in (x, w, dy))
+    Y = torch.empty((T, N), device="cuda")
+    DX = torch.empty((T, K), device="cuda")
+    DW = torch.empty((K, N), device="cuda")
+    zb.zb_linear_forward(X, Wt, Y, _stream())
+    zb.zb_linear_backward_input(DY, Wt, DX, _stream())
+    zb.zb_linear_backward_weight(X, DY, DW, False, _stream())
+    torch.cuda.synchronize()
+    x64, w64, dy64 = x.astype(np.float64), w.astype(np.float64), dy.astype(np.float64)
+    assert np.array_equal(Y.cpu().numpy(), ost.linear_forward(x64, w64))
+    assert np.array_equal(DX.cpu().numpy(), ost.linear_backward_input(dy64, w64))
+    assert np.array_equal(DW.cpu().numpy(), ost.linear_backward_weight(x64, dy64))
+
+
+# ------------------------------------------------------------- pipelines
+
+def _inputs(w):
+    ws = [si.stage_weights(w, s) for s in range(w.n_stages)]
+    xs = [si.stage_input(w, j) for j in range(w.n_micro)]
+    dys = [si.last_stage_grad(w, j) for j in range(w.n_micro)]
+    return ws, xs, dys
+
+
+def _run(w, ws, xs, dys, order, pipe=None):
+    ops, _ = zb.zb_schedule_build(order, w.n_stages, w.n_micro)
+    if pipe is None:
+        pipe = EmulatedPipeline(w, ws, ops=ops)
+    X = [upload(x, w.dtype, "cuda") for x in xs]
+    DY = [upload(d, w.dtype, "cuda") for d in dys]
+    y, dx = pipe.io_buffers()
+    pipe.run(ops, X, DY, y, dx)
+    torch.cuda.synchronize()
+    return pipe, [_host(t) for t in y], [_host(t) for t in dx], pipe.grads_host(), ops
+
+
+REDUCED = {
+    "tiny_bf16": si.WORKLOADS["tiny"],
+    "tiny_fp32": si.WORKLOADS["tiny"].replace(dtype="fp32"),
+    "mlp_linears_reduced": si.reduced(si.WORKLOADS["gpt_mlp_h2048"], hidden=256, seq=128),
+    "mlp_linears_ragged": si.reduced(si.WORKLOADS["gpt_mlp_h2048"], hidden=200, seq=104, n_micro=4,
+                                     n_stages=2, n_layers=2).replace(ffn=328),
+}
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+@pytest.mark.parametrize("order", ["zbh1", "1f1b"])
+def test_pipeline_matches_oracle(name, order):
+    w = REDUCED[name]
+    print(f"pipeline parity {name} {order}", flush=True)
+    ws, xs, dys = _inputs(w)
+    pipe, y, dx, dw, _ = _run(w, ws, xs, dys, order)
+    pipe.close()
+    ref = ost.pipeline(w, ws, xs, dys)
+    P = w.n_stages
+    errs = []
+    for j in range(w.n_micro):
+        errs.append(_rel_err(y[j], ref["y"][P - 1][j]))
+        errs.append(_rel_err(dx[j], ref["dx"][0][j]))
+    for s in range(P):
+        for l in range(w.n_layers):
+            for nm in dw[s][l]:
+                errs.append(_rel_err(dw[s][l][nm], ref["dw"][s][l][nm]))
+    print(f"max rel err {max(errs):.3e}", flush=True)
+    bound = 1e-4 if w.dtype == "fp32" else TOL
+    assert max(errs) <= bound
+
+
+@pytest.mark.parametrize("name", ["tiny_bf16", "mlp_linears_reduced"])
+def test_deferred_w_bit_exact_across_orders(name):
+    w = REDUCED[name]
+    ws, xs, dys = _inputs(w)
+    pipe = EmulatedPipeline(w, ws, ops=None)  # every microbatch may be live: any order fits
+    results = {}
+    orders = ["1f1b", "zbh1", "wlast", "gpipe"] + (["zbh2"] if w.n_micro >= 2 * w.n_stages - 1 else [])
+    for order in orders:
+        _, y, dx, dw, _ = _run(w, ws, xs, dys, order, pipe)
+        results[order] = (y, dx, dw)
+    _, y2, dx2, dw2, _ = _run(w, ws, xs, dys, "zbh1", pipe)  # a second step reproduces the first
+    pipe.close()
+    base_y, base_dx, base_dw = results["1f1b"]
+    for order, (y, dx, dw) in list(results.items()) + [("zbh1-again", (y2, dx2, dw2))]:
+        for j in range(w.n_micro):
+            assert np.array_equal(y[j], base_y[j]), order
+            assert np.array_equal(dx[j], base_dx[j]), order
+        for s in range(w.n_stages):
+            for l in range(w.n_layers):
+                for nm in dw[s][l]:
+                    assert np.array_equal(dw[s][l][nm].view(np.uint32), base_dw[s][l][nm].view(np.uint32)), \
+                        (order, s, l, nm)
+
+
+def test_single_stage_api_order_errors():
+    w = REDUCED["tiny_bf16"]
+    ws, xs, dys = _inputs(w)
+    pipe = EmulatedPipeline(w.replace(n_stages=1), ws[:1], ops=None)
+    h = pipe.handles[0]
+    X = upload(xs[0], "bf16", "cuda")
+    DY = upload(dys[0], "bf16", "cuda")
+    y, dx = pipe.io_buffers()
+    with pytest.raises(zb.ZbError) as e:
+        zb.zb_backward_input(h, 0, DY, dx[0])
+    assert e.value.status == zb.ZB_E_STATE
+    with pytest.raises(zb.ZbError) as e:
+        zb.zb_backward_weight(h, 0)
+    assert e.value.status == zb.ZB_E_STATE
+    zb.zb_forward(h, 0, X, y[0])
+    with pytest.raises(zb.ZbError) as e:
+        zb.zb_forward(h, 0, X, y[0])
+    assert e.value.status == zb.ZB_E_STATE
+    zb.zb_backward_input(h, 0, DY, dx[0])
+    with pytest.raises(zb.ZbError) as e:
+        zb.zb_grad_flush(h)
+    assert e.value.status == zb.ZB_E_MISSING
+    zb.zb_backward_weight(h, 0)
+    with pytest.raises(zb.ZbError) as e:
+        zb.zb_backward_weight(h, 0)
+    assert e.value.status == zb.ZB_E_STATE
+    with pytest.raises(zb.ZbError) as e:
+        zb.zb_forward(h, 99, X, y[0])
+    assert e.value.status == zb.ZB_E_INVALID_MB
+    for j in range(1, w.n_micro):
+        zb.zb_forward(h, j, upload(xs[j], "bf16", "cuda"), y[j])
+        zb.zb_backward_unsplit(h, j, upload(dys[j], "bf16", "cuda"), dx[j])
+    assert zb.zb_grad_flush(h, check_finite=True) == 0
+    torch.cuda.synchronize()
+    pipe.close()
+
+
+def test_run_schedule_rejects_before_launch():
+    w = REDUCED["tiny_bf16"]
+    ws, xs, dys = _inputs(w)
+    ops_h1, _ = zb.zb_schedule_build("zbh1", w.n_stages, w.n_micro)
+    pipe = EmulatedPipeline(w, ws, ops=ops_h1)
+    X = [upload(x, "bf16", "cuda") for x in xs]
+    DY = [upload(d, "bf16", "cuda") for d in dys]
+    y, dx = pipe.io_buffers()
+    bad = list(ops_h1)
+    i = next(k for k, op in enumerate(bad) if op[1] == "B")
+    bad.insert(0, bad.pop(i))
+    with pytest.raises(zb.ZbError) as e:
+        zb.zb_run_schedule(pipe.handles, bad, X, DY, y, dx)
+    assert e.value.status == zb.ZB_E_DEPENDENCY
+    # GPipe keeps all m microbatches live: more than the ZB-H1 plan provides
+    ops_gp, _ = zb.zb_schedule_build("gpipe", w.n_stages, w.n_micro)
+    with pytest.raises(zb.ZbError) as e:
+        zb.zb_run_schedule(pipe.handles, ops_gp, X, DY, y, dx)
+    assert e.value.status == zb.ZB_E_BUDGET
+    # nothing was launched: the planned order still runs and matches the oracle
+    pipe.run(ops_h1, X, DY, y, dx)
+    torch.cuda.synchronize()
+    ref = ost.pipeline(w, ws, xs, dys)
+    assert _rel_err(_host(y[0]), ref["y"][-1][0]) < TOL
+    pipe.close()
+
+
+def test_nonfinite_gradient_is_flagged():
+    w = REDUCED["tiny_bf16"]
+    ws, xs, dys = _inputs(w)
+    dys = [d.copy() for d in dys]
+    dys[1][3, 5] = np.nan
+    ops, _ = zb.zb_schedule_build("zbh1", w.n_stages, w.n_micro)
+    pipe = EmulatedPipeline(w, ws, ops=ops)
+    X = [upload(x, "bf16", "cuda") for x in xs]
+    DY = [upload(d, "bf16", "cuda") for d in dys]
+    y, dx = pipe.io_buffers()
+    _, flags = pipe.run(ops, X, DY, y, dx, check_finite=True)
+    assert flags == [1] * w.n_stages
+    pipe.close()
+
+
+def test_trace_follows_the_linearized_order():
+    w = REDUCED["mlp_linears_reduced"]
+    ws, xs, dys = _inputs(w)
+    ops, _ = zb.zb_schedule_build("zbh1", w.n_stages, w.n_micro)
+    lin_oracle = sch.linearize(sch.stage_orders("zbh1", w.n_stages, w.n_micro),
+                               sch.simulate(sch.stage_orders("zbh1", w.n_stages, w.n_micro), dict(F=1, B=1, W=1)))
+    assert ops == lin_oracle
+    pipe = EmulatedPipeline(w, ws, ops=ops)
+    X = [upload(x, "bf16", "cuda") for x in xs]
+    DY = [upload(d, "bf16", "cuda") for d in dys]
+    y, dx = pipe.io_buffers()
+    tr, _ = pipe.run(ops, X, DY, y, dx, trace=True)
+    assert [r[0] for r in tr] == lin_oracle
+    assert all(r[1] > 0 for r in tr)
+    starts = [r[2] for r in tr]
+    assert starts == sorted(starts)
+    pipe.close()

@@ -1,0 +1,191 @@
+"""The native schedule layer (libzb.so, host code only) against the oracle.
+
+Bit-exact on pass orders, simulated statistics, one-device linearization,
+validator verdicts (crafted and randomly perturbed orders), memory peaks and
+the audit page's timed-event checks.  No GPU is touched.
+"""
+import json
+import os
+import random
+from fractions import Fraction
+
+import pytest
+
+import split_backward_gemms_amd as zb
+from oracle import schedules as sch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+NAMES = ["gpipe", "1f1b", "zbh1", "zbh2", "wlast"]
+CASES = [(2, 4), (4, 8), (4, 16), (8, 24), (8, 32), (3, 7), (1, 3)]
+TIMES = [(1, 1, 1), (2, 3, 1), (3, 4, 2), (5, 7, 3), (1, 2, 2)]
+
+ORACLE_STATUS = {sch.OK: zb.ZB_OK, sch.E_ARG: zb.ZB_E_ARG, sch.E_DUPLICATE: zb.ZB_E_DUPLICATE,
+                 sch.E_INVALID_STAGE: zb.ZB_E_INVALID_STAGE, sch.E_INVALID_MB: zb.ZB_E_INVALID_MB,
+                 sch.E_MISSING: zb.ZB_E_MISSING, sch.E_DEPENDENCY: zb.ZB_E_DEPENDENCY}
+
+
+@pytest.mark.parametrize("name", NAMES)
+@pytest.mark.parametrize("P,m", CASES)
+def test_stage_orders_match_oracle(name, P, m):
+    if name == "zbh2" and m < 2 * P - 1:
+        with pytest.raises(zb.ZbError):
+            zb.zb_schedule_stage_order(name, P, m, 0)
+        return
+    for s in range(P):
+        native = [(k, j) for _, k, j in zb.zb_schedule_stage_order(name, P, m, s)]
+        assert native == sch.ORDERS[name](P, m, s)
+
+
+@pytest.mark.parametrize("name", NAMES)
+@pytest.mark.parametrize("P,m", CASES)
+@pytest.mark.parametrize("t", TIMES)
+def test_simulation_and_linearization_bit_exact(name, P, m, t):
+    if name == "zbh2" and m < 2 * P - 1:
+        return
+    lin, st = zb.zb_schedule_build(name, P, m, t)
+    orders = sch.stage_orders(name, P, m)
+    r = sch.simulate(orders, dict(F=t[0], B=t[1], W=t[2]))
+    assert lin == sch.linearize(orders, r)
+    assert (st["makespan"], st["span"], st["busy"], st["ideal"], st["bubble"]) == (
+        r.makespan, r.span, r.busy, r.ideal, r.bubble)
+
+
+def test_simulate_with_comm_matches_oracle():
+    for name in ("1f1b", "zbh1", "zbh2"):
+        orders = sch.stage_orders(name, 4, 8)
+        flat = [(s, k, j) for s, o in enumerate(orders) for k, j in o]
+        lin, start, end, st = zb.zb_schedule_simulate(4, 8, flat, (3, 4, 2), t_comm=1)
+        r = sch.simulate(orders, dict(F=3, B=4, W=2), t_comm=1)
+        assert lin == sch.linearize(orders, r)
+        assert [r.start[(s, k, j)] for s, k, j in lin] == start
+        assert [r.end[(s, k, j)] for s, k, j in lin] == end
+        assert st["makespan"] == r.makespan
+
+
+def test_closed_forms_native():
+    assert zb.zb_schedule_build("1f1b", 4, 8)[1]["bubble"] == 9  # (P-1)(T_F+T_B+T_W)
+    st = zb.zb_schedule_build("1f1b", 4, 8)[1]
+    assert Fraction(st["bubble"], st["makespan"]) == Fraction(3, 11)
+    assert zb.zb_schedule_build("zbh1", 4, 8)[1]["bubble"] == 3
+    assert zb.zb_schedule_build("zbh2", 4, 8)[1]["bubble"] == 0
+
+
+def test_interleaved_table_native():
+    g = json.load(open(os.path.join(GOLDEN, "tut_interleaved_bubble_table.json")))
+    for row in g["rows"]:
+        for v in (1, 2, 4):
+            st = zb.zb_schedule_simulate_interleaved(row["P"], row["m"], v)
+            rate = Fraction(st["bubble"], st["makespan"])
+            assert rate == Fraction(row["P"] - 1, v * row["m"] + row["P"] - 1)
+            assert round(100 * float(rate), 1) == row["v%d" % v]
+
+
+def _perturb(ops, rng):
+    ops = list(ops)
+    r = rng.random()
+    if r < 0.3 and len(ops) > 1:
+        i, j = rng.randrange(len(ops)), rng.randrange(len(ops))
+        ops[i], ops[j] = ops[j], ops[i]
+    elif r < 0.45:
+        del ops[rng.randrange(len(ops))]
+    elif r < 0.6:
+        ops.insert(rng.randrange(len(ops) + 1), ops[rng.randrange(len(ops))])
+    elif r < 0.7:
+        i = rng.randrange(len(ops))
+        s, k, j = ops[i]
+        ops[i] = (s + rng.choice([-9, 9]), k, j)
+    elif r < 0.8:
+        i = rng.randrange(len(ops))
+        s, k, j = ops[i]
+        ops[i] = (s, k, j + rng.choice([-5, 50]))
+    elif r < 0.85:
+        i = rng.randrange(len(ops))
+        s, k, j = ops[i]
+        ops[i] = (s, rng.choice("XUB"), j)
+    else:
+        i = rng.randrange(len(ops) - 1) if len(ops) > 1 else 0
+        ops[i:i + 2] = ops[i:i + 2][::-1]
+    return ops
+
+
+def test_validator_matches_oracle_on_perturbed_orders():
+    rng = random.Random(1234)
+    for trial in range(1500):
+        name = rng.choice(NAMES)
+        P, m = rng.choice([(2, 4), (3, 5), (4, 8)])
+        if name == "zbh2" and m < 2 * P - 1:
+            name = "zbh1"
+        lin, _ = zb.zb_schedule_build(name, P, m)
+        ops = lin
+        for _ in range(rng.randint(0, 3)):
+            ops = _perturb(ops, rng)
+        want = sch.validate_linear(P, m, ops)
+        got = zb.zb_schedule_validate(P, m, ops)
+        assert got == (ORACLE_STATUS[want[0]], want[1]), (trial, name, P, m)
+
+
+def test_validator_good_orders_and_empty():
+    for name in NAMES:
+        lin, _ = zb.zb_schedule_build(name, 4, 8)
+        assert zb.zb_schedule_validate(4, 8, lin) == (zb.ZB_OK, -1)
+    st, bad = zb.zb_schedule_validate(2, 2, [])
+    assert st == zb.ZB_E_MISSING and bad == 0
+
+
+@pytest.mark.parametrize("P", [2, 4, 8])
+def test_peak_memory_native(P):
+    m = 3 * P
+    for name in ("1f1b", "zbh1", "zbh2"):
+        lin, _ = zb.zb_schedule_build(name, P, m)
+        for s in range(P):
+            got = zb.zb_schedule_peak_memory(lin, s, 7, 5)
+            assert got == sch.peak_memory(sch.ORDERS[name](P, m, s), 7, 5)
+    lin, _ = zb.zb_schedule_build("zbh2", P, m)
+    assert zb.zb_schedule_peak_memory(lin, 0, 7, 5) == (2 * P - 1) * 7
+
+
+def test_events_inspect_audit_golden():
+    g = json.load(open(os.path.join(GOLDEN, "aud_worked_schedule.json")))
+    st, rep, bad = zb.zb_events_inspect(g["tasks"], g["stage_count"])
+    assert st == zb.ZB_OK
+    assert rep["span"] == 8 and rep["unfinished_activations"] == 0
+    assert rep["bubble_ratio"] == 0.25
+    want = {"duplicate_task": zb.ZB_E_DUPLICATE, "invalid_stage": zb.ZB_E_INVALID_STAGE,
+            "stage_overlap": zb.ZB_E_OVERLAP, "dependency_violation": zb.ZB_E_DEPENDENCY}
+    for case in g["rejections"]:
+        st, _, _ = zb.zb_events_inspect(g["tasks"] + [case["extra"]], 2)
+        assert st == want[case["error"]]
+    assert zb.zb_events_inspect(g["tasks"], 1)[0] == zb.ZB_E_ARG
+    bad_dep = [dict(t) for t in g["tasks"]]
+    bad_dep[3]["depends_on"] = ["nope"]
+    assert zb.zb_events_inspect(bad_dep, 2)[0] == zb.ZB_E_MISSING
+    bad_iv = [dict(t) for t in g["tasks"]]
+    bad_iv[0]["end"] = 0
+    assert zb.zb_events_inspect(bad_iv, 2)[0] == zb.ZB_E_INTERVAL
+
+
+def test_events_inspect_matches_oracle_on_simulated_schedules():
+    """A simulated schedule, exported as timed events with its dependency edges,
+    passes both inspectors with the same span and ratio."""
+    for name in ("1f1b", "zbh1", "zbh2"):
+        P, m = 4, 8
+        orders = sch.stage_orders(name, P, m)
+        r = sch.simulate(orders, dict(F=2, B=3, W=1))
+        tasks = []
+        for s, o in enumerate(orders):
+            for k, j in o:
+                deps = []
+                if k == "F" and s > 0:
+                    deps.append(f"{s-1}F{j}")
+                if k in "BU" and s < P - 1:
+                    deps.append(f"{s+1}{'U' if name == '1f1b' else 'B'}{j}")
+                if k == "W":
+                    deps.append(f"{s}B{j}")
+                tasks.append({"id": f"{s}{k}{j}", "stage": s, "micro": j, "kind": k,
+                              "start": r.start[(s, k, j)], "end": r.end[(s, k, j)], "depends_on": deps})
+        want = sch.inspect_events(tasks, P)
+        st, got, _ = zb.zb_events_inspect(tasks, P)
+        assert st == zb.ZB_OK
+        assert got["span"] == want["span"] and got["busy"] == want["busy"]
+        assert abs(got["bubble_ratio"] - float(want["bubble_ratio"])) < 1e-12
