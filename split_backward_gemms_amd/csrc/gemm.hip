@@ -37,6 +37,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BKT = 64;   // K per LDS tile
 constexpr int NT = 256;   // threads per workgroup
@@ -146,6 +147,18 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
 
 // ------------------------------------------------------------- bf16 MFMA GEMM
 
+// Global memory is read and written through buffer resources: an access whose
+// byte offset is at or past the operand's extent returns zero (loads) or is
+// dropped (stores).  Lanes outside the matrix get an offset of kOOB, so edge
+// tiles need no branches.  Every operand extent is below 2 GiB (checked on the
+// host), so kOOB plus any in-range step stays out of range without wrapping.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t extent_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)extent_bytes, kRsrcWord3);
+}
+
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 __device__ __forceinline__ uint32_t half_of(const u32x4& v, int e) {
@@ -153,112 +166,125 @@ __device__ __forceinline__ uint32_t half_of(const u32x4& v, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-// One operand tile of ROWS x 64 (rows = m or n, columns = k) moved global -> regs -> LDS.
-// KCONTIG: element (row, k) at base[row * ld + k]; otherwise at base[k * ld + row].
-// The per-thread base pointer and row validity are fixed at construction; a
-// tile load only adds the k offset.  Rows past rows_lim read as zero; columns
-// past K read as zero only in loads made with CHECK_K (the last, partial tile).
+// One operand tile of ROWS x 64 (rows = m or n, columns = k) moved global ->
+// registers -> LDS.  KCONTIG: element (row, k) at base[row * ld + k];
+// otherwise at base[k * ld + row].  In LDS the tile is [ROWS][64] bf16 with
+// the 16-byte chunks of row r at chunk ^ swz(r).
 template <int ROWS, bool KCONTIG>
 struct TileLoader {
   static constexpr int NREG = ROWS / 32;  // 16-byte registers per thread
   static constexpr int KR = NREG;         // m/n-contiguous: k rows per thread (8 or 4)
   static constexpr int MCH = ROWS / 64;   // m/n-contiguous: 64-wide column groups
   u32x4 r[NREG];
-  const uint16_t* ptr;  // this thread's first element
-  int64_t ld;
-  uint32_t row_ok;      // bit i: register i's row (KCONTIG) / the column block is in range
-  int kofs;             // k of this thread's first element within a tile
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff[NREG];   // byte offset of register i's 16 bytes at k0 = 0 (kOOB if outside)
+  uint32_t kstep;        // bytes per unit of k
+  int kofs;              // k of this thread's first element within a tile
+  uint32_t lds_off[KCONTIG ? 2 : 8];
 
-  __device__ __forceinline__ TileLoader(const uint16_t* base, int64_t ld_, int row0, int rows_lim, int tid) : ld(ld_) {
-    row_ok = 0;
+  __device__ __forceinline__ TileLoader(const uint16_t* base, int64_t ld, int row0, int rows_lim, int K,
+                                        int tid) {
     if constexpr (KCONTIG) {
+      const int64_t extent = ((int64_t)(rows_lim - 1) * ld + K) * 2;
+      rsrc = make_rsrc(base, (uint32_t)extent);
+      kstep = 2;
       const int row = tid >> 3;
       kofs = (tid & 7) * 8;
-      ptr = base + (int64_t)(row0 + row) * ld + kofs;
 #pragma unroll
-      for (int i = 0; i < NREG; ++i)
-        if (row0 + row + i * (NT / 8) < rows_lim) row_ok |= 1u << i;
+      for (int i = 0; i < NREG; ++i) {
+        const int gr = row0 + row + i * (NT / 8);
+        voff[i] = gr < rows_lim ? (uint32_t)(((int64_t)gr * ld + kofs) * 2) : kOOB;
+      }
+      // LDS: row = tid/8 + 32 i, chunk c = tid % 8; swz(row) = (tid/8 % 8) ^ (tid/64) ^ 4 (i % 2)
+      const int c = tid & 7, sw = ((tid >> 3) & 7) ^ (tid >> 6);
+      lds_off[0] = (tid >> 3) * 128 + ((c ^ sw) << 4);
+      lds_off[1] = (tid >> 3) * 128 + ((c ^ sw ^ 4) << 4);
     } else {
+      const int64_t extent = ((int64_t)(K - 1) * ld + rows_lim) * 2;
+      rsrc = make_rsrc(base, (uint32_t)extent);
+      kstep = (uint32_t)(ld * 2);
       const int mc = (tid & 7) + 8 * ((tid >> 6) % MCH);
       const int kg = ((tid >> 3) & 7) + 8 * ((tid >> 6) / MCH);
       kofs = kg * KR;
-      ptr = base + (int64_t)kofs * ld + row0 + mc * 8;
-      row_ok = (row0 + mc * 8 < rows_lim) ? 0xffffffffu : 0u;
+      const int gc = row0 + mc * 8;
+#pragma unroll
+      for (int i = 0; i < KR; ++i)
+        voff[i] = gc < rows_lim ? (uint32_t)(((int64_t)(kofs + i) * ld + gc) * 2) : kOOB;
+      // LDS: column e of the 8-wide block goes to row mc*8+e; swz(row) = e ^ (mc % 8)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (KR == 8)
+          lds_off[e] = (mc * 8 + e) * 128 + ((kg ^ e ^ (mc & 7)) << 4);
+        else
+          lds_off[e] = (mc * 8 + e) * 128 + ((((kg >> 1) ^ e ^ (mc & 7))) << 4) + 8 * (kg & 1);
+      }
     }
   }
 
   template <bool CHECK_K>
   __device__ __forceinline__ void load(int k0, int K) {
-    if constexpr (KCONTIG) {
-      const uint16_t* q = ptr + k0;
+    const uint32_t step = (uint32_t)k0 * kstep;
 #pragma unroll
-      for (int i = 0; i < NREG; ++i) {
-        bool ok = (row_ok >> i) & 1u;
-        if constexpr (CHECK_K) ok = ok && (k0 + kofs < K);
-        r[i] = ok ? *reinterpret_cast<const u32x4*>(q + (int64_t)i * (NT / 8) * ld) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < NREG; ++i) {
+      uint32_t off = voff[i] + step;
+      if constexpr (CHECK_K) {
+        const int k = KCONTIG ? (k0 + kofs) : (k0 + kofs + i);
+        off = k < K ? off : kOOB;
       }
-    } else {
-      const uint16_t* q = ptr + (int64_t)k0 * ld;
-#pragma unroll
-      for (int i = 0; i < KR; ++i) {
-        bool ok = row_ok & 1u;
-        if constexpr (CHECK_K) ok = ok && (k0 + kofs + i < K);
-        r[i] = ok ? *reinterpret_cast<const u32x4*>(q + (int64_t)i * ld) : u32x4{0u, 0u, 0u, 0u};
-      }
+      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 0));
     }
   }
 
-  __device__ __forceinline__ void store(uint16_t* s, int tid) const {
+  __device__ __forceinline__ void store(char* s) const {
     if constexpr (KCONTIG) {
 #pragma unroll
-      for (int i = 0; i < NREG; ++i) {
-        const int row = (tid >> 3) + i * (NT / 8), c = tid & 7;
-        *reinterpret_cast<u32x4*>(s + row * BKT + ((c ^ swz(row)) << 3)) = r[i];
-      }
+      for (int i = 0; i < NREG; ++i)
+        *reinterpret_cast<u32x4*>(s + lds_off[i & 1] + i * (NT / 8) * 128) = r[i];
     } else {
-      const int mc = (tid & 7) + 8 * ((tid >> 6) % MCH);
-      const int kg = ((tid >> 3) & 7) + 8 * ((tid >> 6) / MCH);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int row = mc * 8 + e;
         if constexpr (KR == 8) {
           u32x4 v;
           v[0] = half_of(r[0], e) | (half_of(r[1], e) << 16);
           v[1] = half_of(r[2], e) | (half_of(r[3], e) << 16);
           v[2] = half_of(r[4], e) | (half_of(r[5], e) << 16);
           v[3] = half_of(r[6], e) | (half_of(r[7], e) << 16);
-          *reinterpret_cast<u32x4*>(s + row * BKT + ((kg ^ swz(row)) << 3)) = v;
+          *reinterpret_cast<u32x4*>(s + lds_off[e]) = v;
         } else {
           u32x2 v;
           v[0] = half_of(r[0], e) | (half_of(r[1], e) << 16);
           v[1] = half_of(r[2], e) | (half_of(r[3], e) << 16);
-          *reinterpret_cast<u32x2*>(s + row * BKT + (((kg >> 1) ^ swz(row)) << 3) + 4 * (kg & 1)) = v;
+          *reinterpret_cast<u32x2*>(s + lds_off[e]) = v;
         }
       }
     }
   }
 };
 
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
 template <int BM, int BN, bool AK, bool BKC, int EPI>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_mfma(Params p) {
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * BKT];
+  constexpr int TILE_BYTES = (BM + BN) * BKT * 2;
+  __shared__ __attribute__((aligned(16))) char smem[2 * TILE_BYTES];
 
   int tm, tn;
   tile_coords(p, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  const uint16_t* __restrict__ Ap = static_cast<const uint16_t*>(p.A);
-  const uint16_t* __restrict__ Bp = static_cast<const uint16_t*>(p.B);
 
-  // Lane (l) of the 32x32 MFMA result holds column l%32 and rows
-  // 8*(r/4) + 4*(l/32) + r%4 for its 16 values r.
-  const int lrow = m0 + wm * WTM + (lane >> 5) * 4;
-  const int lcol = n0 + wn * WTN + (lane & 31);
-  const bool full = (m0 + BM <= p.M) && (n0 + BN <= p.N);
+  // The MFMA takes the B fragment as its row operand and the A fragment as its
+  // column operand, so lane l ends up with output row m = .. + l % 32 and the
+  // four consecutive columns n = .. + 8 g + 4 (l / 32) + {0..3} in registers
+  // 4g..4g+3 of each 32x32 block: vector stores in the epilogue.
+  const int em = m0 + wm * WTM + (lane & 31);
+  const int en = n0 + wn * WTN + 4 * (lane >> 5);
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -267,26 +293,52 @@ gemm_bf16_mfma(Params p) {
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  __amdgpu_buffer_rsrc_t crsrc = make_rsrc(p.C, (uint32_t)(((int64_t)(p.M - 1) * p.ldc + p.N) *
+                                                           (EPI == EPI_ACC ? 4 : 2)));
   if constexpr (EPI == EPI_ACC) {
     if (p.beta) {
-      const float* Cp = static_cast<const float*>(p.C);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = lrow + i * 32 + (r >> 2) * 8 + (r & 3);
-          const float* row = Cp + (int64_t)m * p.ldc + lcol;
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            if (full || (m < p.M && lcol + j * 32 < p.N)) acc[i][j][r] = row[j * 32];
-        }
+          for (int g = 0; g < 4; ++g) {
+            const int m = em + i * 32, n = en + j * 32 + 8 * g;
+            const uint32_t off = (m < p.M && n < p.N) ? (uint32_t)(((int64_t)m * p.ldc + n) * 4) : kOOB;
+            const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(crsrc, (int)off, 0, 0));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[i][j][4 * g + t] = v[t];
+          }
     }
   }
 
-  TileLoader<BM, AK> la(Ap, p.lda, m0, p.M, tid);
-  TileLoader<BN, BKC> lb(Bp, p.ldb, n0, p.N, tid);
+  TileLoader<BM, AK> la(static_cast<const uint16_t*>(p.A), p.lda, m0, p.M, p.K, tid);
+  TileLoader<BN, BKC> lb(static_cast<const uint16_t*>(p.B), p.ldb, n0, p.N, p.K, tid);
   const int nk = (p.K + BKT - 1) / BKT;
   const bool k_ragged = (p.K % BKT) != 0;
+
+  // Fragment read offsets: row = base + i*32 + lane%32, chunk = 2 kk + lane/32;
+  // its swizzled chunk is P ^ 2 (kk ^ 2 (i % 2)) with P fixed per lane.
+  uint32_t ra[4], rb[4];
+  {
+    const int P = (lane >> 5) ^ (lane & 7) ^ ((lane >> 3) & 3);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ra[q] = (wm * WTM + (lane & 31)) * 128 + ((P ^ (2 * q)) << 4);
+      rb[q] = BM * 128 + (wn * WTN + (lane & 31)) * 128 + ((P ^ (2 * q)) << 4);
+    }
+  }
+  bf16x8 af[2][TM], bfr[2][TN];
+  auto read_frags = [&](const char* buf, int kk, int fb) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      af[fb][i] = *reinterpret_cast<const bf16x8*>(buf + ra[kk ^ (2 * (i & 1))] + i * 32 * 128);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bfr[fb][j] = *reinterpret_cast<const bf16x8*>(buf + rb[kk ^ (2 * (j & 1))] + j * 32 * 128);
+  };
+
   if (nk > 0) {  // K == 0: empty sum, the epilogue sees the initial accumulators
     if (nk == 1 && k_ragged) {
       la.template load<true>(0, p.K);
@@ -295,15 +347,20 @@ gemm_bf16_mfma(Params p) {
       la.template load<false>(0, p.K);
       lb.template load<false>(0, p.K);
     }
-    la.store(smem, tid);
-    lb.store(smem + BM * BKT, tid);
+    la.store(smem);
+    lb.store(smem + BM * 128);
     __syncthreads();
+    read_frags(smem, 0, 0);
   }
 
+  // Fragments are double-buffered across the four 16-deep k steps of a tile:
+  // LDS reads for step kk+1 are issued ahead of the MFMAs of step kk, and the
+  // next tile (already in registers) goes to the other LDS buffer mid-tile.
   for (int kt = 0; kt < nk; ++kt) {
-    uint16_t* cur = smem + (kt & 1) * (BM + BN) * BKT;
-    uint16_t* nxt = smem + ((kt + 1) & 1) * (BM + BN) * BKT;
-    if (kt + 1 < nk) {
+    const char* cur = smem + (kt & 1) * TILE_BYTES;
+    char* nxt = smem + ((kt + 1) & 1) * TILE_BYTES;
+    const bool has_next = kt + 1 < nk;
+    if (has_next) {
       if (kt + 2 == nk && k_ragged) {
         la.template load<true>((kt + 1) * BKT, p.K);
         lb.template load<true>((kt + 1) * BKT, p.K);
@@ -312,46 +369,79 @@ gemm_bf16_mfma(Params p) {
         lb.template load<false>((kt + 1) * BKT, p.K);
       }
     }
-    const uint16_t* sa = cur;
-    const uint16_t* sb = cur + BM * BKT;
 #pragma unroll
     for (int kk = 0; kk < BKT / 16; ++kk) {
-      const int chunk = kk * 2 + (lane >> 5);
-      bf16x8 af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * WTM + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const bf16x8*>(sa + row * BKT + ((chunk ^ swz(row)) << 3));
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int row = wn * WTN + j * 32 + (lane & 31);
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + row * BKT + ((chunk ^ swz(row)) << 3));
-      }
+      const int fb = kk & 1;
+      if (kk + 1 < BKT / 16) read_frags(cur, kk + 1, fb ^ 1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-      la.store(nxt, tid);
-      lb.store(nxt + BM * BKT, tid);
-    }
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = lrow + i * 32 + (r >> 2) * 8 + (r & 3);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = lcol + j * 32;
-        if (full || (m < p.M && n < p.N)) epi_store<uint16_t, EPI>(p, m, n, acc[i][j][r]);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fb][j], af[fb][i], acc[i][j], 0, 0, 0);
+      if (kk == BKT / 16 - 2 && has_next) {
+        la.store(nxt);
+        lb.store(nxt + BM * 128);
       }
     }
+    __syncthreads();
+    if (has_next) read_frags(nxt, 0, 0);
+  }
+
+  // Epilogue: lane (i, j, g) owns C[em + 32 i][en + 32 j + 8 g + 0..3].
+  if constexpr (EPI == EPI_ACC) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int m = em + i * 32, n = en + j * 32 + 8 * g;
+          const uint32_t off = (m < p.M && n < p.N) ? (uint32_t)(((int64_t)m * p.ldc + n) * 4) : kOOB;
+          f32x4 v;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * g + t];
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), crsrc, (int)off, 0, 0);
+        }
+  } else {
+    __amdgpu_buffer_rsrc_t rrsrc = make_rsrc(EPI == EPI_RESID || EPI == EPI_DGELU ? p.R : p.C,
+                                             (uint32_t)(((int64_t)(p.M - 1) * p.ldr + p.N) * 2));
+    __amdgpu_buffer_rsrc_t zrsrc = make_rsrc(EPI == EPI_GELU ? p.Z : p.C,
+                                             (uint32_t)(((int64_t)(p.M - 1) * p.ldz + p.N) * 2));
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int m = em + i * 32, n = en + j * 32 + 8 * g;
+          const bool ok = m < p.M && n < p.N;
+          float v[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * g + t];
+          if constexpr (EPI == EPI_RESID || EPI == EPI_DGELU) {
+            const uint32_t roff = ok ? (uint32_t)(((int64_t)m * p.ldr + n) * 2) : kOOB;
+            const u32x2 rv = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rrsrc, (int)roff, 0, 0));
+            const float r0 = __uint_as_float(rv[0] << 16), r1 = __uint_as_float(rv[0] & 0xffff0000u);
+            const float r2 = __uint_as_float(rv[1] << 16), r3 = __uint_as_float(rv[1] & 0xffff0000u);
+            if constexpr (EPI == EPI_RESID) {
+              v[0] += r0; v[1] += r1; v[2] += r2; v[3] += r3;
+            } else {
+              v[0] *= gelu_grad_f(r0, p.gelu); v[1] *= gelu_grad_f(r1, p.gelu);
+              v[2] *= gelu_grad_f(r2, p.gelu); v[3] *= gelu_grad_f(r3, p.gelu);
+            }
+          }
+          if constexpr (EPI == EPI_GELU) {
+            const uint32_t zoff = ok ? (uint32_t)(((int64_t)m * p.ldz + n) * 2) : kOOB;
+            const u32x2 zv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            __builtin_amdgcn_raw_buffer_store_b64(zv, zrsrc, (int)zoff, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = gelu_f(v[t], p.gelu);
+          }
+          const uint32_t off = ok ? (uint32_t)(((int64_t)m * p.ldc + n) * 2) : kOOB;
+          const u32x2 cv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          __builtin_amdgcn_raw_buffer_store_b64(cv, crsrc, (int)off, 0, 0);
+        }
+  }
 }
 
 // ------------------------------------------------- fp32 storage (plain FMA tiles)
@@ -509,6 +599,15 @@ zb_status launch_gemm(const GemmDesc& g, hipStream_t s) {
     return set_error(ZB_E_UNSUPPORTED, "gemm: contiguous extents and leading dims must be multiples of 8 "
                                        "(M=%d N=%d K=%d lda=%lld ldb=%lld)", g.M, g.N, g.K,
                      (long long)g.lda, (long long)g.ldb);
+  {
+    // Buffer offsets are 32-bit with out-of-range lanes placed at 2 GiB.
+    const double lim = 2147483648.0 - 256.0;
+    const double ea = 2.0 * ((g.a_kcontig ? (double)(g.M - 1) * g.lda + g.K : (double)(g.K - 1) * g.lda + g.M));
+    const double eb = 2.0 * ((g.b_kcontig ? (double)(g.N - 1) * g.ldb + g.K : (double)(g.K - 1) * g.ldb + g.N));
+    const double ec = (g.epi == EPI_ACC ? 4.0 : 2.0) * ((double)(g.M - 1) * g.ldc + g.N);
+    if (ea >= lim || eb >= lim || ec >= lim)
+      return set_error(ZB_E_UNSUPPORTED, "gemm: an operand spans 2 GiB or more");
+  }
   const bool w_layout = !g.a_kcontig && !g.b_kcontig;
   const int t = pick_tile(g.M, g.N, w_layout ? 1 : 0);
   char name[48];
