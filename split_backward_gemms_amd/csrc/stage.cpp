@@ -189,7 +189,7 @@ struct zb_stage {
   hipStream_t stream = nullptr;
   std::vector<LayerOff> off;
   size_t fw_bytes = 0, fb_bytes = 0, bw_bytes = 0, scratch_bytes = 0;
-  size_t scratch_do = 0, scratch_flag = 0;
+  size_t scratch_do = 0, scratch_flag = 0, scratch_dsum = 0;
   // plan
   bool planned = false;
   int plan_fw = 0, plan_fb = 0, plan_bw = 0;
@@ -250,6 +250,8 @@ void compute_layout(zb_stage* S) {
   S->scratch_flag = sc; sc += kAlign;
   S->scratch_do = sc;
   if (S->d.kind == ZB_KIND_FULL) sc += align_up(T * h * es);
+  S->scratch_dsum = sc;
+  if (S->d.kind == ZB_KIND_FULL) sc += align_up(a * T * 4);
   S->scratch_bytes = sc;
   S->fw.bytes = fw;
   S->fb.bytes = fb;
@@ -380,8 +382,18 @@ zb_status run_forward(zb_stage* S, int mb, void* y) {
         ZB_TRY(gemm_f(S, fwb + o.a, f, lin_index(S, l, LIN_DOWN), out, h, EPI_STORE));
         break;
       }
-      default:
-        return set_error(ZB_E_UNSUPPORTED, "FULL layers need the attention kernels");
+      default: {  // FULL
+        char* qkv = fbb + o.qkv_fb;
+        ZB_TRY(gemm_f(S, X, h, lin_index(S, l, LIN_QKV), qkv, 3 * h, EPI_STORE));
+        AttnArgs at;
+        at.qkv = qkv; at.o = fwb + o.o; at.lse2 = reinterpret_cast<float*>(fbb + o.lse);
+        at.heads = S->d.n_heads; at.seq = S->d.seq; at.nseq = S->d.micro_batch;
+        ZB_TRY(launch_attention_fwd(at, S->stream));
+        ZB_TRY(gemm_f(S, fwb + o.o, h, lin_index(S, l, LIN_PROJ), fwb + o.xup, h, EPI_RESID, X, h));
+        ZB_TRY(gemm_f(S, fwb + o.xup, h, lin_index(S, l, LIN_UP), fwb + o.a, f, EPI_GELU, nullptr, 0, fbb + o.z, f));
+        ZB_TRY(gemm_f(S, fwb + o.a, f, lin_index(S, l, LIN_DOWN), out, h, EPI_RESID, fwb + o.xup, h));
+        break;
+      }
     }
   }
   return ZB_OK;
@@ -422,8 +434,25 @@ zb_status run_backward(zb_stage* S, int mb, void* dx, bool unsplit, int beta) {
         if (unsplit) ZB_TRY(gemm_w(S, fwb + o.x, h, bwb + o.dqkv, 3 * h, qkv, beta));
         break;
       }
-      default:
-        return set_error(ZB_E_UNSUPPORTED, "FULL layers need the attention kernels");
+      default: {  // FULL
+        const int qkv = lin_index(S, l, LIN_QKV), proj = lin_index(S, l, LIN_PROJ);
+        const int up = lin_index(S, l, LIN_UP), down = lin_index(S, l, LIN_DOWN);
+        char* dO = S->scratch + S->scratch_do;
+        ZB_TRY(gemm_b(S, dY, h, down, bwb + o.dz, f, EPI_DGELU, fbb + o.z, f));
+        if (unsplit) ZB_TRY(gemm_w(S, fwb + o.a, f, dY, h, down, beta));
+        ZB_TRY(gemm_b(S, bwb + o.dz, f, up, bwb + o.dp, h, EPI_RESID, dY, h));
+        if (unsplit) ZB_TRY(gemm_w(S, fwb + o.xup, h, bwb + o.dz, f, up, beta));
+        ZB_TRY(gemm_b(S, bwb + o.dp, h, proj, dO, h, EPI_STORE));
+        if (unsplit) ZB_TRY(gemm_w(S, fwb + o.o, h, bwb + o.dp, h, proj, beta));
+        AttnArgs at;
+        at.qkv = fbb + o.qkv_fb; at.o = fwb + o.o; at.lse2 = reinterpret_cast<float*>(fbb + o.lse);
+        at.dout = dO; at.dsum = reinterpret_cast<float*>(S->scratch + S->scratch_dsum); at.dqkv = bwb + o.dqkv;
+        at.heads = S->d.n_heads; at.seq = S->d.seq; at.nseq = S->d.micro_batch;
+        ZB_TRY(launch_attention_bwd(at, S->stream));
+        ZB_TRY(gemm_b(S, bwb + o.dqkv, 3 * h, qkv, out, h, EPI_RESID, bwb + o.dp, h));
+        if (unsplit) ZB_TRY(gemm_w(S, fwb + o.x, h, bwb + o.dqkv, 3 * h, qkv, beta));
+        break;
+      }
     }
   }
   return ZB_OK;
@@ -447,8 +476,12 @@ zb_status run_weight(zb_stage* S, int mb, int beta) {
         ZB_TRY(gemm_w(S, fwb + o.xup, h, bwb + o.dz, f, lin_index(S, l, LIN_UP), beta));
         ZB_TRY(gemm_w(S, fwb + o.a, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
         break;
-      default:
-        return set_error(ZB_E_UNSUPPORTED, "FULL layers need the attention kernels");
+      default:  // FULL
+        ZB_TRY(gemm_w(S, fwb + o.x, h, bwb + o.dqkv, 3 * h, lin_index(S, l, LIN_QKV), beta));
+        ZB_TRY(gemm_w(S, fwb + o.o, h, bwb + o.dp, h, lin_index(S, l, LIN_PROJ), beta));
+        ZB_TRY(gemm_w(S, fwb + o.xup, h, bwb + o.dz, f, lin_index(S, l, LIN_UP), beta));
+        ZB_TRY(gemm_w(S, fwb + o.a, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
+        break;
     }
   }
   return ZB_OK;
@@ -571,7 +604,6 @@ extern "C" zb_status zb_stage_create(const zb_stage_desc* d, int stage_index, co
     if (d->n_heads < 1 || d->hidden % d->n_heads || d->hidden / d->n_heads != 128)
       return set_error(ZB_E_UNSUPPORTED, "FULL needs hidden / n_heads == 128");
     if (d->dtype != ZB_DTYPE_BF16) return set_error(ZB_E_UNSUPPORTED, "FULL is bf16 only");
-    return set_error(ZB_E_UNSUPPORTED, "FULL layers need the attention kernels");
   }
   zb_stage* S = new zb_stage();
   S->d = *d;

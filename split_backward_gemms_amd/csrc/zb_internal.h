@@ -70,6 +70,19 @@ struct GemmDesc {
 
 zb_status launch_gemm(const GemmDesc& g, hipStream_t s);
 
+// Causal attention of one FULL layer (head dim 128).  lse2/dsum: fp32 [heads, T].
+struct AttnArgs {
+  const void* qkv = nullptr;  // [T, 3h] bf16
+  void* o = nullptr;          // [T, h] bf16
+  float* lse2 = nullptr;
+  const void* dout = nullptr; // [T, h] bf16 (backward)
+  float* dsum = nullptr;      // scratch (backward)
+  void* dqkv = nullptr;       // [T, 3h] bf16 (backward output)
+  int heads = 0, seq = 0, nseq = 0;
+};
+zb_status launch_attention_fwd(const AttnArgs& a, hipStream_t s);
+zb_status launch_attention_bwd(const AttnArgs& a, hipStream_t s);
+
 // Fill rows x cols elements (row stride ld, 2 or 4 bytes each) with zero.
 zb_status launch_zero2d(void* p, int64_t rows, int64_t cols, int64_t ld, int elem_bytes, hipStream_t s);
 // Sets *flag (device int) to 1 if any of n fp32 values is NaN/Inf (flag must be pre-zeroed).
