@@ -38,6 +38,22 @@ def gpu_step_flops(w) -> float:
     return float(per_mb_stage) * w.n_micro * w.n_stages
 
 
+def pmc_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE / WRITE_SIZE, calibrated against a plain copy), or None
+    when there is none or the GEMM source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"pmc_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    src = open(os.path.join(ROOT, d["source"]), "rb").read()
+    if hashlib.sha256(src).hexdigest()[:16] != d["source_sha256_16"]:
+        return None
+    k = d["kernels"].get(kernel)
+    return None if k is None else k["hbm_bytes_per_launch"]
+
+
 def cpu_baseline(w, budget_s: float = 12.0) -> dict:
     """The fp64 oracle (as it stands) on a bounded sample: whole F+B+W units of
     one stage and one microbatch at full size, repeated until budget_s elapses."""
@@ -77,7 +93,21 @@ def main() -> int:
     ap.add_argument("--order", default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--mode", choices=["full", "kernels"], default="full",
+                    help="kernels: only the one-stream kernel-timing phase (the phase a kernel profile covers)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run one plain device-to-device copy kernel of BYTES bytes (counter calibration)")
     a = ap.parse_args()
+    if a.calibrate_copy:
+        import torch
+        n = a.calibrate_copy // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 4 * n}))
+        return 0
     if a.gpus != 1:
         print(f"bench.py: this build measures one GPU's share of the pipeline only; --gpus {a.gpus} is not "
               f"supported (stages are emulated on one device).", file=sys.stderr)
@@ -103,67 +133,80 @@ def main() -> int:
 
     ops, sim = zb.zb_schedule_build(order, w.n_stages, w.n_micro)
     ops_fused, sim_fused = zb.zb_schedule_build("1f1b", w.n_stages, w.n_micro)
-    pipe = EmulatedPipeline(w, ws, ops=None, device=dev)
-    del ws
-    X = [upload(x, w.dtype, dev) for x in xs]
-    DY = [upload(d, w.dtype, dev) for d in dys]
-    y, dx = pipe.io_buffers()
-    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
-    log(f"device ready: workspace {pipe.workspace_bytes() / 2**30:.2f} GiB")
 
-    def step(o):
-        pipe.run(o, X, DY, y, dx)
-
-    for _ in range(a.warmup):
-        step(ops)
-    torch.cuda.synchronize()
-    log("warmup done")
-
-    t0 = time.perf_counter()
-    for _ in range(a.steps):
-        step(ops)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = 1000.0 * wall / a.steps
-    flops = gpu_step_flops(w)
-    tflops = flops / (ms_per_step / 1000.0) / 1e12
-    log(f"{order}: {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s")
-
-    # per-pass device times (hipEvent pair per pass) of one more step in each order
-    tr, _ = pipe.run(ops, X, DY, y, dx, trace=True)
-    t_split = {k: sum(ms for (op, ms, _) in tr if op[1] == k) for k in "FBW"}
-    fused = {}
-    if not a.no_fused:
-        for _ in range(a.warmup):
-            step(ops_fused)
+    def timed(pipe, o, X, DY, y, dx, steps, warmup):
+        for _ in range(warmup):
+            pipe.run(o, X, DY, y, dx)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(a.steps):
-            step(ops_fused)
+        for _ in range(steps):
+            pipe.run(o, X, DY, y, dx)
         torch.cuda.synchronize()
-        fused_ms = 1000.0 * (time.perf_counter() - t0) / a.steps
+        return 1000.0 * (time.perf_counter() - t0) / steps
+
+    X = [upload(x, w.dtype, dev) for x in xs]
+    DY = [upload(d, w.dtype, dev) for d in dys]
+    flops = gpu_step_flops(w)
+    fused = {}
+    ms_per_step = tflops = float("nan")
+    if a.mode == "full":
+        # Headline: one HIP stream per emulated stage, so independent stages overlap
+        # the way pipeline stages on separate devices would.
+        pipe = EmulatedPipeline(w, ws, ops=None, device=dev, stage_streams=True)
+        y, dx = pipe.io_buffers()
+        torch.cuda.synchronize()
+        log(f"device ready: workspace {pipe.workspace_bytes() / 2**30:.2f} GiB")
+        ms_per_step = timed(pipe, ops, X, DY, y, dx, a.steps, a.warmup)
+        tflops = flops / (ms_per_step / 1000.0) / 1e12
+        log(f"{order}, stage streams: {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s")
+    if a.mode == "full" and not a.no_fused:
+        fms = timed(pipe, ops_fused, X, DY, y, dx, a.steps, a.warmup)
+        fused["ms_per_step_1f1b_unsplit_stage_streams"] = fms
+        fused["zb_vs_1f1b_speedup_stage_streams"] = fms / ms_per_step - 1.0
+        log(f"1f1b unsplit, stage streams: {fms:.3f} ms/step")
+    if a.mode == "full":
+        pipe.close()
+        del pipe
+        torch.cuda.synchronize()
+
+    # One shared stream: passes and kernels run in isolation, for the per-pass
+    # split overhead and the kernel roofline.
+    pipe = EmulatedPipeline(w, ws, ops=None, device=dev)
+    del ws
+    y, dx = pipe.io_buffers()
+    t_split = {}
+    if a.mode == "full":
+        single_ms = timed(pipe, ops, X, DY, y, dx, max(2, a.steps // 2), 1)
+        tr, _ = pipe.run(ops, X, DY, y, dx, trace=True)
+        t_split = {k: sum(ms for (op, ms, _) in tr if op[1] == k) for k in "FBW"}
+        log(f"{order}, one stream: {single_ms:.3f} ms/step; passes {t_split}")
+    else:
+        pipe.run(ops, X, DY, y, dx)  # one untimed step before the kernel-timing phase
+    if a.mode == "full" and not a.no_fused:
+        fused_ms = timed(pipe, ops_fused, X, DY, y, dx, max(2, a.steps // 2), 1)
         trf, _ = pipe.run(ops_fused, X, DY, y, dx, trace=True)
         t_f = {k: sum(ms for (op, ms, _) in trf if op[1] == k) for k in "FU"}
-        fused = {"ms_per_step_1f1b_unsplit": fused_ms,
-                 "split_overhead_pass": (t_split["B"] + t_split["W"]) / t_f["U"] - 1.0,
-                 "split_overhead_wall": ms_per_step / fused_ms - 1.0,
-                 "pass_ms_1f1b": {"F": t_f["F"], "U": t_f["U"]}}
-        log(f"1f1b unsplit: {fused_ms:.3f} ms/step; split overhead (B+W vs U) "
+        fused.update({"ms_per_step_one_stream": single_ms,
+                      "ms_per_step_1f1b_unsplit_one_stream": fused_ms,
+                      "split_overhead_pass": (t_split["B"] + t_split["W"]) / t_f["U"] - 1.0,
+                      "split_overhead_wall_one_stream": single_ms / fused_ms - 1.0,
+                      "pass_ms_1f1b": {"F": t_f["F"], "U": t_f["U"]}})
+        log(f"1f1b unsplit, one stream: {fused_ms:.3f} ms/step; split overhead (B+W vs U) "
             f"{100 * fused['split_overhead_pass']:.2f}%")
 
-    # kernel-level timing over one more profiled step of the measured order
+    # kernel-level timing over profiled steps of the measured order (one stream)
     zb.zb_prof_reset()
     zb.zb_prof_enable(True)
-    prof_steps = max(1, min(a.steps, 3))
+    prof_steps = 2
     for _ in range(prof_steps):
-        step(ops)
+        pipe.run(ops, X, DY, y, dx)
     torch.cuda.synchronize()
     zb.zb_prof_enable(False)
     kern = zb.zb_prof_read()
     zb.zb_prof_reset()
     kern.sort(key=lambda r: -r["total_ms"])
-    for r in kern[:8]:
+    for r in kern[:10]:
         log(f"  {r['name']:<28} {r['launches']:6d} launches {r['total_ms'] / prof_steps:8.3f} ms/step "
             f"{r['flops'] / r['total_ms'] / 1e9:8.1f} TFLOP/s")
     gemm_ms = sum(r["total_ms"] for r in kern if r["name"].startswith("gemm")) / prof_steps
@@ -173,18 +216,23 @@ def main() -> int:
     per_launch_flops = top["flops"] / top["launches"]
     achieved = per_launch_flops / (avg_ms / 1e3) / 1e12
     roofline = {"bound": "mfma", "kernel": top["name"], "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                "avg_launch_us": avg_ms * 1e3, "flops_per_launch": per_launch_flops}
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": pmc_traffic(w.name, top["name"]),
+                "avg_launch_us": avg_ms * 1e3, "flops_per_launch": per_launch_flops,
+                "measured_on": "one stream, hipEvent pair per launch"}
+    kernels = [{"name": r["name"], "launches_per_step": r["launches"] / prof_steps,
+                "ms_per_step": r["total_ms"] / prof_steps,
+                "tflops": r["flops"] / r["total_ms"] / 1e9} for r in kern]
 
     pipe.close()
     out = {
         "metric": "stage F+B+W TFLOP/s",
-        "value": tflops,
+        "value": tflops if a.mode == "full" else None,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": ms_per_step if a.mode == "full" else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -192,15 +240,17 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "stages_emulated": w.n_stages, "n_micro": w.n_micro,
                    "layers_per_stage": w.n_layers, "hidden": w.hidden, "ffn": w.ffn, "seq": w.seq,
-                   "micro_batch": w.micro_batch, "order": order, "flops_per_step": flops},
-        "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+                   "micro_batch": w.micro_batch, "order": order, "executor": "one HIP stream per stage",
+                   "flops_per_step": flops},
+        "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS if a.mode == "full" else None,
         "gemm_only_tflops": gemm_flops / (gemm_ms / 1e3) / 1e12 if gemm_ms > 0 else None,
         "pass_ms": t_split,
         "sim_bubble_unit_times": {order: sim["bubble"], "1f1b": sim_fused["bubble"]},
         "roofline": roofline,
+        "kernels": kernels,
     }
     out.update(fused)
-    if not a.no_cpu:
+    if not a.no_cpu and a.mode == "full":
         log("timing the CPU oracle sample ...")
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -272,8 +272,14 @@ typedef struct {
   float t0_ms;   /* start, relative to the first pass's start event  */
 } zb_trace_rec;
 
-/* Run a one-device order over P stages (host array stages[P], all on one
- * stream, stage_index p at stages[p]).  The whole list is validated
+/* Run a one-device order over P stages (host array stages[P], stage_index p at
+ * stages[p]).  If all stages share one stream the passes run in list order on
+ * it.  If they have different streams, each pass goes to its stage's stream and
+ * the cross-stage dependencies become event waits (F(s,j) after F(s-1,j),
+ * B|U(s,j) after B|U(s+1,j)), so independent stages run concurrently like
+ * pipeline stages on separate devices; the caller must make x0 and dy_last
+ * visible to every stage stream beforehand and synchronise every stage stream
+ * afterwards.  The whole list is validated
  * (zb_schedule_validate rules) and every stage's workspace plan checked before
  * anything is launched.  x0[mb], dy_last[mb], y_last[mb], dx0[mb] (host arrays
  * of m device pointers, [T, h] each) are the first stage's inputs, the last

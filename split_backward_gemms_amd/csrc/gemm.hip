@@ -27,6 +27,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <type_traits>
 
 #include "zb_internal.h"
 
@@ -58,6 +59,7 @@ struct Params {
   int beta;
   int gelu;
   int nbm, nbn;
+  int xcd_remap;
 };
 
 // ------------------------------------------------------------- elementwise math
@@ -131,10 +133,9 @@ __device__ __forceinline__ void epi_store(const Params& p, int m, int n, float v
 // Workgroup -> output tile.  Consecutive logical tiles share an XCD (its own
 // L2); within the logical order, tiles go in groups of 8 tile-rows so that
 // neighbours reuse A rows and B columns.
-__device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
+__device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn, int b) {
   const int nblk = p.nbm * p.nbn;
-  int b = blockIdx.x;
-  if (nblk % XCDS == 0) b = (b % XCDS) * (nblk / XCDS) + b / XCDS;
+  if (p.xcd_remap && nblk % XCDS == 0) b = (b % XCDS) * (nblk / XCDS) + b / XCDS;
   const int G = 8;
   const int per_group = G * p.nbn;
   const int group = b / per_group;
@@ -175,7 +176,7 @@ struct TileLoader {
   static constexpr int NREG = ROWS / 32;  // 16-byte registers per thread
   static constexpr int KR = NREG;         // m/n-contiguous: k rows per thread (8 or 4)
   static constexpr int MCH = ROWS / 64;   // m/n-contiguous: 64-wide column groups
-  u32x4 r[NREG];
+  using Regs = u32x4[NREG];
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t voff[NREG];   // byte offset of register i's 16 bytes at k0 = 0 (kOOB if outside)
   uint32_t kstep;        // bytes per unit of k
@@ -222,7 +223,7 @@ struct TileLoader {
   }
 
   template <bool CHECK_K>
-  __device__ __forceinline__ void load(int k0, int K) {
+  __device__ __forceinline__ void load(Regs& r, int k0, int K) const {
     const uint32_t step = (uint32_t)k0 * kstep;
 #pragma unroll
     for (int i = 0; i < NREG; ++i) {
@@ -235,7 +236,7 @@ struct TileLoader {
     }
   }
 
-  __device__ __forceinline__ void store(char* s) const {
+  __device__ __forceinline__ void store(const Regs& r, char* s) const {
     if constexpr (KCONTIG) {
 #pragma unroll
       for (int i = 0; i < NREG; ++i)
@@ -265,16 +266,45 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
 
+// Up to kMaxGroup independent GEMMs of one layout and epilogue in one launch;
+// workgroup b works on GEMM g with tile_start[g] <= b < tile_start[g+1].
+constexpr int kMaxGroup = 16;
+struct GroupParams {
+  Params p[kMaxGroup];
+  int tile_start[kMaxGroup + 1];
+  int n;
+};
+
+template <int BM, int BN, bool AK, bool BKC, int EPI>
+__device__ __forceinline__ void gemm_tile(const Params& p, int block, char* smem);
+
 template <int BM, int BN, bool AK, bool BKC, int EPI>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_mfma(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * BKT * 2];
+  gemm_tile<BM, BN, AK, BKC, EPI>(p, blockIdx.x, smem);
+}
+
+template <int BM, int BN, bool AK, bool BKC, int EPI>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
+gemm_bf16_mfma_group(GroupParams gp) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * BKT * 2];
+  int b = blockIdx.x;
+  const int total = gp.tile_start[gp.n];
+  if (total % XCDS == 0) b = (b % XCDS) * (total / XCDS) + b / XCDS;  // one XCD works a GEMM's neighbours
+  int g = 0;
+  while (g + 1 < gp.n && b >= gp.tile_start[g + 1]) ++g;
+  gemm_tile<BM, BN, AK, BKC, EPI>(gp.p[g], b - gp.tile_start[g], smem);
+}
+
+template <int BM, int BN, bool AK, bool BKC, int EPI>
+__device__ __forceinline__ void gemm_tile(const Params& p, int block, char* smem) {
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int TILE_BYTES = (BM + BN) * BKT * 2;
-  __shared__ __attribute__((aligned(16))) char smem[2 * TILE_BYTES];
 
   int tm, tn;
-  tile_coords(p, tm, tn);
+  tile_coords(p, tm, tn, block);
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
@@ -339,35 +369,69 @@ gemm_bf16_mfma(Params p) {
       bfr[fb][j] = *reinterpret_cast<const bf16x8*>(buf + rb[kk ^ (2 * (j & 1))] + j * 32 * 128);
   };
 
-  if (nk > 0) {  // K == 0: empty sum, the epilogue sees the initial accumulators
-    if (nk == 1 && k_ragged) {
-      la.template load<true>(0, p.K);
-      lb.template load<true>(0, p.K);
+  // Two sets of staging registers: tile t travels global -> set t%2 -> LDS
+  // buffer t%2.  Loads run two tiles ahead of the MFMAs.
+  typename TileLoader<BM, AK>::Regs ra_stage[2];
+  typename TileLoader<BN, BKC>::Regs rb_stage[2];
+  auto issue = [&](auto set, int t) {
+    if (t == nk - 1 && k_ragged) {
+      la.template load<true>(ra_stage[decltype(set)::value], t * BKT, p.K);
+      lb.template load<true>(rb_stage[decltype(set)::value], t * BKT, p.K);
     } else {
-      la.template load<false>(0, p.K);
-      lb.template load<false>(0, p.K);
+      la.template load<false>(ra_stage[decltype(set)::value], t * BKT, p.K);
+      lb.template load<false>(rb_stage[decltype(set)::value], t * BKT, p.K);
     }
-    la.store(smem);
-    lb.store(smem + BM * 128);
+  };
+  auto stage_to_lds = [&](auto set, char* buf) {
+    la.store(ra_stage[decltype(set)::value], buf);
+    lb.store(rb_stage[decltype(set)::value], buf + BM * 128);
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+
+  if (nk > 0) {  // K == 0: empty sum, the epilogue sees the initial accumulators
+    issue(S0{}, 0);
+    if (nk > 1) issue(S1{}, 1);
+    stage_to_lds(S0{}, smem);
     __syncthreads();
     read_frags(smem, 0, 0);
   }
 
-  // Fragments are double-buffered across the four 16-deep k steps of a tile:
-  // LDS reads for step kk+1 are issued ahead of the MFMAs of step kk, and the
-  // next tile (already in registers) goes to the other LDS buffer mid-tile.
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* cur = smem + (kt & 1) * TILE_BYTES;
-    char* nxt = smem + ((kt + 1) & 1) * TILE_BYTES;
-    const bool has_next = kt + 1 < nk;
-    if (has_next) {
-      if (kt + 2 == nk && k_ragged) {
-        la.template load<true>((kt + 1) * BKT, p.K);
-        lb.template load<true>((kt + 1) * BKT, p.K);
-      } else {
-        la.template load<false>((kt + 1) * BKT, p.K);
-        lb.template load<false>((kt + 1) * BKT, p.K);
-      }
+  // One tile: fragments are double-buffered across its four 16-deep k steps
+  // (LDS reads for step kk+1 go out before the MFMAs of step kk); the next
+  // tile moves from its staging registers into the other LDS buffer mid-tile.
+  auto tile = [&](auto par, int kt) {
+    constexpr int PAR = decltype(par)::value;
+    const char* cur = smem + PAR * TILE_BYTES;
+    char* nxt = smem + (PAR ^ 1) * TILE_BYTES;
+    if (kt + 2 < nk) issue(par, kt + 2);
+#pragma unroll
+    for (int kk = 0; kk < BKT / 16; ++kk) {
+      const int fb = kk & 1;
+      if (kk + 1 < BKT / 16) read_frags(cur, kk + 1, fb ^ 1);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fb][j], af[fb][i], acc[i][j], 0, 0, 0);
+      if (kk == BKT / 16 - 2 && kt + 1 < nk) stage_to_lds(std::integral_constant<int, PAR ^ 1>{}, nxt);
+    }
+    __syncthreads();
+    if (kt + 1 < nk) read_frags(nxt, 0, 0);
+  };
+
+  // Steady state (tile kt+2 exists): one branch-free block per tile, so the
+  // compiler can schedule loads, LDS traffic and MFMAs of a tile together.
+  auto tile_steady = [&](auto par, int kt) {
+    constexpr int PAR = decltype(par)::value;
+    const char* cur = smem + PAR * TILE_BYTES;
+    char* nxt = smem + (PAR ^ 1) * TILE_BYTES;
+    if (k_ragged) {
+      la.template load<true>(ra_stage[PAR], (kt + 2) * BKT, p.K);
+      lb.template load<true>(rb_stage[PAR], (kt + 2) * BKT, p.K);
+    } else {
+      la.template load<false>(ra_stage[PAR], (kt + 2) * BKT, p.K);
+      lb.template load<false>(rb_stage[PAR], (kt + 2) * BKT, p.K);
     }
 #pragma unroll
     for (int kk = 0; kk < BKT / 16; ++kk) {
@@ -378,14 +442,22 @@ gemm_bf16_mfma(Params p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fb][j], af[fb][i], acc[i][j], 0, 0, 0);
-      if (kk == BKT / 16 - 2 && has_next) {
-        la.store(nxt);
-        lb.store(nxt + BM * 128);
-      }
+      if (kk == BKT / 16 - 2) stage_to_lds(std::integral_constant<int, PAR ^ 1>{}, nxt);
+      __builtin_amdgcn_sched_barrier(0);  // keep each k step's reads next to its MFMAs
     }
     __syncthreads();
-    if (has_next) read_frags(nxt, 0, 0);
+    read_frags(nxt, 0, 0);
+  };
+
+  int kt = 0;
+  for (; kt + 3 < nk; kt += 2) {
+    tile_steady(S0{}, kt);
+    tile_steady(S1{}, kt + 1);
   }
+  // The last one to three tiles, with their guards; kt is even here.
+  if (kt < nk) tile(S0{}, kt);
+  if (kt + 1 < nk) tile(S1{}, kt + 1);
+  if (kt + 2 < nk) tile(S0{}, kt + 2);
 
   // Epilogue: lane (i, j, g) owns C[em + 32 i][en + 32 j + 8 g + 0..3].
   if constexpr (EPI == EPI_ACC) {
@@ -451,7 +523,7 @@ __global__ void __launch_bounds__(256) gemm_simt(Params p, int ak, int bk) {
   constexpr int TB = 64, KB = 16;
   __shared__ float sA[KB][TB + 1], sB[KB][TB + 1];
   int tm, tn;
-  tile_coords(p, tm, tn);
+  tile_coords(p, tm, tn, blockIdx.x);
   const int m0 = tm * TB, n0 = tn * TB;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const T* A = static_cast<const T*>(p.A);
@@ -531,7 +603,22 @@ template <int BM, int BN, bool AK, bool BKC, int EPI>
 void launch_mfma(Params p, hipStream_t s) {
   p.nbm = (p.M + BM - 1) / BM;
   p.nbn = (p.N + BN - 1) / BN;
+  p.xcd_remap = 1;
   hipLaunchKernelGGL((gemm_bf16_mfma<BM, BN, AK, BKC, EPI>), dim3(p.nbm * p.nbn), dim3(NT), 0, s, p);
+}
+
+template <int BM, int BN>
+void launch_w_group(GroupParams gp, hipStream_t s) {
+  int total = 0;
+  for (int g = 0; g < gp.n; ++g) {
+    gp.p[g].nbm = (gp.p[g].M + BM - 1) / BM;
+    gp.p[g].nbn = (gp.p[g].N + BN - 1) / BN;
+    gp.p[g].xcd_remap = 0;
+    gp.tile_start[g] = total;
+    total += gp.p[g].nbm * gp.p[g].nbn;
+  }
+  gp.tile_start[gp.n] = total;
+  hipLaunchKernelGGL((gemm_bf16_mfma_group<BM, BN, false, false, EPI_ACC>), dim3(total), dim3(NT), 0, s, gp);
 }
 
 template <bool AK, bool BKC, int EPI>
@@ -566,6 +653,40 @@ void launch_simt_epi(int epi, const Params& p, bool ak, bool bk, hipStream_t s) 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
 }  // namespace
+
+// Several weight-gradient GEMMs (W layout, fp32 accumulate) in one launch.
+zb_status launch_gemm_w_group(const GemmDesc* gs, int n, hipStream_t s) {
+  if (n <= 0) return ZB_OK;
+  for (int i = 0; i < n; i += kMaxGroup) {
+    const int cnt = std::min(kMaxGroup, n - i);
+    GroupParams gp{};
+    gp.n = 0;
+    double flops = 0.0, bytes = 0.0;
+    for (int k = 0; k < cnt; ++k) {
+      const GemmDesc& g = gs[i + k];
+      if (g.a_kcontig || g.b_kcontig || g.epi != EPI_ACC || g.dtype != ZB_DTYPE_BF16)
+        return set_error(ZB_E_ARG, "grouped W launch takes bf16 W-layout GEMMs only");
+      if (g.M == 0 || g.N == 0) continue;
+      if (g.M % 8 || g.N % 8 || g.lda % 8 || g.ldb % 8 || !aligned16(g.A) || !aligned16(g.B))
+        return set_error(ZB_E_UNSUPPORTED, "gemm: contiguous extents and leading dims must be multiples of 8");
+      const double lim = 2147483648.0 - 256.0;
+      if (2.0 * ((double)(g.K - 1) * g.lda + g.M) >= lim || 2.0 * ((double)(g.K - 1) * g.ldb + g.N) >= lim ||
+          4.0 * ((double)(g.M - 1) * g.ldc + g.N) >= lim)
+        return set_error(ZB_E_UNSUPPORTED, "gemm: an operand spans 2 GiB or more");
+      Params& p = gp.p[gp.n++];
+      p.M = g.M; p.N = g.N; p.K = g.K;
+      p.A = g.A; p.lda = g.lda; p.B = g.B; p.ldb = g.ldb; p.C = g.C; p.ldc = g.ldc;
+      p.R = nullptr; p.ldr = 0; p.Z = nullptr; p.ldz = 0; p.beta = g.beta; p.gelu = g.gelu;
+      flops += 2.0 * g.M * g.N * (double)g.K;
+      bytes += 2.0 * ((double)g.M * g.K + (double)g.K * g.N) + (g.beta ? 8.0 : 4.0) * g.M * g.N;
+    }
+    if (gp.n == 0) continue;
+    ProfScope ps("gemm_w_group_256x128", flops, bytes, s);
+    launch_w_group<256, 128>(gp, s);
+    ZB_HIP_CHECK(hipGetLastError());
+  }
+  return ZB_OK;
+}
 
 zb_status launch_gemm(const GemmDesc& g, hipStream_t s) {
   if (g.M < 0 || g.N < 0 || g.K < 0) return set_error(ZB_E_ARG, "gemm: negative size");
@@ -611,7 +732,8 @@ zb_status launch_gemm(const GemmDesc& g, hipStream_t s) {
   const bool w_layout = !g.a_kcontig && !g.b_kcontig;
   const int t = pick_tile(g.M, g.N, w_layout ? 1 : 0);
   char name[48];
-  snprintf(name, sizeof name, "gemm_%s_%dx%d", g.tag, kTiles[t].bm, kTiles[t].bn);
+  static const char* kEpi[] = {"store", "resid", "gelu", "dgelu", "acc"};
+  snprintf(name, sizeof name, "gemm_%s_%dx%d_%s", g.tag, kTiles[t].bm, kTiles[t].bn, kEpi[g.epi]);
   ProfScope ps(name, flops, bytes, s);
   const bool ak = g.a_kcontig, bk = g.b_kcontig;
   if (ak && !bk) {  // F

@@ -139,17 +139,29 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Slots of one tensor class.
+// Slots of one tensor class.  When stages run on different streams, a slot
+// released on one stream and claimed from another is ordered by an event
+// recorded at the release.
 struct Pool {
   size_t bytes = 0;  // per slot
   int n = 0;
   char* base = nullptr;
   std::vector<int> free_list;
+  std::vector<hipEvent_t> ev;          // per slot, created on first cross-stream use
+  std::vector<hipStream_t> ev_stream;  // stream of the last recorded release (null: none)
   void reset(char* b, int count) {
     base = b;
     n = count;
     free_list.clear();
     for (int i = count - 1; i >= 0; --i) free_list.push_back(i);
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
+    ev.assign(count, nullptr);
+    ev_stream.assign(count, nullptr);
+  }
+  ~Pool() {
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
   }
   int acquire() {
     if (free_list.empty()) return -1;
@@ -157,8 +169,23 @@ struct Pool {
     free_list.pop_back();
     return s;
   }
-  void release(int s) {
-    if (s >= 0) free_list.push_back(s);
+  // Orders work on `s` after the slot's last release when that was on another stream.
+  zb_status order_after_release(int slot, hipStream_t s) {
+    if (slot < 0 || !ev_stream[slot] || ev_stream[slot] == s) return ZB_OK;
+    ZB_HIP_CHECK(hipStreamWaitEvent(s, ev[slot], 0));
+    return ZB_OK;
+  }
+  zb_status release(int slot, hipStream_t s, bool multi) {
+    if (slot < 0) return ZB_OK;
+    if (multi) {
+      if (!ev[slot]) ZB_HIP_CHECK(hipEventCreateWithFlags(&ev[slot], hipEventDisableTiming));
+      ZB_HIP_CHECK(hipEventRecord(ev[slot], s));
+      ev_stream[slot] = s;
+    } else {
+      ev_stream[slot] = nullptr;
+    }
+    free_list.push_back(slot);
+    return ZB_OK;
   }
   char* at(int s) const { return base + (size_t)s * bytes; }
 };
@@ -202,6 +229,15 @@ struct zb_stage {
   // per microbatch
   std::vector<int> st, s_fw, s_fb, s_bw;
   int w_count = 0;
+  // multi-stream schedules: stages on different streams
+  bool multi = false;
+  std::vector<hipEvent_t> f_done, b_done;  // per microbatch, created on first use
+  ~zb_stage() {
+    for (hipEvent_t e : f_done)
+      if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : b_done)
+      if (e) (void)hipEventDestroy(e);
+  }
 };
 
 namespace {
@@ -338,14 +374,18 @@ zb_status gemm_b(zb_stage* S, const void* dY, int64_t lddy, int lin, void* dX, i
 }
 
 // dW[K_in, N_out] (+)= X^T . dY
-zb_status gemm_w(zb_stage* S, const void* X, int64_t ldx, const void* dY, int64_t lddy, int lin, int beta) {
+GemmDesc w_desc(const zb_stage* S, const void* X, int64_t ldx, const void* dY, int64_t lddy, int lin, int beta) {
   GemmDesc g;
   g.M = (int)S->wK[lin]; g.N = (int)S->wN[lin]; g.K = S->T;
   g.A = X; g.lda = ldx; g.a_kcontig = false;
   g.B = dY; g.ldb = lddy; g.b_kcontig = false;
   g.C = S->dw[lin]; g.ldc = S->wN[lin];
   g.epi = EPI_ACC; g.beta = beta; g.dtype = S->d.dtype; g.tag = "w";
-  return launch_gemm(g, S->stream);
+  return g;
+}
+
+zb_status gemm_w(zb_stage* S, const void* X, int64_t ldx, const void* dY, int64_t lddy, int lin, int beta) {
+  return launch_gemm(w_desc(S, X, ldx, dY, lddy, lin, beta), S->stream);
 }
 
 #define ZB_TRY(expr)                   \
@@ -458,32 +498,37 @@ zb_status run_backward(zb_stage* S, int mb, void* dx, bool unsplit, int beta) {
   return ZB_OK;
 }
 
+// W pass: every linear's weight gradient.  They are independent of each other,
+// so in bf16 they go out as one grouped launch.
 zb_status run_weight(zb_stage* S, int mb, int beta) {
   char* fwb = S->fw.at(S->s_fw[mb]);
   char* bwb = S->bw.at(S->s_bw[mb]);
   const int64_t h = S->h, f = S->f;
   const size_t es = S->es;
+  std::vector<GemmDesc> gs;
   for (int l = 0; l < S->L; ++l) {
     const LayerOff& o = S->off[l];
     switch (S->d.kind) {
       case ZB_KIND_TINY_MLP:
-        ZB_TRY(gemm_w(S, fwb + o.x, h, bwb + o.dz, f, lin_index(S, l, LIN_UP), beta));
-        ZB_TRY(gemm_w(S, fwb + o.a, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
+        gs.push_back(w_desc(S, fwb + o.x, h, bwb + o.dz, f, lin_index(S, l, LIN_UP), beta));
+        gs.push_back(w_desc(S, fwb + o.a, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
         break;
       case ZB_KIND_MLP_LINEARS:
-        ZB_TRY(gemm_w(S, fwb + o.x, h, bwb + o.dqkv, 3 * h, lin_index(S, l, LIN_QKV), beta));
-        ZB_TRY(gemm_w(S, elem(fwb, o.qkv_fw, 2 * h, es), 3 * h, bwb + o.dp, h, lin_index(S, l, LIN_PROJ), beta));
-        ZB_TRY(gemm_w(S, fwb + o.xup, h, bwb + o.dz, f, lin_index(S, l, LIN_UP), beta));
-        ZB_TRY(gemm_w(S, fwb + o.a, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
+        gs.push_back(w_desc(S, fwb + o.x, h, bwb + o.dqkv, 3 * h, lin_index(S, l, LIN_QKV), beta));
+        gs.push_back(w_desc(S, elem(fwb, o.qkv_fw, 2 * h, es), 3 * h, bwb + o.dp, h, lin_index(S, l, LIN_PROJ), beta));
+        gs.push_back(w_desc(S, fwb + o.xup, h, bwb + o.dz, f, lin_index(S, l, LIN_UP), beta));
+        gs.push_back(w_desc(S, fwb + o.a, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
         break;
       default:  // FULL
-        ZB_TRY(gemm_w(S, fwb + o.x, h, bwb + o.dqkv, 3 * h, lin_index(S, l, LIN_QKV), beta));
-        ZB_TRY(gemm_w(S, fwb + o.o, h, bwb + o.dp, h, lin_index(S, l, LIN_PROJ), beta));
-        ZB_TRY(gemm_w(S, fwb + o.xup, h, bwb + o.dz, f, lin_index(S, l, LIN_UP), beta));
-        ZB_TRY(gemm_w(S, fwb + o.a, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
+        gs.push_back(w_desc(S, fwb + o.x, h, bwb + o.dqkv, 3 * h, lin_index(S, l, LIN_QKV), beta));
+        gs.push_back(w_desc(S, fwb + o.o, h, bwb + o.dp, h, lin_index(S, l, LIN_PROJ), beta));
+        gs.push_back(w_desc(S, fwb + o.xup, h, bwb + o.dz, f, lin_index(S, l, LIN_UP), beta));
+        gs.push_back(w_desc(S, fwb + o.a, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
         break;
     }
   }
+  if (S->d.dtype == ZB_DTYPE_BF16) return launch_gemm_w_group(gs.data(), (int)gs.size(), S->stream);
+  for (const GemmDesc& g : gs) ZB_TRY(launch_gemm(g, S->stream));
   return ZB_OK;
 }
 
@@ -501,30 +546,31 @@ zb_status check_mb(const zb_stage* S, int mb) {
   return ZB_OK;
 }
 
-// Claims (if not yet held) the input slot of mb.
-zb_status claim_fw(zb_stage* S, int mb) {
+// Claims (if not yet held) the input slot of mb for work enqueued on `by`.
+zb_status claim_fw(zb_stage* S, int mb, hipStream_t by) {
   if (S->s_fw[mb] >= 0) return ZB_OK;
   int s = S->fw.acquire();
   if (s < 0) return set_error(ZB_E_BUDGET, "stage %d: no free F->W slot for mb %d (workspace planned for %d)",
                               S->index, mb, S->fw.n);
   S->s_fw[mb] = s;
-  return ZB_OK;
+  return S->fw.order_after_release(s, by);
 }
 
-zb_status claim_bw(zb_stage* S, int mb) {
+zb_status claim_bw(zb_stage* S, int mb, hipStream_t by) {
   if (S->s_bw[mb] >= 0) return ZB_OK;
   int s = S->bw.acquire();
   if (s < 0) return set_error(ZB_E_BUDGET, "stage %d: no free B->W slot for mb %d (workspace planned for %d)",
                               S->index, mb, S->bw.n);
   S->s_bw[mb] = s;
-  return ZB_OK;
+  return S->bw.order_after_release(s, by);
 }
 
-void release_all(zb_stage* S, int mb) {
-  S->fw.release(S->s_fw[mb]);
-  S->fb.release(S->s_fb[mb]);
-  S->bw.release(S->s_bw[mb]);
+zb_status release_all(zb_stage* S, int mb) {
+  ZB_TRY(S->fw.release(S->s_fw[mb], S->stream, S->multi));
+  ZB_TRY(S->fb.release(S->s_fb[mb], S->stream, S->multi));
+  ZB_TRY(S->bw.release(S->s_bw[mb], S->stream, S->multi));
   S->s_fw[mb] = S->s_fb[mb] = S->s_bw[mb] = -1;
+  return ZB_OK;
 }
 
 zb_status do_forward(zb_stage* S, int mb, const void* x, void* y) {
@@ -532,16 +578,13 @@ zb_status do_forward(zb_stage* S, int mb, const void* x, void* y) {
   if (!x || !y) return set_error(ZB_E_ARG, "null x or y");
   if (S->st[mb] != MB_IDLE) return set_error(ZB_E_STATE, "stage %d mb %d already forwarded this step", S->index, mb);
   const bool had_fw = S->s_fw[mb] >= 0;
-  ZB_TRY(claim_fw(S, mb));
-  int sfb = S->fb.acquire();
-  if (sfb < 0) {
-    if (!had_fw) {
-      S->fw.release(S->s_fw[mb]);
-      S->s_fw[mb] = -1;
-    }
+  if (!had_fw && S->fb.free_list.empty())
     return set_error(ZB_E_BUDGET, "stage %d: no free F->B slot for mb %d", S->index, mb);
-  }
+  ZB_TRY(claim_fw(S, mb, S->stream));
+  int sfb = S->fb.acquire();
+  if (sfb < 0) return set_error(ZB_E_BUDGET, "stage %d: no free F->B slot for mb %d", S->index, mb);
   S->s_fb[mb] = sfb;
+  ZB_TRY(S->fb.order_after_release(sfb, S->stream));
   ZB_TRY(copy_in(S, S->fw.at(S->s_fw[mb]) + S->off[0].x, x));
   ZB_TRY(run_forward(S, mb, y));
   S->st[mb] = MB_F;
@@ -554,14 +597,14 @@ zb_status do_backward(zb_stage* S, int mb, const void* dy, void* dx, bool unspli
   if (S->st[mb] != MB_F)
     return set_error(ZB_E_STATE, "stage %d mb %d: backward needs a finished forward and no earlier backward",
                      S->index, mb);
-  ZB_TRY(claim_bw(S, mb));
+  ZB_TRY(claim_bw(S, mb, S->stream));
   const int beta = S->w_count > 0 ? 1 : 0;
   ZB_TRY(copy_in(S, S->bw.at(S->s_bw[mb]) + S->off[S->L - 1].dy, dy));
   ZB_TRY(run_backward(S, mb, dx, unsplit, beta));
-  S->fb.release(S->s_fb[mb]);
+  ZB_TRY(S->fb.release(S->s_fb[mb], S->stream, S->multi));
   S->s_fb[mb] = -1;
   if (unsplit) {
-    release_all(S, mb);
+    ZB_TRY(release_all(S, mb));
     S->st[mb] = MB_DONE;
     S->w_count += 1;
   } else {
@@ -575,7 +618,7 @@ zb_status do_weight(zb_stage* S, int mb) {
   if (S->st[mb] != MB_B)
     return set_error(ZB_E_STATE, "stage %d mb %d: W needs its B first (and runs once)", S->index, mb);
   ZB_TRY(run_weight(S, mb, S->w_count > 0 ? 1 : 0));
-  release_all(S, mb);
+  ZB_TRY(release_all(S, mb));
   S->st[mb] = MB_DONE;
   S->w_count += 1;
   return ZB_OK;
@@ -705,7 +748,7 @@ extern "C" zb_status zb_stage_input_slot(zb_stage* S, int mb, void** p) {
   if (!p) return set_error(ZB_E_ARG, "null output");
   ZB_TRY(check_mb(S, mb));
   if (S->st[mb] != MB_IDLE) return set_error(ZB_E_STATE, "stage %d mb %d already forwarded", S->index, mb);
-  ZB_TRY(claim_fw(S, mb));
+  ZB_TRY(claim_fw(S, mb, S->stream));
   *p = S->fw.at(S->s_fw[mb]) + S->off[0].x;
   return ZB_OK;
 }
@@ -716,7 +759,7 @@ extern "C" zb_status zb_stage_grad_slot(zb_stage* S, int mb, void** p) {
   ZB_TRY(check_mb(S, mb));
   if (S->st[mb] != MB_IDLE && S->st[mb] != MB_F)
     return set_error(ZB_E_STATE, "stage %d mb %d already past its B", S->index, mb);
-  ZB_TRY(claim_bw(S, mb));
+  ZB_TRY(claim_bw(S, mb, S->stream));
   *p = S->bw.at(S->s_bw[mb]) + S->off[S->L - 1].dy;
   return ZB_OK;
 }
@@ -764,17 +807,32 @@ extern "C" zb_status zb_grad_flush(zb_stage* S, int* nonfinite_out) {
   return ZB_OK;
 }
 
+namespace {
+zb_status ensure_done_events(zb_stage* S) {
+  const int m = S->d.n_micro;
+  if ((int)S->f_done.size() == m) return ZB_OK;
+  S->f_done.assign(m, nullptr);
+  S->b_done.assign(m, nullptr);
+  for (int j = 0; j < m; ++j) {
+    ZB_HIP_CHECK(hipEventCreateWithFlags(&S->f_done[j], hipEventDisableTiming));
+    ZB_HIP_CHECK(hipEventCreateWithFlags(&S->b_done[j], hipEventDisableTiming));
+  }
+  return ZB_OK;
+}
+}  // namespace
+
 extern "C" zb_status zb_run_schedule(zb_stage* const* stages, int P, const zb_op* ops, int n_ops,
                                      const void* const* x0, const void* const* dy_last, void* const* y_last,
                                      void* const* dx0, zb_trace_rec* trace) {
   clear_error();
   if (!stages || P < 1 || !ops || n_ops < 1 || !x0 || !dy_last || !y_last || !dx0)
     return set_error(ZB_E_ARG, "null argument");
+  bool multi = false;
   for (int p = 0; p < P; ++p) {
     const zb_stage* S = stages[p];
     if (!S) return set_error(ZB_E_ARG, "stages[%d] is null", p);
     if (S->index != p) return set_error(ZB_E_ARG, "stages[%d] was created as stage %d", p, S->index);
-    if (S->stream != stages[0]->stream) return set_error(ZB_E_ARG, "stages must share one stream");
+    if (S->stream != stages[0]->stream) multi = true;
     if (S->d.n_micro != stages[0]->d.n_micro || S->T != stages[0]->T || S->h != stages[0]->h ||
         S->d.dtype != stages[0]->d.dtype)
       return set_error(ZB_E_ARG, "stage %d: microbatch count, tokens, hidden or dtype differ", p);
@@ -796,40 +854,66 @@ extern "C" zb_status zb_run_schedule(zb_stage* const* stages, int P, const zb_op
       return set_error(ZB_E_BUDGET, "stage %d: order needs %d/%d/%d slots (F->W, F->B, B->W), workspace has %d/%d/%d",
                        p, a, b, c, S->fw.n, S->fb.n, S->bw.n);
   }
-  hipStream_t s = stages[0]->stream;
+  if (multi)
+    for (int p = 0; p < P; ++p) ZB_TRY(ensure_done_events(stages[p]));
+  for (int p = 0; p < P; ++p) stages[p]->multi = multi;
   std::vector<hipEvent_t> ev;
   if (trace) {
     ev.resize(2 * (size_t)n_ops, nullptr);
     for (auto& e : ev) ZB_HIP_CHECK(hipEventCreate(&e));
   }
+  // With one stream per stage, stage s+1's forward waits for stage s's forward
+  // of the same microbatch and stage s's backward for stage s+1's backward;
+  // everything else is ordered by the stage's own stream.
   zb_status rc = ZB_OK;
   for (int i = 0; i < n_ops && rc == ZB_OK; ++i) {
     const zb_op& o = ops[i];
     zb_stage* S = stages[o.stage];
+    hipStream_t st = S->stream;
     const int j = o.mb;
-    if (trace) (void)hipEventRecord(ev[2 * i], s);
+    if (trace) (void)hipEventRecord(ev[2 * i], st);
     switch (o.kind) {
       case 'F': {
+        if (multi && o.stage > 0 && hipStreamWaitEvent(st, stages[o.stage - 1]->f_done[j], 0) != hipSuccess) {
+          rc = set_error(ZB_E_HIP, "hipStreamWaitEvent failed");
+          break;
+        }
         void* y = y_last[j];
         if (o.stage + 1 < P) {
-          rc = zb_stage_input_slot(stages[o.stage + 1], j, &y);
+          zb_stage* N = stages[o.stage + 1];
+          if (N->st[j] != MB_IDLE) {
+            rc = set_error(ZB_E_STATE, "stage %d mb %d already forwarded", N->index, j);
+            break;
+          }
+          rc = claim_fw(N, j, st);
           if (rc != ZB_OK) break;
+          y = N->fw.at(N->s_fw[j]) + N->off[0].x;
         }
         const void* x = x0[j];
         if (o.stage > 0) x = S->fw.at(S->s_fw[j]) + S->off[0].x;
         rc = do_forward(S, j, x, y);
+        if (rc == ZB_OK && multi && hipEventRecord(S->f_done[j], st) != hipSuccess)
+          rc = set_error(ZB_E_HIP, "hipEventRecord failed");
         break;
       }
       case 'B':
       case 'U': {
+        if (multi && o.stage + 1 < P && hipStreamWaitEvent(st, stages[o.stage + 1]->b_done[j], 0) != hipSuccess) {
+          rc = set_error(ZB_E_HIP, "hipStreamWaitEvent failed");
+          break;
+        }
         void* dx = dx0[j];
         if (o.stage > 0) {
-          rc = zb_stage_grad_slot(stages[o.stage - 1], j, &dx);
+          zb_stage* U = stages[o.stage - 1];
+          rc = claim_bw(U, j, st);
           if (rc != ZB_OK) break;
+          dx = U->bw.at(U->s_bw[j]) + U->off[U->L - 1].dy;
         }
         const void* dy = dy_last[j];
         if (o.stage + 1 < P) dy = S->bw.at(S->s_bw[j]) + S->off[S->L - 1].dy;
         rc = do_backward(S, j, dy, dx, o.kind == 'U');
+        if (rc == ZB_OK && multi && hipEventRecord(S->b_done[j], st) != hipSuccess)
+          rc = set_error(ZB_E_HIP, "hipEventRecord failed");
         break;
       }
       case 'W':
@@ -838,14 +922,14 @@ extern "C" zb_status zb_run_schedule(zb_stage* const* stages, int P, const zb_op
       default:
         rc = set_error(ZB_E_ARG, "op %d kind", i);
     }
-    if (trace) (void)hipEventRecord(ev[2 * i + 1], s);
+    if (trace) (void)hipEventRecord(ev[2 * i + 1], st);
   }
   if (rc != ZB_OK) {
     for (auto& e : ev) (void)hipEventDestroy(e);
     return rc;
   }
   if (trace) {
-    ZB_HIP_CHECK(hipEventSynchronize(ev.back()));
+    for (auto& e : ev) ZB_HIP_CHECK(hipEventSynchronize(e));
     for (int i = 0; i < n_ops; ++i) {
       trace[i].op = ops[i];
       float ms = 0.f, t0 = 0.f;

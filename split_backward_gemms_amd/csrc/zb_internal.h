@@ -69,6 +69,8 @@ struct GemmDesc {
 };
 
 zb_status launch_gemm(const GemmDesc& g, hipStream_t s);
+// Independent weight-gradient GEMMs (bf16, W layout, fp32 accumulate) in as few launches as possible.
+zb_status launch_gemm_w_group(const GemmDesc* gs, int n, hipStream_t s);
 
 // Causal attention of one FULL layer (head dim 128).  lse2/dsum: fp32 [heads, T].
 struct AttnArgs {

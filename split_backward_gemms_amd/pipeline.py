@@ -35,11 +35,16 @@ class EmulatedPipeline:
     """P stages of one workload, each with its own weights, on one device and one stream."""
 
     def __init__(self, w, weights: Sequence[Sequence[Dict[str, np.ndarray]]], ops: Optional[Sequence] = None,
-                 device: str = "cuda", stream: Optional[torch.cuda.Stream] = None):
+                 device: str = "cuda", stream: Optional[torch.cuda.Stream] = None,
+                 stage_streams: bool = False):
+        """stage_streams=True gives every emulated stage its own HIP stream (default
+        priority), so independent stages' passes run concurrently."""
         self.w = w
         self.device = torch.device(device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         self.P = w.n_stages
+        self.streams = ([torch.cuda.Stream(self.device) for _ in range(self.P)] if stage_streams
+                        else [self.stream] * self.P)
         self.handles: List[int] = []
         self.weights: List[List[torch.Tensor]] = []
         self.grads: List[List[torch.Tensor]] = []
@@ -51,7 +56,7 @@ class EmulatedPipeline:
             wt = [upload(weights[s][l][nm], w.dtype, self.device) for l in range(w.n_layers) for nm in names]
             gr = [torch.empty(shapes[nm], dtype=torch.float32, device=self.device)
                   for _ in range(w.n_layers) for nm in names]
-            h = zb.zb_stage_create(desc, s, wt, gr, self.stream.cuda_stream)
+            h = zb.zb_stage_create(desc, s, wt, gr, self.streams[s].cuda_stream)
             self.handles.append(h)
             self.weights.append(wt)
             self.grads.append(gr)
@@ -80,10 +85,18 @@ class EmulatedPipeline:
 
     def run(self, ops, xs: Sequence[torch.Tensor], dys: Sequence[torch.Tensor], y_last, dx0, trace: bool = False,
             flush: bool = True, check_finite: bool = False):
+        cur = torch.cuda.current_stream(self.device)
+        distinct = {id(s): s for s in self.streams}.values()
+        for st in distinct:
+            if st != cur:
+                st.wait_stream(cur)  # inputs written on the caller's stream
         tr = zb.zb_run_schedule(self.handles, ops, xs, dys, y_last, dx0, trace=trace)
         flags = None
         if flush:
             flags = [zb.zb_grad_flush(h, check_finite) for h in self.handles]
+        for st in distinct:
+            if st != cur:
+                cur.wait_stream(st)
         return tr, flags
 
     def grads_host(self) -> List[List[Dict[str, np.ndarray]]]:

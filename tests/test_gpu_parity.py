@@ -364,3 +364,29 @@ def test_full_layer_error_per_layer_is_small():
     errs += [_rel_err(dx[j], ref["dx"][0][j]) for j in range(w.n_micro)]
     errs += [_rel_err(dw[0][0][nm], ref["dw"][0][0][nm]) for nm in dw[0][0]]
     assert max(errs) <= 6e-3, errs
+
+
+@pytest.mark.parametrize("name", ["mlp_linears_reduced", "full_reduced"])
+def test_stage_streams_match_single_stream_bitwise(name):
+    """One HIP stream per emulated stage (concurrent stages) gives the same bits
+    as one shared stream: only the overlap changes, not any summation order."""
+    w = REDUCED[name]
+    ws, xs, dys = _inputs(w)
+    _, y1, dx1, dw1, _ = _run(w, ws, xs, dys, "zbh1")
+    ops, _ = zb.zb_schedule_build("zbh1", w.n_stages, w.n_micro)
+    pipe = EmulatedPipeline(w, ws, ops=ops, stage_streams=True)
+    X = [upload(x, w.dtype, "cuda") for x in xs]
+    DY = [upload(d, w.dtype, "cuda") for d in dys]
+    for step in range(2):
+        y, dx = pipe.io_buffers()
+        pipe.run(ops, X, DY, y, dx)
+        torch.cuda.synchronize()
+        dw = pipe.grads_host()
+        for j in range(w.n_micro):
+            assert np.array_equal(_host(y[j]), y1[j])
+            assert np.array_equal(_host(dx[j]), dx1[j])
+        for s_ in range(w.n_stages):
+            for l in range(w.n_layers):
+                for nm in dw[s_][l]:
+                    assert np.array_equal(dw[s_][l][nm].view(np.uint32), dw1[s_][l][nm].view(np.uint32))
+    pipe.close()
