@@ -66,11 +66,15 @@ struct Params {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // keep NaN quiet
-  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);                 // nearest even
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round to nearest even, two at a time (v_cvt_pk_bf16_f32); NaN stays NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)pack_bf16x2(f, 0.0f); }
 
 __device__ __forceinline__ float gelu_f(float z, int kind) {
   if (kind == ZB_GELU_TANH) {
@@ -162,109 +166,105 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-__device__ __forceinline__ uint32_t half_of(const u32x4& v, int e) {
-  uint32_t w = v[e >> 1];
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+// Global -> LDS copies are issued with inline assembly, so the compiler does
+// not track them: every wait for them is explicit.  WAIT_VM_BARRIER<N> lets
+// at most N of this wave's copies stay in flight, drains its LDS reads, and
+// meets the other waves at the barrier; after it, the copies each wave had
+// issued before its last N are visible to all.  The memory clobbers keep the
+// compiler from moving LDS reads across either statement.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// One operand tile of ROWS x 64 (rows = m or n, columns = k) moved global ->
-// registers -> LDS.  KCONTIG: element (row, k) at base[row * ld + k];
-// otherwise at base[k * ld + row].  In LDS the tile is [ROWS][64] bf16 with
-// the 16-byte chunks of row r at chunk ^ swz(r).
-template <int ROWS, bool KCONTIG>
-struct TileLoader {
-  static constexpr int NREG = ROWS / 32;  // 16-byte registers per thread
-  static constexpr int KR = NREG;         // m/n-contiguous: k rows per thread (8 or 4)
-  static constexpr int MCH = ROWS / 64;   // m/n-contiguous: 64-wide column groups
-  using Regs = u32x4[NREG];
-  __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t voff[NREG];   // byte offset of register i's 16 bytes at k0 = 0 (kOOB if outside)
-  uint32_t kstep;        // bytes per unit of k
-  int kofs;              // k of this thread's first element within a tile
-  uint32_t lds_off[KCONTIG ? 2 : 8];
+// Buffer descriptor (gfx9): 48-bit base, stride 0, extent in bytes, raw
+// addressing with range checking against the extent.
+__device__ __forceinline__ u32x4 make_rsrc4(const void* base, uint32_t extent_bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = (uint32_t)b;
+  r[1] = (uint32_t)(b >> 32) & 0xffffu;
+  r[2] = extent_bytes;
+  r[3] = (uint32_t)kRsrcWord3;
+  return r;
+}
 
-  __device__ __forceinline__ TileLoader(const uint16_t* base, int64_t ld, int row0, int rows_lim, int K,
-                                        int tid) {
+// 16 bytes per lane from rsrc at byte offset off (zero when out of range)
+// into LDS at lds + 16 * lane.  lds must be wave-uniform.
+__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t lds, uint32_t off) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// One operand tile (ROWS m/n rows by 64 k) copied global -> LDS by the
+// buffer unit, without passing through registers.  One instruction moves 64
+// lanes x 16 bytes into 1 KiB of consecutive LDS (lane l at byte 16 l); the
+// swizzle is applied by choosing which global chunk each lane fetches.
+//   KCONTIG:   LDS [ROWS][64] bf16; chunk c (8 k values) of row r sits at
+//              position c ^ swz(r) of its 128-byte row.
+//   otherwise: LDS [64][ROWS] bf16; chunk c (8 m values) of k-row k sits at
+//              position c ^ 4 (k % 4) of its 2 ROWS-byte row.
+// The four waves of the workgroup each move a quarter of the tile.
+template <int ROWS, bool KCONTIG>
+struct DmaLoader {
+  static constexpr int NI = ROWS / 32;  // instructions per wave per tile
+  u32x4 rsrc;
+  uint32_t voff[NI];                    // lane's byte offset at k0 = 0 (kOOB outside the matrix)
+  int kofs[KCONTIG ? NI : 1];           // KCONTIG: lane's first k within the tile
+  uint32_t kstep;                       // bytes per unit of k
+  uint32_t lds0;                        // this wave's first KiB within the operand tile (uniform)
+
+  __device__ __forceinline__ DmaLoader(const uint16_t* base, int64_t ld, int row0, int rows_lim, int K,
+                                       int wave, int lane) {
+    lds0 = (uint32_t)(wave * NI * 1024);
     if constexpr (KCONTIG) {
-      const int64_t extent = ((int64_t)(rows_lim - 1) * ld + K) * 2;
-      rsrc = make_rsrc(base, (uint32_t)extent);
+      rsrc = make_rsrc4(base, (uint32_t)(((int64_t)(rows_lim - 1) * ld + K) * 2));
       kstep = 2;
-      const int row = tid >> 3;
-      kofs = (tid & 7) * 8;
 #pragma unroll
-      for (int i = 0; i < NREG; ++i) {
-        const int gr = row0 + row + i * (NT / 8);
-        voff[i] = gr < rows_lim ? (uint32_t)(((int64_t)gr * ld + kofs) * 2) : kOOB;
+      for (int q = 0; q < NI; ++q) {
+        const int row = (wave * NI + q) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(row);
+        const int gr = row0 + row;
+        kofs[q] = 8 * c;
+        voff[q] = gr < rows_lim ? (uint32_t)(((int64_t)gr * ld + 8 * c) * 2) : kOOB;
       }
-      // LDS: row = tid/8 + 32 i, chunk c = tid % 8; swz(row) = (tid/8 % 8) ^ (tid/64) ^ 4 (i % 2)
-      const int c = tid & 7, sw = ((tid >> 3) & 7) ^ (tid >> 6);
-      lds_off[0] = (tid >> 3) * 128 + ((c ^ sw) << 4);
-      lds_off[1] = (tid >> 3) * 128 + ((c ^ sw ^ 4) << 4);
     } else {
-      const int64_t extent = ((int64_t)(K - 1) * ld + rows_lim) * 2;
-      rsrc = make_rsrc(base, (uint32_t)extent);
+      constexpr int CH = ROWS / 8;  // 16-byte chunks per k-row
+      rsrc = make_rsrc4(base, (uint32_t)(((int64_t)(K - 1) * ld + rows_lim) * 2));
       kstep = (uint32_t)(ld * 2);
-      const int mc = (tid & 7) + 8 * ((tid >> 6) % MCH);
-      const int kg = ((tid >> 3) & 7) + 8 * ((tid >> 6) / MCH);
-      kofs = kg * KR;
-      const int gc = row0 + mc * 8;
 #pragma unroll
-      for (int i = 0; i < KR; ++i)
-        voff[i] = gc < rows_lim ? (uint32_t)(((int64_t)(kofs + i) * ld + gc) * 2) : kOOB;
-      // LDS: column e of the 8-wide block goes to row mc*8+e; swz(row) = e ^ (mc % 8)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if constexpr (KR == 8)
-          lds_off[e] = (mc * 8 + e) * 128 + ((kg ^ e ^ (mc & 7)) << 4);
-        else
-          lds_off[e] = (mc * 8 + e) * 128 + ((((kg >> 1) ^ e ^ (mc & 7))) << 4) + 8 * (kg & 1);
+      for (int q = 0; q < NI; ++q) {
+        const int L = (wave * NI + q) * 64 + lane;
+        const int k = L / CH;
+        const int c = (L % CH) ^ (4 * (k & 3));
+        const int gm = row0 + 8 * c;
+        voff[q] = gm < rows_lim ? (uint32_t)(((int64_t)k * ld + gm) * 2) : kOOB;
       }
+      kofs[0] = 0;
     }
   }
 
+  // The tile starting at k0 into the operand tile at LDS address dst.
+  // CHECK_K: the tile straddles K (k-rows past K of an m/n-contiguous operand
+  // fall outside the buffer by themselves).
   template <bool CHECK_K>
-  __device__ __forceinline__ void load(Regs& r, int k0, int K) const {
+  __device__ __forceinline__ void load(uint32_t dst, int k0, int K) const {
     const uint32_t step = (uint32_t)k0 * kstep;
 #pragma unroll
-    for (int i = 0; i < NREG; ++i) {
-      uint32_t off = voff[i] + step;
-      if constexpr (CHECK_K) {
-        const int k = KCONTIG ? (k0 + kofs) : (k0 + kofs + i);
-        off = k < K ? off : kOOB;
-      }
-      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 0));
-    }
-  }
-
-  __device__ __forceinline__ void store(const Regs& r, char* s) const {
-    if constexpr (KCONTIG) {
-#pragma unroll
-      for (int i = 0; i < NREG; ++i)
-        *reinterpret_cast<u32x4*>(s + lds_off[i & 1] + i * (NT / 8) * 128) = r[i];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if constexpr (KR == 8) {
-          u32x4 v;
-          v[0] = half_of(r[0], e) | (half_of(r[1], e) << 16);
-          v[1] = half_of(r[2], e) | (half_of(r[3], e) << 16);
-          v[2] = half_of(r[4], e) | (half_of(r[5], e) << 16);
-          v[3] = half_of(r[6], e) | (half_of(r[7], e) << 16);
-          *reinterpret_cast<u32x4*>(s + lds_off[e]) = v;
-        } else {
-          u32x2 v;
-          v[0] = half_of(r[0], e) | (half_of(r[1], e) << 16);
-          v[1] = half_of(r[2], e) | (half_of(r[3], e) << 16);
-          *reinterpret_cast<u32x2*>(s + lds_off[e]) = v;
-        }
-      }
+    for (int q = 0; q < NI; ++q) {
+      uint32_t off = voff[q] + step;
+      if constexpr (CHECK_K && KCONTIG) off = (k0 + kofs[q] < K) ? off : kOOB;
+      dma16(rsrc, dst + lds0 + q * 1024, off);
     }
   }
 };
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
 
 // Up to kMaxGroup independent GEMMs of one layout and epilogue in one launch;
 // workgroup b works on GEMM g with tile_start[g] <= b < tile_start[g+1].
@@ -275,38 +275,72 @@ struct GroupParams {
   int n;
 };
 
+// LDS ring depth per tile shape: as many 64-deep stages as fit in 160 KiB
+// (a 256x256 stage is 64 KiB, 256x128 48 KiB, 128x128 32 KiB).
+template <int BM, int BN>
+struct Ring {
+  static constexpr int STAGE = (BM + BN) * BKT * 2;
+  static constexpr int NS = BM * BN >= 256 * 256 ? 2 : (BM * BN >= 256 * 128 ? 3 : 4);
+  static constexpr int S2 = NS > 2 ? STAGE : 16;
+  static constexpr int S3 = NS > 3 ? STAGE : 16;
+};
+
 template <int BM, int BN, bool AK, bool BKC, int EPI>
-__device__ __forceinline__ void gemm_tile(const Params& p, int block, char* smem);
+__device__ __forceinline__ void gemm_tile(const Params& p, int block, char* s0, char* s1, char* s2, char* s3);
+
+// The ring stages are separate LDS objects so that the compiler tracks the
+// buffer-to-LDS copies into each one separately when it places its waits.
+#define ZB_GEMM_LDS(BM, BN)                                                  \
+  __shared__ __attribute__((aligned(1024))) char s0[Ring<BM, BN>::STAGE];  \
+  __shared__ __attribute__((aligned(1024))) char s1[Ring<BM, BN>::STAGE];  \
+  __shared__ __attribute__((aligned(1024))) char s2[Ring<BM, BN>::S2];     \
+  __shared__ __attribute__((aligned(1024))) char s3[Ring<BM, BN>::S3]
 
 template <int BM, int BN, bool AK, bool BKC, int EPI>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_mfma(Params p) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * BKT * 2];
-  gemm_tile<BM, BN, AK, BKC, EPI>(p, blockIdx.x, smem);
+  ZB_GEMM_LDS(BM, BN);
+  gemm_tile<BM, BN, AK, BKC, EPI>(p, blockIdx.x, s0, s1, s2, s3);
 }
 
 template <int BM, int BN, bool AK, bool BKC, int EPI>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_mfma_group(GroupParams gp) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * BKT * 2];
+  ZB_GEMM_LDS(BM, BN);
   int b = blockIdx.x;
   const int total = gp.tile_start[gp.n];
   if (total % XCDS == 0) b = (b % XCDS) * (total / XCDS) + b / XCDS;  // one XCD works a GEMM's neighbours
   int g = 0;
   while (g + 1 < gp.n && b >= gp.tile_start[g + 1]) ++g;
-  gemm_tile<BM, BN, AK, BKC, EPI>(gp.p[g], b - gp.tile_start[g], smem);
+  gemm_tile<BM, BN, AK, BKC, EPI>(gp.p[g], b - gp.tile_start[g], s0, s1, s2, s3);
+}
+
+// 32x16 bf16 MFMA operand (lane l: row l % 32, k = 8 (l / 32) .. +7) read
+// from a k-contiguous LDS tile: one 16-byte read at a precomputed offset.
+__device__ __forceinline__ bf16x8 frag_k(const char* tile, uint32_t off) {
+  return *reinterpret_cast<const bf16x8*>(tile + off);
+}
+// The same operand from an m/n-contiguous tile: two transposing 8-byte reads
+// (k 0..3 and 4..7 of the lane's eight), rows RB bytes apart.
+template <int RB>
+__device__ __forceinline__ bf16x8 frag_t(const char* tile, uint32_t off) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off + 4 * RB));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 template <int BM, int BN, bool AK, bool BKC, int EPI>
-__device__ __forceinline__ void gemm_tile(const Params& p, int block, char* smem) {
+__device__ __forceinline__ void gemm_tile(const Params& p, int block, char* s0, char* s1, char* s2, char* s3) {
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int TILE_BYTES = (BM + BN) * BKT * 2;
+  constexpr int NS = Ring<BM, BN>::NS;
+  char* const bufs[4] = {s0, s1, s2, s3};
 
   int tm, tn;
   tile_coords(p, tm, tn, block);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
 
   // The MFMA takes the B fragment as its row operand and the A fragment as its
@@ -326,141 +360,157 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int block, char* smem
 
   __amdgpu_buffer_rsrc_t crsrc = make_rsrc(p.C, (uint32_t)(((int64_t)(p.M - 1) * p.ldc + p.N) *
                                                            (EPI == EPI_ACC ? 4 : 2)));
-  if constexpr (EPI == EPI_ACC) {
-    if (p.beta) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int m = em + i * 32, n = en + j * 32 + 8 * g;
-            const uint32_t off = (m < p.M && n < p.N) ? (uint32_t)(((int64_t)m * p.ldc + n) * 4) : kOOB;
-            const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(crsrc, (int)off, 0, 0));
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc[i][j][4 * g + t] = v[t];
-          }
-    }
-  }
 
-  TileLoader<BM, AK> la(static_cast<const uint16_t*>(p.A), p.lda, m0, p.M, p.K, tid);
-  TileLoader<BN, BKC> lb(static_cast<const uint16_t*>(p.B), p.ldb, n0, p.N, p.K, tid);
+  DmaLoader<BM, AK> la(static_cast<const uint16_t*>(p.A), p.lda, m0, p.M, p.K, wave, lane);
+  DmaLoader<BN, BKC> lb(static_cast<const uint16_t*>(p.B), p.ldb, n0, p.N, p.K, wave, lane);
+  constexpr int NI = DmaLoader<BM, AK>::NI + DmaLoader<BN, BKC>::NI;  // copies per wave per tile
   const int nk = (p.K + BKT - 1) / BKT;
   const bool k_ragged = (p.K % BKT) != 0;
 
-  // Fragment read offsets: row = base + i*32 + lane%32, chunk = 2 kk + lane/32;
-  // its swizzled chunk is P ^ 2 (kk ^ 2 (i % 2)) with P fixed per lane.
+  // Fragment read offsets within an operand tile.
+  //  k-contiguous: row = base + 32 i + lane % 32, chunk = 2 kk + lane / 32,
+  //    stored at P ^ 2 (kk ^ 2 (i % 2)) with P fixed per lane: ra[kk ^ 2 (i % 2)] + 4096 i.
+  //  m/n-contiguous (transposing reads): lane l = 16 g + ii reads k-row
+  //    16 kk + 8 (g / 2) + 4 h + ii / 4 at column base + 32 i + 16 (g % 2) + 4 (ii % 4);
+  //    with r = ii / 4 = k % 4 the chunk's position is ((base / 32 + i) ^ r) * 4 + s.
   uint32_t ra[4], rb[4];
   {
     const int P = (lane >> 5) ^ (lane & 7) ^ ((lane >> 3) & 3);
+    const int g = lane >> 4, ii = lane & 15, r = ii >> 2;
+    const int s = 2 * (g & 1) + ((ii & 3) >> 1);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      ra[q] = (wm * WTM + (lane & 31)) * 128 + ((P ^ (2 * q)) << 4);
-      rb[q] = BM * 128 + (wn * WTN + (lane & 31)) * 128 + ((P ^ (2 * q)) << 4);
+      if constexpr (AK) {
+        ra[q] = (wm * WTM + (lane & 31)) * 128 + ((P ^ (2 * q)) << 4);
+      } else {
+        const int blk = wm * WTM / 32 + q;
+        ra[q] = (8 * (g >> 1) + r) * (BM * 2) + 64 * (blk ^ r) + 16 * s + 8 * (ii & 1);
+      }
+      if constexpr (BKC) {
+        rb[q] = (wn * WTN + (lane & 31)) * 128 + ((P ^ (2 * q)) << 4);
+      } else {
+        const int blk = wn * WTN / 32 + q;
+        rb[q] = (8 * (g >> 1) + r) * (BN * 2) + 64 * (blk ^ r) + 16 * s + 8 * (ii & 1);
+      }
     }
   }
   bf16x8 af[2][TM], bfr[2][TN];
-  auto read_frags = [&](const char* buf, int kk, int fb) {
+  auto read_a = [&](const char* buf, int kk, int fb) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      af[fb][i] = *reinterpret_cast<const bf16x8*>(buf + ra[kk ^ (2 * (i & 1))] + i * 32 * 128);
+    for (int i = 0; i < TM; ++i) {
+      if constexpr (AK) af[fb][i] = frag_k(buf, ra[kk ^ (2 * (i & 1))] + i * 32 * 128);
+      else af[fb][i] = frag_t<BM * 2>(buf, ra[i] + kk * 16 * (BM * 2));
+    }
+  };
+  auto read_b = [&](const char* buf, int kk, int fb) {
+    const char* bt = buf + BM * 128;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (BKC) bfr[fb][j] = frag_k(bt, rb[kk ^ (2 * (j & 1))] + j * 32 * 128);
+      else bfr[fb][j] = frag_t<BN * 2>(bt, rb[j] + kk * 16 * (BN * 2));
+    }
+  };
+  auto read_frags = [&](const char* buf, int kk, int fb) {
+    read_a(buf, kk, fb);
+    read_b(buf, kk, fb);
+  };
+  auto mfma_row = [&](int fb, int i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      bfr[fb][j] = *reinterpret_cast<const bf16x8*>(buf + rb[kk ^ (2 * (j & 1))] + j * 32 * 128);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fb][j], af[fb][i], acc[i][j], 0, 0, 0);
   };
-
-  // Two sets of staging registers: tile t travels global -> set t%2 -> LDS
-  // buffer t%2.  Loads run two tiles ahead of the MFMAs.
-  typename TileLoader<BM, AK>::Regs ra_stage[2];
-  typename TileLoader<BN, BKC>::Regs rb_stage[2];
-  auto issue = [&](auto set, int t) {
-    if (t == nk - 1 && k_ragged) {
-      la.template load<true>(ra_stage[decltype(set)::value], t * BKT, p.K);
-      lb.template load<true>(rb_stage[decltype(set)::value], t * BKT, p.K);
+  auto mfmas = [&](int fb) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) mfma_row(fb, i);
+  };
+  // Copies of tile t into ring stage BI: operand A (which = 0) or B (1).
+  auto dma_op = [&](auto bi, int which, int t) {
+    const uint32_t b = __builtin_amdgcn_readfirstlane(lds_addr(bufs[decltype(bi)::value]));
+    const bool rag = k_ragged && t == nk - 1;
+    if (which == 0) {
+      if (rag) la.template load<true>(b, t * BKT, p.K);
+      else la.template load<false>(b, t * BKT, p.K);
     } else {
-      la.template load<false>(ra_stage[decltype(set)::value], t * BKT, p.K);
-      lb.template load<false>(rb_stage[decltype(set)::value], t * BKT, p.K);
+      if (rag) lb.template load<true>(b + BM * 128, t * BKT, p.K);
+      else lb.template load<false>(b + BM * 128, t * BKT, p.K);
     }
   };
-  auto stage_to_lds = [&](auto set, char* buf) {
-    la.store(ra_stage[decltype(set)::value], buf);
-    lb.store(rb_stage[decltype(set)::value], buf + BM * 128);
+  auto dma = [&](auto bi, int t) {
+    dma_op(bi, 0, t);
+    dma_op(bi, 1, t);
   };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
 
-  if (nk > 0) {  // K == 0: empty sum, the epilogue sees the initial accumulators
-    issue(S0{}, 0);
-    if (nk > 1) issue(S1{}, 1);
-    stage_to_lds(S0{}, smem);
-    __syncthreads();
-    read_frags(smem, 0, 0);
+  // Ring: tiles t+1 .. t+NS-1 are in flight while tile t feeds the MFMAs;
+  // tile t+NS goes into tile t's stage once every wave has read it.
+  dma(std::integral_constant<int, 0>{}, 0);
+  if (NS > 1 && 1 < nk) dma(std::integral_constant<int, 1>{}, 1);
+  if (NS > 2 && 2 < nk) dma(std::integral_constant<int, (NS > 2 ? 2 : 0)>{}, 2);
+  if (NS > 3 && 3 < nk) dma(std::integral_constant<int, (NS > 3 ? 3 : 0)>{}, 3);
+  if (nk > 0) {  // K == 0: empty sum
+    if (nk >= NS) wait_vm_barrier<(NS - 1) * NI>();
+    else wait_vm_barrier<0>();
+    read_frags(bufs[0], 0, 0);
   }
 
-  // One tile: fragments are double-buffered across its four 16-deep k steps
-  // (LDS reads for step kk+1 go out before the MFMAs of step kk); the next
-  // tile moves from its staging registers into the other LDS buffer mid-tile.
-  auto tile = [&](auto par, int kt) {
-    constexpr int PAR = decltype(par)::value;
-    const char* cur = smem + PAR * TILE_BYTES;
-    char* nxt = smem + (PAR ^ 1) * TILE_BYTES;
-    if (kt + 2 < nk) issue(par, kt + 2);
+  // One tile from stage CUR: fragments double-buffered across its four
+  // 16-deep k steps.  Before the last step every wave waits for its own copies
+  // of tile t+1 and for its reads of tile t, then meets the others at the
+  // barrier.  The last step's MFMA rows are interleaved with the first reads
+  // of tile t+1 (issued even past the last tile, where they are discarded, so
+  // the compiler sees one path) and with the refill of stage CUR.
+  auto body = [&](auto bi, int t) {
+    constexpr int CUR = decltype(bi)::value;
+    constexpr int NXT = (CUR + 1) % NS;
+    const char* cur = bufs[CUR];
 #pragma unroll
-    for (int kk = 0; kk < BKT / 16; ++kk) {
-      const int fb = kk & 1;
-      if (kk + 1 < BKT / 16) read_frags(cur, kk + 1, fb ^ 1);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fb][j], af[fb][i], acc[i][j], 0, 0, 0);
-      if (kk == BKT / 16 - 2 && kt + 1 < nk) stage_to_lds(std::integral_constant<int, PAR ^ 1>{}, nxt);
+    for (int kk = 0; kk < BKT / 16 - 1; ++kk) {
+      read_frags(cur, kk + 1, (kk + 1) & 1);  // all reads go out ahead of the step's MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(kk & 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
-    if (kt + 1 < nk) read_frags(nxt, 0, 0);
+    if (t + NS - 1 < nk) wait_vm_barrier<(NS - 2) * NI>();
+    else wait_vm_barrier<0>();
+    const bool refill = t + NS < nk;
+    read_a(bufs[NXT], 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_row(1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_b(bufs[NXT], 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_row(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (refill) dma_op(bi, 0, t + NS);
+    if constexpr (TM > 2) mfma_row(1, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (refill) dma_op(bi, 1, t + NS);
+    if constexpr (TM > 3) mfma_row(1, 3);
+    __builtin_amdgcn_sched_barrier(0);
   };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, (NS > 2 ? 2 : 0)>;
+  using B3 = std::integral_constant<int, (NS > 3 ? 3 : 0)>;
 
-  // Steady state (tile kt+2 exists): one branch-free block per tile, so the
-  // compiler can schedule loads, LDS traffic and MFMAs of a tile together.
-  auto tile_steady = [&](auto par, int kt) {
-    constexpr int PAR = decltype(par)::value;
-    const char* cur = smem + PAR * TILE_BYTES;
-    char* nxt = smem + (PAR ^ 1) * TILE_BYTES;
-    if (k_ragged) {
-      la.template load<true>(ra_stage[PAR], (kt + 2) * BKT, p.K);
-      lb.template load<true>(rb_stage[PAR], (kt + 2) * BKT, p.K);
-    } else {
-      la.template load<false>(ra_stage[PAR], (kt + 2) * BKT, p.K);
-      lb.template load<false>(rb_stage[PAR], (kt + 2) * BKT, p.K);
-    }
-#pragma unroll
-    for (int kk = 0; kk < BKT / 16; ++kk) {
-      const int fb = kk & 1;
-      if (kk + 1 < BKT / 16) read_frags(cur, kk + 1, fb ^ 1);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fb][j], af[fb][i], acc[i][j], 0, 0, 0);
-      if (kk == BKT / 16 - 2) stage_to_lds(std::integral_constant<int, PAR ^ 1>{}, nxt);
-      __builtin_amdgcn_sched_barrier(0);  // keep each k step's reads next to its MFMAs
-    }
-    __syncthreads();
-    read_frags(nxt, 0, 0);
-  };
-
-  int kt = 0;
-  for (; kt + 3 < nk; kt += 2) {
-    tile_steady(S0{}, kt);
-    tile_steady(S1{}, kt + 1);
+  int t = 0;
+  for (; t + NS <= nk; t += NS) {
+    body(B0{}, t);
+    body(B1{}, t + 1);
+    if constexpr (NS > 2) body(B2{}, t + 2);
+    if constexpr (NS > 3) body(B3{}, t + 3);
   }
-  // The last one to three tiles, with their guards; kt is even here.
-  if (kt < nk) tile(S0{}, kt);
-  if (kt + 1 < nk) tile(S1{}, kt + 1);
-  if (kt + 2 < nk) tile(S0{}, kt + 2);
+  // Fewer than NS tiles left; t is a multiple of NS, so tile t + b is in stage b.
+  if (t < nk) body(B0{}, t);
+  if constexpr (NS > 2) {
+    if (t + 1 < nk) body(B1{}, t + 1);
+  }
+  if constexpr (NS > 3) {
+    if (t + 2 < nk) body(B2{}, t + 2);
+  }
 
   // Epilogue: lane (i, j, g) owns C[em + 32 i][en + 32 j + 8 g + 0..3].
   if constexpr (EPI == EPI_ACC) {
+    // dW (+)= this GEMM's sum over k, in fp32.
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -471,7 +521,12 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int block, char* smem
           const uint32_t off = (m < p.M && n < p.N) ? (uint32_t)(((int64_t)m * p.ldc + n) * 4) : kOOB;
           f32x4 v;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * g + t];
+          for (int t2 = 0; t2 < 4; ++t2) v[t2] = acc[i][j][4 * g + t2];
+          if (p.beta) {
+            const f32x4 c = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(crsrc, (int)off, 0, 0));
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2) v[t2] = c[t2] + v[t2];
+          }
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), crsrc, (int)off, 0, 0);
         }
   } else {
@@ -489,7 +544,7 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int block, char* smem
           const bool ok = m < p.M && n < p.N;
           float v[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * g + t];
+          for (int t2 = 0; t2 < 4; ++t2) v[t2] = acc[i][j][4 * g + t2];
           if constexpr (EPI == EPI_RESID || EPI == EPI_DGELU) {
             const uint32_t roff = ok ? (uint32_t)(((int64_t)m * p.ldr + n) * 2) : kOOB;
             const u32x2 rv = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rrsrc, (int)roff, 0, 0));
@@ -507,7 +562,7 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int block, char* smem
             const u32x2 zv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
             __builtin_amdgcn_raw_buffer_store_b64(zv, zrsrc, (int)zoff, 0, 0);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] = gelu_f(v[t], p.gelu);
+            for (int t2 = 0; t2 < 4; ++t2) v[t2] = gelu_f(v[t2], p.gelu);
           }
           const uint32_t off = ok ? (uint32_t)(((int64_t)m * p.ldc + n) * 2) : kOOB;
           const u32x2 cv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -624,9 +679,7 @@ void launch_w_group(GroupParams gp, hipStream_t s) {
 template <bool AK, bool BKC, int EPI>
 void launch_tile(int t, const Params& p, hipStream_t s) {
   switch (t) {
-    case 0:
-      if constexpr (AK || BKC) launch_mfma<256, 256, AK, BKC, EPI>(p, s);
-      break;
+    case 0: launch_mfma<256, 256, AK, BKC, EPI>(p, s); break;
     case 1: launch_mfma<256, 128, AK, BKC, EPI>(p, s); break;
     default: launch_mfma<128, 128, AK, BKC, EPI>(p, s); break;
   }
@@ -729,8 +782,7 @@ zb_status launch_gemm(const GemmDesc& g, hipStream_t s) {
     if (ea >= lim || eb >= lim || ec >= lim)
       return set_error(ZB_E_UNSUPPORTED, "gemm: an operand spans 2 GiB or more");
   }
-  const bool w_layout = !g.a_kcontig && !g.b_kcontig;
-  const int t = pick_tile(g.M, g.N, w_layout ? 1 : 0);
+  const int t = pick_tile(g.M, g.N, 0);
   char name[48];
   static const char* kEpi[] = {"store", "resid", "gelu", "dgelu", "acc"};
   snprintf(name, sizeof name, "gemm_%s_%dx%d_%s", g.tag, kTiles[t].bm, kTiles[t].bn, kEpi[g.epi]);
