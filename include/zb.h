@@ -222,7 +222,8 @@ zb_status zb_stage_class_bytes(const zb_stage* st, size_t* fw, size_t* fb, size_
 zb_status zb_stage_workspace_bytes(zb_stage* st, const zb_op* ops, int n_ops, size_t* bytes);
 
 /* Hand the stage a device buffer of at least the planned size (256-byte
- * aligned).  The stage sub-allocates its stash from it; the caller keeps
+ * aligned).  The stage sub-allocates its stash and the scratch of its kernels
+ * (including the split-K partial sums of its GEMMs) from it; the caller keeps
  * ownership.  Only allowed while no microbatch is live.
  * Errors: ZB_E_ARG (null, misaligned), ZB_E_BUDGET (too small), ZB_E_STATE. */
 zb_status zb_stage_bind_workspace(zb_stage* st, void* dev_ptr, size_t bytes);

@@ -60,6 +60,10 @@ struct Params {
   int gelu;
   int nbm, nbn;
   int xcd_remap;
+  // Split-K: `splits` workgroups share an output tile, each reducing over
+  // `kts` 64-deep k tiles; with EPI_PART split s writes its fp32 sum to
+  // C + s * M * ldc, and a second kernel adds the splits in order.
+  int splits, kts;
 };
 
 // ------------------------------------------------------------- elementwise math
@@ -134,12 +138,15 @@ __device__ __forceinline__ void epi_store(const Params& p, int m, int n, float v
   }
 }
 
-// Workgroup -> output tile.  Consecutive logical tiles share an XCD (its own
-// L2); within the logical order, tiles go in groups of 8 tile-rows so that
-// neighbours reuse A rows and B columns.
-__device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn, int b) {
-  const int nblk = p.nbm * p.nbn;
-  if (p.xcd_remap && nblk % XCDS == 0) b = (b % XCDS) * (nblk / XCDS) + b / XCDS;
+// Workgroups are dealt to the 8 XCDs round-robin; renumber them so that
+// consecutive logical indices run on one XCD (its own L2).
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  return total % XCDS == 0 ? (b % XCDS) * (total / XCDS) + b / XCDS : b;
+}
+
+// Logical tile index -> output tile.  Tiles go in groups of 8 tile-rows so
+// that neighbours reuse A rows and B columns.
+__device__ __forceinline__ void tile_raster(const Params& p, int& tm, int& tn, int b) {
   const int G = 8;
   const int per_group = G * p.nbn;
   const int group = b / per_group;
@@ -148,6 +155,11 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn, i
   const int r = b - group * per_group;
   tm = first_m + r % gsz;
   tn = r / gsz;
+}
+
+__device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn, int b) {
+  if (p.xcd_remap) b = xcd_remap(b, p.nbm * p.nbn);
+  tile_raster(p, tm, tn, b);
 }
 
 // ------------------------------------------------------------- bf16 MFMA GEMM
@@ -286,7 +298,8 @@ struct Ring {
 };
 
 template <int BM, int BN, bool AK, bool BKC, int EPI>
-__device__ __forceinline__ void gemm_tile(const Params& p, int block, char* s0, char* s1, char* s2, char* s3);
+__device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, char* s0, char* s1, char* s2,
+                                          char* s3);
 
 // The ring stages are separate LDS objects so that the compiler tracks the
 // buffer-to-LDS copies into each one separately when it places its waits.
@@ -300,7 +313,9 @@ template <int BM, int BN, bool AK, bool BKC, int EPI>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_mfma(Params p) {
   ZB_GEMM_LDS(BM, BN);
-  gemm_tile<BM, BN, AK, BKC, EPI>(p, blockIdx.x, s0, s1, s2, s3);
+  int b = blockIdx.x;
+  if (p.xcd_remap) b = xcd_remap(b, p.nbm * p.nbn * p.splits);  // a tile's splits share an XCD
+  gemm_tile<BM, BN, AK, BKC, EPI>(p, b / p.splits, b % p.splits, s0, s1, s2, s3);
 }
 
 template <int BM, int BN, bool AK, bool BKC, int EPI>
@@ -312,7 +327,7 @@ gemm_bf16_mfma_group(GroupParams gp) {
   if (total % XCDS == 0) b = (b % XCDS) * (total / XCDS) + b / XCDS;  // one XCD works a GEMM's neighbours
   int g = 0;
   while (g + 1 < gp.n && b >= gp.tile_start[g + 1]) ++g;
-  gemm_tile<BM, BN, AK, BKC, EPI>(gp.p[g], b - gp.tile_start[g], s0, s1, s2, s3);
+  gemm_tile<BM, BN, AK, BKC, EPI>(gp.p[g], b - gp.tile_start[g], 0, s0, s1, s2, s3);
 }
 
 // 32x16 bf16 MFMA operand (lane l: row l % 32, k = 8 (l / 32) .. +7) read
@@ -330,14 +345,15 @@ __device__ __forceinline__ bf16x8 frag_t(const char* tile, uint32_t off) {
 }
 
 template <int BM, int BN, bool AK, bool BKC, int EPI>
-__device__ __forceinline__ void gemm_tile(const Params& p, int block, char* s0, char* s1, char* s2, char* s3) {
+__device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, char* s0, char* s1, char* s2,
+                                          char* s3) {
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int NS = Ring<BM, BN>::NS;
   char* const bufs[4] = {s0, s1, s2, s3};
 
   int tm, tn;
-  tile_coords(p, tm, tn, block);
+  tile_raster(p, tm, tn, tile);
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -364,8 +380,11 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int block, char* s0, 
   DmaLoader<BM, AK> la(static_cast<const uint16_t*>(p.A), p.lda, m0, p.M, p.K, wave, lane);
   DmaLoader<BN, BKC> lb(static_cast<const uint16_t*>(p.B), p.ldb, n0, p.N, p.K, wave, lane);
   constexpr int NI = DmaLoader<BM, AK>::NI + DmaLoader<BN, BKC>::NI;  // copies per wave per tile
-  const int nk = (p.K + BKT - 1) / BKT;
-  const bool k_ragged = (p.K % BKT) != 0;
+  // This workgroup's k tiles: [kt0, kt0 + nk) of the product's ceil(K / 64).
+  const int nk_all = (p.K + BKT - 1) / BKT;
+  const int kt0 = split * p.kts;
+  const int nk = min(nk_all - kt0, p.kts);
+  const bool k_ragged = (p.K % BKT) != 0;  // only the product's last tile straddles K
 
   // Fragment read offsets within an operand tile.
   //  k-contiguous: row = base + 32 i + lane % 32, chunk = 2 kk + lane / 32,
@@ -426,13 +445,14 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int block, char* s0, 
   // Copies of tile t into ring stage BI: operand A (which = 0) or B (1).
   auto dma_op = [&](auto bi, int which, int t) {
     const uint32_t b = __builtin_amdgcn_readfirstlane(lds_addr(bufs[decltype(bi)::value]));
-    const bool rag = k_ragged && t == nk - 1;
+    const int k0 = (kt0 + t) * BKT;
+    const bool rag = k_ragged && kt0 + t == nk_all - 1;
     if (which == 0) {
-      if (rag) la.template load<true>(b, t * BKT, p.K);
-      else la.template load<false>(b, t * BKT, p.K);
+      if (rag) la.template load<true>(b, k0, p.K);
+      else la.template load<false>(b, k0, p.K);
     } else {
-      if (rag) lb.template load<true>(b + BM * 128, t * BKT, p.K);
-      else lb.template load<false>(b + BM * 128, t * BKT, p.K);
+      if (rag) lb.template load<true>(b + BM * 128, k0, p.K);
+      else lb.template load<false>(b + BM * 128, k0, p.K);
     }
   };
   auto dma = [&](auto bi, int t) {
@@ -509,7 +529,24 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int block, char* s0, 
   }
 
   // Epilogue: lane (i, j, g) owns C[em + 32 i][en + 32 j + 8 g + 0..3].
-  if constexpr (EPI == EPI_ACC) {
+  if constexpr (EPI == EPI_PART) {
+    // This split's fp32 partial sum, to its own M x N slice.
+    float* const cp = static_cast<float*>(p.C) + (int64_t)split * p.M * p.ldc;
+    const __amdgpu_buffer_rsrc_t prsrc = make_rsrc(cp, (uint32_t)(((int64_t)(p.M - 1) * p.ldc + p.N) * 4));
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int m = em + i * 32, n = en + j * 32 + 8 * g;
+          const uint32_t off = (m < p.M && n < p.N) ? (uint32_t)(((int64_t)m * p.ldc + n) * 4) : kOOB;
+          f32x4 v;
+#pragma unroll
+          for (int t2 = 0; t2 < 4; ++t2) v[t2] = acc[i][j][4 * g + t2];
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), prsrc, (int)off, 0, 0);
+        }
+  } else if constexpr (EPI == EPI_ACC) {
     // dW (+)= this GEMM's sum over k, in fp32.
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -569,6 +606,49 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int block, char* s0, 
           __builtin_amdgcn_raw_buffer_store_b64(cv, crsrc, (int)off, 0, 0);
         }
   }
+}
+
+// Split-K second pass: C = epilogue(sum of the splits' fp32 partials, added in
+// split order).  Partials are [splits][M][N] fp32; each thread takes 8
+// consecutive outputs of a row (N and the leading dimensions of C, R and Z are
+// multiples of 8, checked on the host).
+template <int EPI>
+__global__ void __launch_bounds__(256) splitk_reduce(Params p, const float* part) {
+  const int groups = p.N / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)p.M * groups) return;
+  const int m = (int)(idx / groups), n = (int)(idx % groups) * 8;
+  const int64_t slice = (int64_t)p.M * p.N;
+  const f32x4* q = reinterpret_cast<const f32x4*>(part + (int64_t)m * p.N + n);
+  f32x4 a = q[0], b = q[1];
+  for (int s = 1; s < p.splits; ++s) {
+    const f32x4* r = reinterpret_cast<const f32x4*>(part + s * slice + (int64_t)m * p.N + n);
+    a += r[0];
+    b += r[1];
+  }
+  float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  if constexpr (EPI == EPI_RESID || EPI == EPI_DGELU) {
+    const u32x4 rv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.R) + (int64_t)m * p.ldr + n);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = rv[e >> 1];
+      const float r = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+      if constexpr (EPI == EPI_RESID) v[e] += r;
+      else v[e] *= gelu_grad_f(r, p.gelu);
+    }
+  }
+  if constexpr (EPI == EPI_GELU) {
+    u32x4 zv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) zv[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.Z) + (int64_t)m * p.ldz + n) = zv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = gelu_f(v[e], p.gelu);
+  }
+  u32x4 cv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) cv[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+  *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.C) + (int64_t)m * p.ldc + n) = cv;
 }
 
 // ------------------------------------------------- fp32 storage (plain FMA tiles)
@@ -633,22 +713,43 @@ __global__ void __launch_bounds__(256) gemm_simt(Params p, int ak, int bk) {
 
 struct TileCfg {
   int bm, bn;
-  float eff;  // relative per-CU throughput of the tile shape
+  double rate;  // FLOP per microsecond of one workgroup with every CU busy (measured, MI355X)
 };
-constexpr TileCfg kTiles[] = {{256, 256, 1.0f}, {256, 128, 0.85f}, {128, 128, 0.7f}};
+constexpr TileCfg kTiles[] = {{256, 256, 5.4e6}, {256, 128, 4.75e6}, {128, 128, 4.1e6}};
 constexpr int kCUs = 256;
+constexpr double kFixedUs = 2.0;        // per workgroup: first copies in, epilogue out
+constexpr double kReduceFixedUs = 3.0;  // split-K: the second launch
+constexpr double kReduceBytesPerUs = 4e6;   // its fp32 partial reads and bf16 traffic
+constexpr double kPartWriteBytesPerUs = 8e6;  // the partial writes, beside the MFMA work
 
-// first_tile = 1 skips 256x256 (the W layout needs too many registers for it).
-int pick_tile(int M, int N, int first_tile) {
-  int best = first_tile;
-  double best_cost = 1e300;
-  for (int t = first_tile; t < 3; ++t) {
-    const int nb = ((M + kTiles[t].bm - 1) / kTiles[t].bm) * ((N + kTiles[t].bn - 1) / kTiles[t].bn);
-    const int waves = (nb + kCUs - 1) / kCUs;
-    const double cost = (double)waves * kTiles[t].bm * kTiles[t].bn / kTiles[t].eff;
-    if (cost < best_cost - 1e-9) {
-      best_cost = cost;
-      best = t;
+struct GemmPlan {
+  int tile = 2, splits = 1, kts = 0;
+  double cost = 1e300;
+};
+
+// Tile shape and split-K factor by a wave-quantised cost model: whole waves
+// of workgroups over the CUs, each taking its k tiles at the shape's rate plus
+// a fixed overhead; a split adds the pass that reads the fp32 partials back.
+// Splitting is only considered while the tiles alone leave CUs idle, and only
+// when the partials fit in `arena` bytes.
+GemmPlan plan_gemm(int M, int N, int K, bool can_split, size_t arena) {
+  const int nk = (K + BKT - 1) / BKT;
+  GemmPlan best;
+  best.kts = nk;
+  for (int t = 0; t < 3; ++t) {
+    const TileCfg& c = kTiles[t];
+    const int nb = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+    for (int S = 1; S <= 4; S *= 2) {
+      if (S > 1 && (!can_split || S > nk || nb >= kCUs)) continue;
+      const int kts = S > 1 ? (nk + S - 1) / S : nk;
+      if (S > 1 && (S - 1) * kts >= nk) continue;
+      if (S > 1 && (double)S * M * N * 4 > (double)arena) continue;
+      const int waves = (nb * S + kCUs - 1) / kCUs;
+      double cost = waves * (2.0 * c.bm * c.bn * (double)kts * BKT / c.rate + kFixedUs);
+      if (S > 1)
+        cost += kReduceFixedUs + (4.0 * S + 4.0) * M * (double)N / kReduceBytesPerUs +
+                4.0 * S * M * (double)N / kPartWriteBytesPerUs;
+      if (cost < best.cost - 1e-9) best = GemmPlan{t, S, kts, cost};
     }
   }
   return best;
@@ -659,7 +760,11 @@ void launch_mfma(Params p, hipStream_t s) {
   p.nbm = (p.M + BM - 1) / BM;
   p.nbn = (p.N + BN - 1) / BN;
   p.xcd_remap = 1;
-  hipLaunchKernelGGL((gemm_bf16_mfma<BM, BN, AK, BKC, EPI>), dim3(p.nbm * p.nbn), dim3(NT), 0, s, p);
+  if (p.splits < 1) {
+    p.splits = 1;
+    p.kts = (p.K + BKT - 1) / BKT;
+  }
+  hipLaunchKernelGGL((gemm_bf16_mfma<BM, BN, AK, BKC, EPI>), dim3(p.nbm * p.nbn * p.splits), dim3(NT), 0, s, p);
 }
 
 template <int BM, int BN>
@@ -669,6 +774,8 @@ void launch_w_group(GroupParams gp, hipStream_t s) {
     gp.p[g].nbm = (gp.p[g].M + BM - 1) / BM;
     gp.p[g].nbn = (gp.p[g].N + BN - 1) / BN;
     gp.p[g].xcd_remap = 0;
+    gp.p[g].splits = 1;
+    gp.p[g].kts = (gp.p[g].K + BKT - 1) / BKT;
     gp.tile_start[g] = total;
     total += gp.p[g].nbm * gp.p[g].nbn;
   }
@@ -741,6 +848,12 @@ zb_status launch_gemm_w_group(const GemmDesc* gs, int n, hipStream_t s) {
   return ZB_OK;
 }
 
+size_t gemm_split_arena(int M, int N, int K) {
+  if (N % 8) return 0;
+  const GemmPlan pl = plan_gemm(M, N, K, true, (size_t)-1);
+  return pl.splits == 1 ? 0 : (size_t)pl.splits * M * N * 4;
+}
+
 zb_status launch_gemm(const GemmDesc& g, hipStream_t s) {
   if (g.M < 0 || g.N < 0 || g.K < 0) return set_error(ZB_E_ARG, "gemm: negative size");
   if (g.M == 0 || g.N == 0) return ZB_OK;
@@ -782,12 +895,43 @@ zb_status launch_gemm(const GemmDesc& g, hipStream_t s) {
     if (ea >= lim || eb >= lim || ec >= lim)
       return set_error(ZB_E_UNSUPPORTED, "gemm: an operand spans 2 GiB or more");
   }
-  const int t = pick_tile(g.M, g.N, 0);
+  // Split-K needs an arena and 16-byte rows in the second pass.
+  const bool rz8 = (g.epi != EPI_RESID && g.epi != EPI_DGELU) || (g.ldr % 8 == 0 && aligned16(g.R));
+  const bool z8 = g.epi != EPI_GELU || (g.ldz % 8 == 0 && aligned16(g.Z));
+  const bool can_split = g.epi != EPI_ACC && g.part && g.N % 8 == 0 && g.ldc % 8 == 0 && aligned16(g.C) &&
+                         aligned16(g.part) && rz8 && z8;
+  const GemmPlan pl = plan_gemm(g.M, g.N, g.K, can_split, g.part_bytes);
+  const int t = pl.tile;
+  p.splits = pl.splits;
+  p.kts = pl.kts;
   char name[48];
   static const char* kEpi[] = {"store", "resid", "gelu", "dgelu", "acc"};
-  snprintf(name, sizeof name, "gemm_%s_%dx%d_%s", g.tag, kTiles[t].bm, kTiles[t].bn, kEpi[g.epi]);
+  if (pl.splits > 1)
+    snprintf(name, sizeof name, "gemm_%s_%dx%dk%d_%s", g.tag, kTiles[t].bm, kTiles[t].bn, pl.splits, kEpi[g.epi]);
+  else
+    snprintf(name, sizeof name, "gemm_%s_%dx%d_%s", g.tag, kTiles[t].bm, kTiles[t].bn, kEpi[g.epi]);
   ProfScope ps(name, flops, bytes, s);
   const bool ak = g.a_kcontig, bk = g.b_kcontig;
+  if (pl.splits > 1) {
+    Params pp = p;
+    pp.C = g.part;
+    pp.ldc = g.N;
+    if (ak && !bk) launch_tile<true, false, EPI_PART>(t, pp, s);
+    else if (ak && bk) launch_tile<true, true, EPI_PART>(t, pp, s);
+    else return set_error(ZB_E_UNSUPPORTED, "gemm: split-K of this layout not built");
+    ZB_HIP_CHECK(hipGetLastError());
+    const int64_t threads = (int64_t)g.M * (g.N / 8);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    switch (g.epi) {
+      case EPI_STORE: hipLaunchKernelGGL(splitk_reduce<EPI_STORE>, grid, dim3(256), 0, s, p, g.part); break;
+      case EPI_RESID: hipLaunchKernelGGL(splitk_reduce<EPI_RESID>, grid, dim3(256), 0, s, p, g.part); break;
+      case EPI_GELU: hipLaunchKernelGGL(splitk_reduce<EPI_GELU>, grid, dim3(256), 0, s, p, g.part); break;
+      case EPI_DGELU: hipLaunchKernelGGL(splitk_reduce<EPI_DGELU>, grid, dim3(256), 0, s, p, g.part); break;
+      default: return set_error(ZB_E_UNSUPPORTED, "gemm: epilogue %d with split-K", g.epi);
+    }
+    ZB_HIP_CHECK(hipGetLastError());
+    return ZB_OK;
+  }
   if (ak && !bk) {  // F
     switch (g.epi) {
       case EPI_STORE: launch_tile<true, false, EPI_STORE>(t, p, s); break;

@@ -217,6 +217,7 @@ struct zb_stage {
   std::vector<LayerOff> off;
   size_t fw_bytes = 0, fb_bytes = 0, bw_bytes = 0, scratch_bytes = 0;
   size_t scratch_do = 0, scratch_flag = 0, scratch_dsum = 0;
+  size_t scratch_part = 0, part_bytes = 0;  // split-K arena of the F/B GEMMs
   // plan
   bool planned = false;
   int plan_fw = 0, plan_fb = 0, plan_bw = 0;
@@ -288,6 +289,17 @@ void compute_layout(zb_stage* S) {
   if (S->d.kind == ZB_KIND_FULL) sc += align_up(T * h * es);
   S->scratch_dsum = sc;
   if (S->d.kind == ZB_KIND_FULL) sc += align_up(a * T * 4);
+  // Split-K arena: the largest any F or B GEMM of the stage asks for (bf16 only).
+  size_t part = 0;
+  if (S->d.dtype == ZB_DTYPE_BF16) {
+    for (int i = 0; i < S->nlin; ++i) {
+      part = std::max(part, gemm_split_arena(S->T, (int)S->wN[i], (int)S->wK[i]));  // F
+      part = std::max(part, gemm_split_arena(S->T, (int)S->wK[i], (int)S->wN[i]));  // B
+    }
+  }
+  S->scratch_part = sc;
+  S->part_bytes = part;
+  sc += align_up(part);
   S->scratch_bytes = sc;
   S->fw.bytes = fw;
   S->fb.bytes = fb;
@@ -350,6 +362,14 @@ size_t ws_size(const zb_stage* S, int nfw, int nfb, int nbw) {
 
 // ------------------------------------------------------------- GEMM calls
 
+// The stage's split-K arena: its passes run in stream order, so its GEMMs
+// share one arena.
+void set_arena(zb_stage* S, GemmDesc& g) {
+  if (S->part_bytes == 0 || !S->scratch) return;
+  g.part = reinterpret_cast<float*>(S->scratch + S->scratch_part);
+  g.part_bytes = S->part_bytes;
+}
+
 zb_status gemm_f(zb_stage* S, const void* X, int64_t ldx, int lin, void* Y, int64_t ldy, int epi,
                  const void* R = nullptr, int64_t ldr = 0, void* Z = nullptr, int64_t ldz = 0) {
   GemmDesc g;
@@ -358,6 +378,7 @@ zb_status gemm_f(zb_stage* S, const void* X, int64_t ldx, int lin, void* Y, int6
   g.B = S->w[lin]; g.ldb = S->wN[lin]; g.b_kcontig = false;
   g.C = Y; g.ldc = ldy; g.R = R; g.ldr = ldr; g.Z = Z; g.ldz = ldz;
   g.epi = epi; g.dtype = S->d.dtype; g.gelu = S->d.gelu; g.tag = "f";
+  set_arena(S, g);
   return launch_gemm(g, S->stream);
 }
 
@@ -370,6 +391,7 @@ zb_status gemm_b(zb_stage* S, const void* dY, int64_t lddy, int lin, void* dX, i
   g.B = S->w[lin]; g.ldb = S->wN[lin]; g.b_kcontig = true;
   g.C = dX; g.ldc = lddx; g.R = R; g.ldr = ldr;
   g.epi = epi; g.dtype = S->d.dtype; g.gelu = S->d.gelu; g.tag = "b";
+  set_arena(S, g);
   return launch_gemm(g, S->stream);
 }
 

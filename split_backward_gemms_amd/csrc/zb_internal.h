@@ -41,7 +41,8 @@ enum Epilogue {
   EPI_RESID = 1,   // C = acc + R
   EPI_GELU = 2,    // Z = acc; C = gelu(acc)
   EPI_DGELU = 3,   // C = acc * gelu'(R)          (R = saved pre-activation)
-  EPI_ACC = 4      // C(fp32) = (beta ? C : 0) + acc, accumulated in the MFMA chain
+  EPI_ACC = 4,     // C(fp32) = (beta ? C : 0) + acc
+  EPI_PART = 5     // split-K partial: C(fp32) + split * M * ldc = acc (internal to the GEMM launcher)
 };
 
 // C[M,N] = sum_k A(m,k) B(k,n) with
@@ -66,9 +67,16 @@ struct GemmDesc {
   int dtype = ZB_DTYPE_BF16; // storage type of A, B, R, Z and (non-ACC) C
   int gelu = ZB_GELU_ERF;
   const char* tag = "gemm";  // pass name for kernel timing ("f", "b", "w")
+  // Split-K arena (optional, not for EPI_ACC): room for the fp32 partial sums
+  // of the splits.  GEMMs that share an arena must run in stream order.
+  float* part = nullptr;
+  size_t part_bytes = 0;
 };
 
 zb_status launch_gemm(const GemmDesc& g, hipStream_t s);
+// Arena bytes launch_gemm would use to split the K of an M x N x K product of
+// the F or B layout; 0 when it would not split.
+size_t gemm_split_arena(int M, int N, int K);
 // Independent weight-gradient GEMMs (bf16, W layout, fp32 accumulate) in as few launches as possible.
 zb_status launch_gemm_w_group(const GemmDesc* gs, int n, hipStream_t s);
 
