@@ -841,8 +841,8 @@ zb_status launch_gemm_w_group(const GemmDesc* gs, int n, hipStream_t s) {
       bytes += 2.0 * ((double)g.M * g.K + (double)g.K * g.N) + (g.beta ? 8.0 : 4.0) * g.M * g.N;
     }
     if (gp.n == 0) continue;
-    ProfScope ps("gemm_w_group_256x128", flops, bytes, s);
-    launch_w_group<256, 128>(gp, s);
+    ProfScope ps("gemm_w_group_256x256", flops, bytes, s);
+    launch_w_group<256, 256>(gp, s);
     ZB_HIP_CHECK(hipGetLastError());
   }
   return ZB_OK;
