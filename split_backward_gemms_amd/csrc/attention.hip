@@ -22,25 +22,44 @@
 // registers.  Forward and dQ keep one query row per lane column; dK/dV keep
 // one key row per lane column.
 //
+// Blocks of 64 sequence rows x 128 head dims go from global memory straight
+// into LDS (buffer loads with the LDS bit) through a two-stage ring, one
+// barrier per block.  In LDS a block is row-major, 256 bytes per row, with
+// the 16-byte chunk c of row r at position c ^ f(r), f(r) = 4 (r % 4) +
+// (r / 4) % 4: 16-byte reads of 16 consecutive rows (operands contracted over
+// the head dimension) and transposing 8-byte reads of 4 rows x 4 chunks
+// (ds_read_b64_tr_b16, operands contracted over positions) are both free of
+// bank conflicts, so no block is ever transposed in registers.
+//
 // Determinism: dQ and dK/dV are separate passes (query-block and key-block
 // parallel); no atomics, fixed summation order.
 #include <hip/hip_runtime.h>
 
+#include "device_common.h"
 #include "zb_internal.h"
 
 namespace zb {
 namespace {
+
+using dev::dma16;
+using dev::kOOB;
+using dev::lds_addr;
+using dev::make_rsrc4;
+using dev::pack_bf16x2;
+using dev::wait_vm_barrier;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int HD = 128;        // head dim
-constexpr int NT = 256;        // 4 waves
-constexpr uint32_t kOOB = 0x80000000u;
-constexpr int kRsrcWord3 = 0x00020000;
+constexpr int HD = 128;           // head dim
+constexpr int NT = 256;           // 4 waves
+constexpr int BLK = 64 * 256;     // one 64 x 128 bf16 block in LDS
+constexpr int NI_BLK = 4;         // copies per wave per block (16 KiB / 4 waves / 1 KiB)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnParams {
@@ -55,7 +74,7 @@ struct AttnParams {
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t extent) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)extent, kRsrcWord3);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)extent, (int)dev::kRsrcWord3);
 }
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
@@ -63,19 +82,12 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 __device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
 }
-
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
-__device__ __forceinline__ uint32_t pack2(float a, float b) { return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // 8 fp32 -> bf16x8 fragment
 __device__ __forceinline__ bf16x8 to_frag(const float* v) {
-  u32x4 u = {pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+  u32x4 u = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
   return __builtin_bit_cast(bf16x8, u);
 }
 
@@ -90,77 +102,99 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// ---- LDS tiles -------------------------------------------------------------
-// "Row" tile [R][128] bf16: 256 bytes per row, 16-byte chunk c at (c ^ (row % 8)).
-__device__ __forceinline__ uint32_t row_off(int row, int chunk) { return row * 256 + ((chunk ^ (row & 7)) << 4); }
-// "Transposed" tile [128][64] bf16 (rows = head dim, 64 sequence positions):
-// 128 bytes per row; chunk c (8 positions) at c ^ (row % 8), its two 8-byte
-// halves swapped when (row / 8) is odd.
-__device__ __forceinline__ uint32_t tr_off(int row, int chunk, int half) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4) + ((half ^ ((row >> 3) & 1)) << 3);
-}
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// X fragment, contracted over the head dim, from a row tile: row p, k = 16 kk + 8h .. +7.
-__device__ __forceinline__ bf16x8 frag_row(const char* base, int row, int kk, int h) {
-  return *reinterpret_cast<const bf16x8*>(base + row_off(row, 2 * kk + h));
-}
-// X fragment, contracted over positions, from a transposed tile: row p (head dim),
-// positions 16 s + {4h..4h+3, 8+4h..8+4h+3}.
-__device__ __forceinline__ bf16x8 frag_tr(const char* base, int row, int s, int h) {
-  const u32x2 a = *reinterpret_cast<const u32x2*>(base + tr_off(row, 2 * s, h));
-  const u32x2 b = *reinterpret_cast<const u32x2*>(base + tr_off(row, 2 * s + 1, h));
-  u32x4 u = {a[0], a[1], b[0], b[1]};
-  return __builtin_bit_cast(bf16x8, u);
-}
+// ---- LDS blocks ------------------------------------------------------------
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-// Cooperative loads of 64 sequence rows x 128 head dims (one head's block).
-// Rows at or past `valid` (end of the sequence) read as zero.
-// Row tile: 64 rows x 16 chunks = 1024 chunks, 4 per thread.
-__device__ __forceinline__ void load_row_tile(char* lds, __amdgpu_buffer_rsrc_t r, int64_t row0, int valid,
-                                              int64_t ld, int col0, int tid) {
+// Copies of one block: rows row0 .. row0+63 (those at or past `valid` read as
+// zero), columns col0 .. col0+127 of a row-major bf16 matrix with leading
+// dimension ld.  Wave w issues copies 4w .. 4w+3; copy q covers LDS bytes
+// 1024 q .. +1023, i.e. rows 4q .. 4q+3, with lane l at LDS chunk l of them.
+struct BlockDma {
+  dev::u32x4 rsrc;
+  uint32_t boff[NI_BLK];  // lane's byte offset at row0 = 0
+  uint32_t rowstep;       // bytes per row
+  int row0;               // the lane's row within the block for copy 0 (copy q adds 4 q)
+  uint32_t lds0;          // this wave's first KiB within the block
+
+  __device__ __forceinline__ BlockDma(const uint16_t* base, uint32_t extent, int64_t ld, int col0, int wave,
+                                      int lane) {
+    rsrc = make_rsrc4(base, extent);
+    rowstep = (uint32_t)(ld * 2);
+    lds0 = (uint32_t)(wave * NI_BLK * 1024);
+    row0 = wave * NI_BLK * 4 + (lane >> 4);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 4) + 16 * i, c = tid & 15;
-    const uint32_t off = row < valid ? (uint32_t)(((row0 + row) * ld + col0 + 8 * c) * 2) : kOOB;
-    *reinterpret_cast<u32x4*>(lds + row_off(row, c)) = bload16(r, off);
-  }
-}
-// Transposed tile: thread takes 4 rows x 8 head dims, writes 8 head-dim rows x 4 positions.
-__device__ __forceinline__ void load_tr_tile(char* lds, __amdgpu_buffer_rsrc_t r, int64_t row0, int valid, int64_t ld,
-                                             int col0, int tid) {
-  const int dc = tid & 15, kg = tid >> 4;  // head dims 8dc..8dc+7, positions 4kg..4kg+3
-  u32x4 v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 4 * kg + i;
-    const uint32_t off = row < valid ? (uint32_t)(((row0 + row) * ld + col0 + 8 * dc) * 2) : kOOB;
-    v[i] = bload16(r, off);
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t w = e >> 1;
-    uint32_t x0 = v[0][w], x1 = v[1][w], x2 = v[2][w], x3 = v[3][w];
-    if (e & 1) {
-      x0 >>= 16; x1 >>= 16; x2 >>= 16; x3 >>= 16;
+    for (int q = 0; q < NI_BLK; ++q) {
+      const int r = row0 + 4 * q;
+      const int c = (lane & 15) ^ swz(r);
+      boff[q] = (uint32_t)(((int64_t)r * ld + col0 + 8 * c) * 2);
     }
-    const u32x2 out = {(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
-    const int drow = 8 * dc + e;
-    *reinterpret_cast<u32x2*>(lds + tr_off(drow, kg >> 1, kg & 1)) = out;
   }
-}
+  __device__ __forceinline__ void load(uint32_t dst, int64_t first_row, int valid) const {
+    const uint32_t step = (uint32_t)(first_row * rowstep);
+#pragma unroll
+    for (int q = 0; q < NI_BLK; ++q)
+      dma16(rsrc, dst + lds0 + q * 1024, row0 + 4 * q < valid ? boff[q] + step : kOOB);
+  }
+};
+
+// Operand contracted over the head dim (16-byte reads): rows 32 b + lc of a
+// block, k = 16 kk + 8 h .. +7.  rb[kk] = lane's offset for kk (rows 32 b
+// differ by 8192 bytes and keep the swizzle).
+struct RowFrag {
+  uint32_t rb[8];
+  __device__ __forceinline__ RowFrag(int lane) {
+    const int lc = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) rb[kk] = lc * 256 + (((2 * kk + h) ^ swz(lc)) << 4);
+  }
+  __device__ __forceinline__ bf16x8 get(const char* blk, int b, int kk) const {
+    return *reinterpret_cast<const bf16x8*>(blk + rb[kk] + b * 32 * 256);
+  }
+};
+
+// Operand contracted over positions (transposing reads): X[p = head dim
+// 32 db + lc][k = positions 16 ks + {4h..4h+3, 8+4h..8+4h+3}] from a block
+// holding rows = positions.  Lane l = 16 g + i reads rows 16 ks + 4 (g / 2) +
+// i / 4 (+ 8) at columns 32 db + 16 (g % 2) + 4 (i % 4).  tb[half][db] is the
+// lane's offset for ks = 0.
+struct TrFrag {
+  uint32_t tb[2][4];
+  __device__ __forceinline__ TrFrag(int lane) {
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int r = 4 * (g >> 1) + (i >> 2) + 8 * half;
+        const int c = 4 * db + 2 * (g & 1) + ((i & 3) >> 1);
+        tb[half][db] = r * 256 + ((c ^ swz(r)) << 4) + 8 * (i & 1);
+      }
+  }
+  __device__ __forceinline__ bf16x8 get(const char* blk, int db, int ks) const {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(blk + tb[0][db] + ks * 16 * 256));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(blk + tb[1][db] + ks * 16 * 256));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
 
 // ============================================================== forward
-// Workgroup: 128 query rows (32 per wave) of one (sequence, head); keys in blocks of 64.
-__global__ void __launch_bounds__(NT) attn_fwd(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[64 * 256 + 128 * 128];
-  char* sK = lds;             // [64][128] row tile
-  char* sVt = lds + 64 * 256; // [128][64] transposed
+// Workgroup: 128 query rows (32 per wave) of one (sequence, head); keys in
+// blocks of 64 through a two-stage ring of (K, V) blocks.
+__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2))) attn_fwd(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) char sK0[BLK];
+  __shared__ __attribute__((aligned(1024))) char sV0[BLK];
+  __shared__ __attribute__((aligned(1024))) char sK1[BLK];
+  __shared__ __attribute__((aligned(1024))) char sV1[BLK];
   const int nqb = (p.seq + 127) / 128;
   const int qb = nqb - 1 - (int)blockIdx.x;  // heaviest blocks first
   const int hd = blockIdx.y % p.heads, sq = blockIdx.y / p.heads;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, lc = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, lc = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t ld3 = 3LL * p.h, base_row = (int64_t)sq * p.seq;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv, (uint32_t)((int64_t)p.T * ld3 * 2));
+  const uint32_t ext3 = (uint32_t)((int64_t)p.T * ld3 * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv, ext3);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o, (uint32_t)((int64_t)p.T * p.h * 2));
   const float c = p.scale * kLog2e;
 
@@ -172,68 +206,94 @@ __global__ void __launch_bounds__(NT) attn_fwd(AttnParams p) {
     const uint32_t off = qv ? (uint32_t)(((base_row + q) * ld3 + hd * HD + 16 * kk + 8 * h) * 2) : kOOB;
     qf[kk] = __builtin_bit_cast(bf16x8, bload16(rq, off));
   }
+  const BlockDma dk(p.qkv, ext3, ld3, p.h + hd * HD, w, lane);
+  const BlockDma dv(p.qkv, ext3, ld3, 2 * p.h + hd * HD, w, lane);
+  const RowFrag rf(lane);
+  const TrFrag tf(lane);
+
   f32x16 o[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) o[d] = zero16();
   float m = -INFINITY, l = 0.0f;
-  const int q_wave_max = qb * 128 + 32 * w + 31;
-  const int nkb = min((qb * 128 + 127) / 64, (p.seq - 1) / 64) + 1;
+  const int q_wave_min = qb * 128 + 32 * w, q_wave_max = q_wave_min + 31;
+  const int nkb = min(qb * 128 + 127, p.seq - 1) / 64 + 1;
 
-  for (int kb = 0; kb < nkb; ++kb) {
+  auto fetch = [&](char* sk, char* sv, int kb) {
     const int k0 = kb * 64;
-    __syncthreads();
-    load_row_tile(sK, rq, base_row + k0, p.seq - k0, ld3, p.h + hd * HD, tid);
-    load_tr_tile(sVt, rq, base_row + k0, p.seq - k0, ld3, 2 * p.h + hd * HD, tid);
-    __syncthreads();
-    if (k0 > q_wave_max) continue;
-    f32x16 s[2];
+    dk.load(__builtin_amdgcn_readfirstlane(lds_addr(sk)), base_row + k0, p.seq - k0);
+    dv.load(__builtin_amdgcn_readfirstlane(lds_addr(sv)), base_row + k0, p.seq - k0);
+  };
+  fetch(sK0, sV0, 0);
+  if (nkb > 1) fetch(sK1, sV1, 1);
+  if (nkb > 1) wait_vm_barrier<2 * NI_BLK>();
+  else wait_vm_barrier<0>();
+
+  // Block kb from (sk, sv); at the end every wave has its copies of block
+  // kb+1 and is done with block kb, whose stage then takes block kb+2.
+  auto body = [&](char* sk, char* sv, int kb) {
+    const int k0 = kb * 64;
+    if (k0 <= q_wave_max) {
+      f32x16 s[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      s[b] = zero16();
+      for (int b = 0; b < 2; ++b) {
+        s[b] = zero16();
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) s[b] = mfma(frag_row(sK, 32 * b + lc, kk, h), qf[kk], s[b]);
-    }
-    // scale, causal mask, running max
-    float mb = -INFINITY;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kv = k0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-        const float v = (kv <= q && kv < p.seq) ? s[b][r] * c : -INFINITY;
-        s[b][r] = v;
-        mb = fmaxf(mb, v);
+        for (int kk = 0; kk < 8; ++kk) s[b] = mfma(rf.get(sk, b, kk), qf[kk], s[b]);
       }
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float mn = fmaxf(m, mb);
-    const float alpha = exp2f(m - mn);
-    m = mn;
-    l *= alpha;
+      if (k0 + 63 > q_wave_min || k0 + 64 > p.seq) {  // diagonal or last block: mask
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = exp2f(s[b][r] - mn);
-        s[b][r] = e;
-        l += e;
+          for (int r = 0; r < 16; ++r) {
+            const int kv = k0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (kv > q || kv >= p.seq) s[b][r] = -INFINITY;
+          }
       }
-    // O^T[d][q] += sum_kv V[kv][d] P[q][kv]
+      float mb = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+        for (int r = 0; r < 16; ++r) mb = fmaxf(mb, s[b][r]);
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      const float mn = fmaxf(m, mb * c);  // block 0 always has key 0 <= q, so mn is finite
+      const float alpha = exp2_hw(m - mn);
+      m = mn;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+        l *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = exp2_hw(fmaf(s[b][r], c, -mn));
+          s[b][r] = e;
+          l += e;
+        }
+      // O^T[d][q] += sum_kv V^T[d][kv] P^T[kv][q]
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
         float pv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = s[b][8 * st + e];
+        for (int e = 0; e < 8; ++e) pv[e] = s[ks >> 1][8 * (ks & 1) + e];
         const bf16x8 pf = to_frag(pv);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) o[d] = mfma(frag_tr(sVt, 32 * d + lc, 2 * b + st, h), pf, o[d]);
+        for (int d = 0; d < 4; ++d) o[d] = mfma(tf.get(sv, d, ks), pf, o[d]);
       }
+    }
+    wait_vm_barrier<0>();
+    if (kb + 2 < nkb) fetch(sk, sv, kb + 2);
+  };
+  int kb = 0;
+  for (; kb + 1 < nkb; kb += 2) {
+    body(sK0, sV0, kb);
+    body(sK1, sV1, kb + 1);
   }
+  if (kb < nkb) body(sK0, sV0, kb);
+
   l += __shfl_xor(l, 32);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
@@ -242,27 +302,31 @@ __global__ void __launch_bounds__(NT) attn_fwd(AttnParams p) {
     for (int g = 0; g < 4; ++g) {
       const int dd = 32 * d + 8 * g + 4 * h;
       const uint32_t off = qv ? (uint32_t)(((base_row + q) * p.h + hd * HD + dd) * 2) : kOOB;
-      const u32x2 v = {pack2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv), pack2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv)};
+      const u32x2 v = {pack_bf16x2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv),
+                       pack_bf16x2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv)};
       bstore8(ro, off, v);
     }
   if (qv && h == 0) p.lse2[(int64_t)hd * p.T + base_row + q] = m + log2f(l);
 }
 
 // ================================================================ dQ (+ D)
-__global__ void __launch_bounds__(NT) attn_bwd_dq(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[64 * 256 * 2 + 128 * 128];
-  char* sK = lds;                  // [64][128]
-  char* sV = lds + 64 * 256;       // [64][128]
-  char* sKt = lds + 2 * 64 * 256;  // [128][64]
+// Workgroup: 128 query rows of one (sequence, head); (K, V) blocks of 64 keys.
+__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2))) attn_bwd_dq(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) char sK0[BLK];
+  __shared__ __attribute__((aligned(1024))) char sV0[BLK];
+  __shared__ __attribute__((aligned(1024))) char sK1[BLK];
+  __shared__ __attribute__((aligned(1024))) char sV1[BLK];
   const int nqb = (p.seq + 127) / 128;
   const int qb = nqb - 1 - (int)blockIdx.x;
   const int hd = blockIdx.y % p.heads, sq = blockIdx.y / p.heads;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, lc = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, lc = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t ld3 = 3LL * p.h, base_row = (int64_t)sq * p.seq;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv, (uint32_t)((int64_t)p.T * ld3 * 2));
+  const uint32_t ext3 = (uint32_t)((int64_t)p.T * ld3 * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv, ext3);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o, (uint32_t)((int64_t)p.T * p.h * 2));
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout, (uint32_t)((int64_t)p.T * p.h * 2));
-  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(p.dqkv, (uint32_t)((int64_t)p.T * ld3 * 2));
+  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(p.dqkv, ext3);
   const float c = p.scale * kLog2e;
 
   const int q = qb * 128 + 32 * w + lc;
@@ -284,53 +348,68 @@ __global__ void __launch_bounds__(NT) attn_bwd_dq(AttnParams p) {
   dsum += __shfl_xor(dsum, 32);
   const float lse = qv ? p.lse2[(int64_t)hd * p.T + base_row + q] : 0.0f;
   if (qv && h == 0) p.dsum[(int64_t)hd * p.T + base_row + q] = dsum;
+  const BlockDma dk(p.qkv, ext3, ld3, p.h + hd * HD, w, lane);
+  const BlockDma dv(p.qkv, ext3, ld3, 2 * p.h + hd * HD, w, lane);
+  const RowFrag rf(lane);
+  const TrFrag tf(lane);
 
   f32x16 dq[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) dq[d] = zero16();
-  const int q_wave_max = qb * 128 + 32 * w + 31;
-  const int nkb = min((qb * 128 + 127) / 64, (p.seq - 1) / 64) + 1;
-  for (int kb = 0; kb < nkb; ++kb) {
+  const int q_wave_min = qb * 128 + 32 * w, q_wave_max = q_wave_min + 31;
+  const int nkb = min(qb * 128 + 127, p.seq - 1) / 64 + 1;
+
+  auto fetch = [&](char* sk, char* sv, int kb) {
     const int k0 = kb * 64;
-    __syncthreads();
-    load_row_tile(sK, rq, base_row + k0, p.seq - k0, ld3, p.h + hd * HD, tid);
-    load_row_tile(sV, rq, base_row + k0, p.seq - k0, ld3, 2 * p.h + hd * HD, tid);
-    load_tr_tile(sKt, rq, base_row + k0, p.seq - k0, ld3, p.h + hd * HD, tid);
-    __syncthreads();
-    if (k0 > q_wave_max) continue;
-    f32x16 s[2], dp[2];
+    dk.load(__builtin_amdgcn_readfirstlane(lds_addr(sk)), base_row + k0, p.seq - k0);
+    dv.load(__builtin_amdgcn_readfirstlane(lds_addr(sv)), base_row + k0, p.seq - k0);
+  };
+  fetch(sK0, sV0, 0);
+  if (nkb > 1) fetch(sK1, sV1, 1);
+  if (nkb > 1) wait_vm_barrier<2 * NI_BLK>();
+  else wait_vm_barrier<0>();
+
+  auto body = [&](char* sk, char* sv, int kb) {
+    const int k0 = kb * 64;
+    if (k0 <= q_wave_max) {
+      const bool masked = k0 + 63 > q_wave_min || k0 + 64 > p.seq;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      s[b] = zero16();
-      dp[b] = zero16();
+      for (int b = 0; b < 2; ++b) {  // two 32-key halves, one at a time
+        f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        s[b] = mfma(frag_row(sK, 32 * b + lc, kk, h), qf[kk], s[b]);
-        dp[b] = mfma(frag_row(sV, 32 * b + lc, kk, h), dof[kk], dp[b]);
+        for (int kk = 0; kk < 8; ++kk) {
+          s = mfma(rf.get(sk, b, kk), qf[kk], s);     // S^T[kv][q]
+          dp = mfma(rf.get(sv, b, kk), dof[kk], dp);  // dP^T[kv][q]
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kv = k0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
+          float pr = exp2_hw(fmaf(s[r], c, -lse));
+          if (masked && (kv > q || kv >= p.seq)) pr = 0.0f;
+          s[r] = pr * (dp[r] - dsum);  // dS^T
+        }
+        // dQ^T[d][q] += sum_kv K^T[d][kv] dS^T[kv][q]
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = s[8 * st + e];
+          const bf16x8 f = to_frag(v);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) dq[d] = mfma(tf.get(sk, d, 2 * b + st), f, dq[d]);
+        }
       }
     }
-    // dS^T = P^T * (dP^T - D)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kv = k0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-        const float pr = (kv <= q && kv < p.seq) ? exp2f(s[b][r] * c - lse) : 0.0f;
-        s[b][r] = pr * (dp[b][r] - dsum);
-      }
-    // dQ^T[d][q] += sum_kv K[kv][d] dS[q][kv]
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = s[b][8 * st + e];
-        const bf16x8 f = to_frag(v);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) dq[d] = mfma(frag_tr(sKt, 32 * d + lc, 2 * b + st, h), f, dq[d]);
-      }
+    wait_vm_barrier<0>();
+    if (kb + 2 < nkb) fetch(sk, sv, kb + 2);
+  };
+  int kb = 0;
+  for (; kb + 1 < nkb; kb += 2) {
+    body(sK0, sV0, kb);
+    body(sK1, sV1, kb + 1);
   }
+  if (kb < nkb) body(sK0, sV0, kb);
+
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -338,31 +417,34 @@ __global__ void __launch_bounds__(NT) attn_bwd_dq(AttnParams p) {
       const int dd = 32 * d + 8 * g + 4 * h;
       const uint32_t off = qv ? (uint32_t)(((base_row + q) * ld3 + hd * HD + dd) * 2) : kOOB;
       const float sc = p.scale;
-      const u32x2 v = {pack2(dq[d][4 * g] * sc, dq[d][4 * g + 1] * sc), pack2(dq[d][4 * g + 2] * sc, dq[d][4 * g + 3] * sc)};
+      const u32x2 v = {pack_bf16x2(dq[d][4 * g] * sc, dq[d][4 * g + 1] * sc),
+                       pack_bf16x2(dq[d][4 * g + 2] * sc, dq[d][4 * g + 3] * sc)};
       bstore8(rdq, off, v);
     }
 }
 
 // =============================================================== dK, dV
-// Workgroup: 128 key rows (32 per wave) of one (sequence, head); queries in blocks of 64.
-__global__ void __launch_bounds__(NT) attn_bwd_dkdv(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * 64 * 256 + 2 * 128 * 128 + 2 * 64 * 4];
-  char* sQ = lds;                          // [64][128]
-  char* sG = lds + 64 * 256;               // dO [64][128]
-  char* sQt = lds + 2 * 64 * 256;          // [128][64]
-  char* sGt = sQt + 128 * 128;             // dO^T [128][64]
-  float* sL = reinterpret_cast<float*>(sGt + 128 * 128);  // LSE2 [64]
-  float* sD = sL + 64;                                    // D [64]
-  const int nkb = (p.seq + 127) / 128;
-  const int kb = (int)blockIdx.x;  // lightest first is fine: heavy blocks are the early keys
+// Workgroup: 128 key rows (32 per wave) of one (sequence, head); (Q, dO)
+// blocks of 64 queries, from the first query that can see the keys to the end.
+// LSE2 and D of a block ride along: lanes 0-15 of one extra copy fetch 64
+// LSE2 values, lanes 16-31 the 64 D values (the rest read as zero).
+__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) attn_bwd_dkdv(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) char sQ0[BLK];
+  __shared__ __attribute__((aligned(1024))) char sG0[BLK];
+  __shared__ __attribute__((aligned(1024))) char sQ1[BLK];
+  __shared__ __attribute__((aligned(1024))) char sG1[BLK];
+  __shared__ __attribute__((aligned(1024))) char sLD0[1024];
+  __shared__ __attribute__((aligned(1024))) char sLD1[1024];
+  const int kb = (int)blockIdx.x;  // the first key blocks see the most queries: they go first
   const int hd = blockIdx.y % p.heads, sq = blockIdx.y / p.heads;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, lc = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, lc = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t ld3 = 3LL * p.h, base_row = (int64_t)sq * p.seq;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv, (uint32_t)((int64_t)p.T * ld3 * 2));
-  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout, (uint32_t)((int64_t)p.T * p.h * 2));
-  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(p.dqkv, (uint32_t)((int64_t)p.T * ld3 * 2));
+  const uint32_t ext3 = (uint32_t)((int64_t)p.T * ld3 * 2);
+  const uint32_t exth = (uint32_t)((int64_t)p.T * p.h * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv, ext3);
+  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(p.dqkv, ext3);
   const float c = p.scale * kLog2e;
-  (void)nkb;
 
   const int kv = kb * 128 + 32 * w + lc;  // this lane's key row
   const bool kvv = kv < p.seq;
@@ -375,64 +457,96 @@ __global__ void __launch_bounds__(NT) attn_bwd_dkdv(AttnParams p) {
     kf[kk] = __builtin_bit_cast(bf16x8, bload16(rq, offk));
     vf[kk] = __builtin_bit_cast(bf16x8, bload16(rq, offv));
   }
+  const BlockDma dmq(p.qkv, ext3, ld3, hd * HD, w, lane);
+  const BlockDma dmg(p.dout, exth, p.h, hd * HD, w, lane);
+  // LSE2 / D copy: the [heads, T] fp32 rows of this head, 16 bytes per lane.
+  const dev::u32x4 rl = make_rsrc4(p.lse2 + (int64_t)hd * p.T + base_row, (uint32_t)(p.seq * 4));
+  const dev::u32x4 rd = make_rsrc4(p.dsum + (int64_t)hd * p.T + base_row, (uint32_t)(p.seq * 4));
+  const RowFrag rf(lane);
+  const TrFrag tf(lane);
+
   f32x16 dk[4], dv[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     dk[d] = zero16();
     dv[d] = zero16();
   }
-  const int kv_wave_min = kb * 128 + 32 * w;
-  for (int q0 = kb * 128; q0 < p.seq; q0 += 64) {
-    __syncthreads();
-    load_row_tile(sQ, rq, base_row + q0, p.seq - q0, ld3, hd * HD, tid);
-    load_row_tile(sG, rdo, base_row + q0, p.seq - q0, p.h, hd * HD, tid);
-    load_tr_tile(sQt, rq, base_row + q0, p.seq - q0, ld3, hd * HD, tid);
-    load_tr_tile(sGt, rdo, base_row + q0, p.seq - q0, p.h, hd * HD, tid);
-    if (tid < 64) {
-      const bool ok = q0 + tid < p.seq;
-      sL[tid] = ok ? p.lse2[(int64_t)hd * p.T + base_row + q0 + tid] : 0.0f;
-      sD[tid] = ok ? p.dsum[(int64_t)hd * p.T + base_row + q0 + tid] : 0.0f;
+  const int kv_wave_min = kb * 128 + 32 * w, kv_wave_max = kv_wave_min + 31;
+  const int qb0 = kb * 2;                // first 64-query block that can see these keys
+  const int nqb = (p.seq + 63) / 64 - qb0;
+
+  auto fetch = [&](char* sq_, char* sg, char* sld, int j) {
+    const int q0 = (qb0 + j) * 64;
+    dmq.load(__builtin_amdgcn_readfirstlane(lds_addr(sq_)), base_row + q0, p.seq - q0);
+    dmg.load(__builtin_amdgcn_readfirstlane(lds_addr(sg)), base_row + q0, p.seq - q0);
+    if (w == 0) {
+      const bool is_l = lane < 16;
+      const int e = 4 * (lane & 15);
+      const uint32_t off = lane < 32 && q0 + e < p.seq ? (uint32_t)((q0 + e) * 4) : kOOB;
+      if (is_l) dma16(rl, __builtin_amdgcn_readfirstlane(lds_addr(sld)), off);
+      else dma16(rd, __builtin_amdgcn_readfirstlane(lds_addr(sld)), off);
     }
-    __syncthreads();
-    if (q0 + 63 < kv_wave_min) continue;  // every query of the block precedes this wave's keys
-    for (int b = 0; b < 2; ++b) {  // two 32-query halves, one at a time
-      f32x16 s = zero16(), dp = zero16();
+  };
+  (void)kv_wave_max;
+  fetch(sQ0, sG0, sLD0, 0);
+  if (nqb > 1) fetch(sQ1, sG1, sLD1, 1);
+  wait_vm_barrier<0>();
+
+  auto body = [&](char* sq_, char* sg, const char* sld, int j) {
+    const int q0 = (qb0 + j) * 64;
+    if (q0 + 63 >= kv_wave_min) {  // some query of the block sees some key of the wave
+      const float* sL = reinterpret_cast<const float*>(sld);
+      const float* sD = reinterpret_cast<const float*>(sld + 256);
+      const bool masked = q0 < kv_wave_max || q0 + 64 > p.seq;
+      for (int b = 0; b < 2; ++b) {  // two 32-query halves, one at a time
+        f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        s = mfma(frag_row(sQ, 32 * b + lc, kk, h), kf[kk], s);   // S[q][kv]
-        dp = mfma(frag_row(sG, 32 * b + lc, kk, h), vf[kk], dp); // dP[q][kv]
-      }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ql = 32 * b + 8 * g + 4 * h;  // local query row of register 4g
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(sL + ql);
-        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(sD + ql);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int qq = q0 + ql + t;
-          const int r = 4 * g + t;
-          const float pr = (kv <= qq && qq < p.seq) ? exp2f(s[r] * c - lv[t]) : 0.0f;
-          s[r] = pr;                       // P
-          dp[r] = pr * (dp[r] - dv4[t]);   // dS
+        for (int kk = 0; kk < 8; ++kk) {
+          s = mfma(rf.get(sq_, b, kk), kf[kk], s);   // S[q][kv]
+          dp = mfma(rf.get(sg, b, kk), vf[kk], dp);  // dP[q][kv]
         }
-      }
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        float pv[8], sv[8];
+        for (int g = 0; g < 4; ++g) {
+          const int ql = 32 * b + 8 * g + 4 * h;  // local query row of register 4g
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(sL + ql);
+          const f32x4 dv4 = *reinterpret_cast<const f32x4*>(sD + ql);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pv[e] = s[8 * st + e];
-          sv[e] = dp[8 * st + e];
+          for (int t = 0; t < 4; ++t) {
+            const int qq = q0 + ql + t;
+            const int r = 4 * g + t;
+            float pr = exp2_hw(fmaf(s[r], c, -lv[t]));
+            if (masked && (kv > qq || qq >= p.seq)) pr = 0.0f;
+            s[r] = pr;                      // P
+            dp[r] = pr * (dp[r] - dv4[t]);  // dS
+          }
         }
-        const bf16x8 pf = to_frag(pv), sf = to_frag(sv);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          dv[d] = mfma(frag_tr(sGt, 32 * d + lc, 2 * b + st, h), pf, dv[d]);  // dV^T[d][kv]
-          dk[d] = mfma(frag_tr(sQt, 32 * d + lc, 2 * b + st, h), sf, dk[d]);  // dK^T[d][kv]
+        for (int st = 0; st < 2; ++st) {
+          float pv[8], sv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pv[e] = s[8 * st + e];
+            sv[e] = dp[8 * st + e];
+          }
+          const bf16x8 pf = to_frag(pv), sf = to_frag(sv);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            dv[d] = mfma(tf.get(sg, d, 2 * b + st), pf, dv[d]);   // dV^T[d][kv]
+            dk[d] = mfma(tf.get(sq_, d, 2 * b + st), sf, dk[d]);  // dK^T[d][kv]
+          }
         }
       }
     }
+    wait_vm_barrier<0>();
+    if (j + 2 < nqb) fetch(sq_, sg, const_cast<char*>(sld), j + 2);
+  };
+  int j = 0;
+  for (; j + 1 < nqb; j += 2) {
+    body(sQ0, sG0, sLD0, j);
+    body(sQ1, sG1, sLD1, j + 1);
   }
+  if (j < nqb) body(sQ0, sG0, sLD0, j);
+
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -442,8 +556,9 @@ __global__ void __launch_bounds__(NT) attn_bwd_dkdv(AttnParams p) {
       const uint32_t offk = kvv ? (uint32_t)((row * ld3 + p.h + dd) * 2) : kOOB;
       const uint32_t offv = kvv ? (uint32_t)((row * ld3 + 2 * p.h + dd) * 2) : kOOB;
       const float sc = p.scale;
-      const u32x2 kv2 = {pack2(dk[d][4 * g] * sc, dk[d][4 * g + 1] * sc), pack2(dk[d][4 * g + 2] * sc, dk[d][4 * g + 3] * sc)};
-      const u32x2 vv2 = {pack2(dv[d][4 * g], dv[d][4 * g + 1]), pack2(dv[d][4 * g + 2], dv[d][4 * g + 3])};
+      const u32x2 kv2 = {pack_bf16x2(dk[d][4 * g] * sc, dk[d][4 * g + 1] * sc),
+                         pack_bf16x2(dk[d][4 * g + 2] * sc, dk[d][4 * g + 3] * sc)};
+      const u32x2 vv2 = {pack_bf16x2(dv[d][4 * g], dv[d][4 * g + 1]), pack_bf16x2(dv[d][4 * g + 2], dv[d][4 * g + 3])};
       bstore8(rdq, offk, kv2);
       bstore8(rdq, offv, vv2);
     }
@@ -459,6 +574,7 @@ zb_status launch_attention_fwd(const AttnArgs& a, hipStream_t s) {
   p.T = a.seq * a.nseq; p.h = a.heads * HD; p.heads = a.heads; p.seq = a.seq; p.nseq = a.nseq;
   p.scale = 0.08838834764831845f;
   if (3.0 * p.T * p.h * 2 >= 2147483648.0) return set_error(ZB_E_UNSUPPORTED, "attention: QKV spans 2 GiB or more");
+  if (a.seq <= 0 || a.heads <= 0 || a.nseq <= 0) return ZB_OK;
   const dim3 grid((a.seq + 127) / 128, a.heads * a.nseq);
   const double flops = 2.0 * a.nseq * (double)a.seq * a.seq * p.h;  // causal half of 4 s^2 h
   ProfScope ps("attn_fwd", flops, 2.0 * p.T * 4.0 * p.h, s);
@@ -478,6 +594,7 @@ zb_status launch_attention_bwd(const AttnArgs& a, hipStream_t s) {
   p.T = a.seq * a.nseq; p.h = a.heads * HD; p.heads = a.heads; p.seq = a.seq; p.nseq = a.nseq;
   p.scale = 0.08838834764831845f;
   if (3.0 * p.T * p.h * 2 >= 2147483648.0) return set_error(ZB_E_UNSUPPORTED, "attention: QKV spans 2 GiB or more");
+  if (a.seq <= 0 || a.heads <= 0 || a.nseq <= 0) return ZB_OK;
   const dim3 grid((a.seq + 127) / 128, a.heads * a.nseq);
   // Algorithmic backward = causal half of 8 s^2 h = four s x s x d products; the
   // two passes execute seven (three in dQ, four in dK/dV) and share them out 3:4.

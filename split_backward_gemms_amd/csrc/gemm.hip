@@ -311,47 +311,50 @@ struct GroupParams {
   int n;
 };
 
-// LDS ring depth per tile shape: as many 64-deep stages as fit in 160 KiB
-// (a 256x256 stage is 64 KiB, 256x128 48 KiB, 128x128 32 KiB).
-template <int BM, int BN>
+// LDS ring depth per tile shape: as many 64-deep stages (up to 4) as fit in a
+// CU's 160 KiB shared by OCC workgroups (a 256x256 stage is 64 KiB, 256x128
+// 48 KiB, 128x128 32 KiB).
+template <int BM, int BN, int OCC = 1>
 struct Ring {
   static constexpr int STAGE = (BM + BN) * BKT * 2;
-  static constexpr int NS = BM * BN >= 256 * 256 ? 2 : (BM * BN >= 256 * 128 ? 3 : 4);
+  static constexpr int FIT = (160 * 1024 / OCC) / STAGE;  // OCC workgroups share a CU's 160 KiB
+  static constexpr int NS = FIT < 4 ? FIT : 4;
+  static_assert(NS >= 2, "the ring needs two stages");
   static constexpr int S2 = NS > 2 ? STAGE : 16;
   static constexpr int S3 = NS > 3 ? STAGE : 16;
 };
 
-template <int BM, int BN, bool AK, bool BKC, int EPI>
+template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC = 1>
 __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, char* s0, char* s1, char* s2,
                                           char* s3);
 
-// The ring stages are separate LDS objects so that the compiler tracks the
-// buffer-to-LDS copies into each one separately when it places its waits.
-#define ZB_GEMM_LDS(BM, BN)                                                  \
-  __shared__ __attribute__((aligned(1024))) char s0[Ring<BM, BN>::STAGE];  \
-  __shared__ __attribute__((aligned(1024))) char s1[Ring<BM, BN>::STAGE];  \
-  __shared__ __attribute__((aligned(1024))) char s2[Ring<BM, BN>::S2];     \
-  __shared__ __attribute__((aligned(1024))) char s3[Ring<BM, BN>::S3]
+// The ring stages are separate LDS objects (so the code that addresses each
+// one is fixed at compile time).
+#define ZB_GEMM_LDS(BM, BN, OCC)                                                  \
+  __shared__ __attribute__((aligned(1024))) char s0[Ring<BM, BN, OCC>::STAGE];  \
+  __shared__ __attribute__((aligned(1024))) char s1[Ring<BM, BN, OCC>::STAGE];  \
+  __shared__ __attribute__((aligned(1024))) char s2[Ring<BM, BN, OCC>::S2];     \
+  __shared__ __attribute__((aligned(1024))) char s3[Ring<BM, BN, OCC>::S3]
 
 template <int BM, int BN, bool AK, bool BKC, int EPI>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_mfma(Params p) {
-  ZB_GEMM_LDS(BM, BN);
+  ZB_GEMM_LDS(BM, BN, 1);
   int b = blockIdx.x;
   if (p.xcd_remap) b = xcd_remap(b, p.nbm * p.nbn * p.splits);  // a tile's splits share an XCD
   gemm_tile<BM, BN, AK, BKC, EPI>(p, b / p.splits, b % p.splits, s0, s1, s2, s3);
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(OCC, OCC)))
 gemm_bf16_mfma_group(GroupParams gp) {
-  ZB_GEMM_LDS(BM, BN);
+  ZB_GEMM_LDS(BM, BN, OCC);
   int b = blockIdx.x;
   const int total = gp.tile_start[gp.n];
   if (total % XCDS == 0) b = (b % XCDS) * (total / XCDS) + b / XCDS;  // one XCD works a GEMM's neighbours
   int g = 0;
   while (g + 1 < gp.n && b >= gp.tile_start[g + 1]) ++g;
-  gemm_tile<BM, BN, AK, BKC, EPI>(gp.p[g], b - gp.tile_start[g], 0, s0, s1, s2, s3);
+  gemm_tile<BM, BN, AK, BKC, EPI, OCC>(gp.p[g], b - gp.tile_start[g], 0, s0, s1, s2, s3);
 }
 
 // 32x16 bf16 MFMA operand (lane l: row l % 32, k = 8 (l / 32) .. +7) read
@@ -368,12 +371,12 @@ __device__ __forceinline__ bf16x8 frag_t(const char* tile, uint32_t off) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI>
+template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC>
 __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, char* s0, char* s1, char* s2,
                                           char* s3) {
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int NS = Ring<BM, BN>::NS;
+  constexpr int NS = Ring<BM, BN, OCC>::NS;
   char* const bufs[4] = {s0, s1, s2, s3};
 
   int tm, tn;
@@ -791,7 +794,7 @@ void launch_mfma(Params p, hipStream_t s) {
   hipLaunchKernelGGL((gemm_bf16_mfma<BM, BN, AK, BKC, EPI>), dim3(p.nbm * p.nbn * p.splits), dim3(NT), 0, s, p);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int OCC = 1>
 void launch_w_group(GroupParams gp, hipStream_t s) {
   int total = 0;
   for (int g = 0; g < gp.n; ++g) {
@@ -804,7 +807,7 @@ void launch_w_group(GroupParams gp, hipStream_t s) {
     total += gp.p[g].nbm * gp.p[g].nbn;
   }
   gp.tile_start[gp.n] = total;
-  hipLaunchKernelGGL((gemm_bf16_mfma_group<BM, BN, false, false, EPI_ACC>), dim3(total), dim3(NT), 0, s, gp);
+  hipLaunchKernelGGL((gemm_bf16_mfma_group<BM, BN, false, false, EPI_ACC, OCC>), dim3(total), dim3(NT), 0, s, gp);
 }
 
 template <bool AK, bool BKC, int EPI>
