@@ -435,7 +435,6 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
   __shared__ __attribute__((aligned(1024))) char sG1[BLK];
   __shared__ __attribute__((aligned(1024))) char sLD0[1024];
   __shared__ __attribute__((aligned(1024))) char sLD1[1024];
-  const int kb = (int)blockIdx.x;  // the first key blocks see the most queries: they go first
   const int hd = blockIdx.y % p.heads, sq = blockIdx.y / p.heads;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, lc = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -445,6 +444,12 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv, ext3);
   const __amdgpu_buffer_rsrc_t rdq = make_rsrc(p.dqkv, ext3);
   const float c = p.scale * kLog2e;
+  // Key blocks x and nkb-1-x share a workgroup: together they see a fixed
+  // number of query blocks, so every workgroup has the same work.
+  const int nkb = (p.seq + 127) / 128;
+  for (int pass = 0; pass < 2; ++pass) {
+  const int kb = pass == 0 ? (int)blockIdx.x : nkb - 1 - (int)blockIdx.x;
+  if (pass == 1 && kb <= (int)blockIdx.x) break;
 
   const int kv = kb * 128 + 32 * w + lc;  // this lane's key row
   const bool kvv = kv < p.seq;
@@ -498,7 +503,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
       const float* sL = reinterpret_cast<const float*>(sld);
       const float* sD = reinterpret_cast<const float*>(sld + 256);
       const bool masked = q0 < kv_wave_max || q0 + 64 > p.seq;
-      for (int b = 0; b < 2; ++b) {  // two 32-query halves, one at a time
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {  // two 32-query halves
         f32x16 s = zero16(), dp = zero16();
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
@@ -562,6 +568,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
       bstore8(rdq, offk, kv2);
       bstore8(rdq, offv, vv2);
     }
+  }  // pass
 }
 
 }  // namespace
@@ -606,7 +613,8 @@ zb_status launch_attention_bwd(const AttnArgs& a, hipStream_t s) {
   }
   {
     ProfScope ps("attn_bwd_dkdv", alg * 4.0 / 7.0, 2.0 * p.T * 6.0 * p.h, s);
-    hipLaunchKernelGGL(attn_bwd_dkdv, grid, dim3(NT), 0, s, p);
+    const dim3 grid2((a.seq + 255) / 256, a.heads * a.nseq);  // pairs of 128-key blocks
+    hipLaunchKernelGGL(attn_bwd_dkdv, grid2, dim3(NT), 0, s, p);
     ZB_HIP_CHECK(hipGetLastError());
   }
   return ZB_OK;
