@@ -153,26 +153,31 @@ def main() -> int:
     if a.mode == "full":
         # Headline: one HIP stream per emulated stage, so independent stages overlap
         # the way pipeline stages on separate devices would.
-        pipe = EmulatedPipeline(w, ws, ops=None, device=dev, stage_streams=True)
+        pipe = EmulatedPipeline(w, ws, ops=ops, device=dev, stage_streams=True)
         y, dx = pipe.io_buffers()
         torch.cuda.synchronize()
-        log(f"device ready: workspace {pipe.workspace_bytes() / 2**30:.2f} GiB")
+        log(f"device ready: workspace {pipe.workspace_bytes() / 2**30:.2f} GiB, "
+            f"{'A rebuilt for W' if pipe.recompute_act else 'A stashed'}")
         ms_per_step = timed(pipe, ops, X, DY, y, dx, a.steps, a.warmup)
         tflops = flops / (ms_per_step / 1000.0) / 1e12
         log(f"{order}, stage streams: {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s")
     if a.mode == "full" and not a.no_fused:
+        pipe.plan(ops_fused)  # workspaces sized for the fused order
         fms = timed(pipe, ops_fused, X, DY, y, dx, a.steps, a.warmup)
         fused["ms_per_step_1f1b_unsplit_stage_streams"] = fms
         fused["zb_vs_1f1b_speedup_stage_streams"] = fms / ms_per_step - 1.0
         log(f"1f1b unsplit, stage streams: {fms:.3f} ms/step")
+    recompute_act = None
     if a.mode == "full":
+        recompute_act = pipe.recompute_act
         pipe.close()
         del pipe
         torch.cuda.synchronize()
+        torch.cuda.empty_cache()  # hand the first pipeline's blocks back before the second allocates
 
     # One shared stream: passes and kernels run in isolation, for the per-pass
     # split overhead and the kernel roofline.
-    pipe = EmulatedPipeline(w, ws, ops=None, device=dev)
+    pipe = EmulatedPipeline(w, ws, ops=ops, device=dev, recompute_act=recompute_act)
     del ws
     y, dx = pipe.io_buffers()
     t_split = {}
@@ -184,8 +189,10 @@ def main() -> int:
     else:
         pipe.run(ops, X, DY, y, dx)  # one untimed step before the kernel-timing phase
     if a.mode == "full" and not a.no_fused:
+        pipe.plan(ops_fused)
         fused_ms = timed(pipe, ops_fused, X, DY, y, dx, max(2, a.steps // 2), 1)
         trf, _ = pipe.run(ops_fused, X, DY, y, dx, trace=True)
+        pipe.plan(ops)
         t_f = {k: sum(ms for (op, ms, _) in trf if op[1] == k) for k in "FU"}
         fused.update({"ms_per_step_one_stream": single_ms,
                       "ms_per_step_1f1b_unsplit_one_stream": fused_ms,
@@ -241,6 +248,7 @@ def main() -> int:
         "config": {"workload": w.name, "stages_emulated": w.n_stages, "n_micro": w.n_micro,
                    "layers_per_stage": w.n_layers, "hidden": w.hidden, "ffn": w.ffn, "seq": w.seq,
                    "micro_batch": w.micro_batch, "order": order, "executor": "one HIP stream per stage",
+                   "recompute_act": recompute_act if recompute_act is not None else pipe.recompute_act,
                    "flops_per_step": flops},
         "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS if a.mode == "full" else None,
         "gemm_only_tflops": gemm_flops / (gemm_ms / 1e3) / 1e12 if gemm_ms > 0 else None,

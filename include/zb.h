@@ -84,6 +84,12 @@ typedef struct {
   int micro_batch;  /* sequences per microbatch                    */
   int n_micro;      /* m, microbatches per step                    */
   int gelu;         /* ZB_GELU_*                                   */
+  int recompute_act; /* 0: stash the MLP activation A = GeLU(Z) from F to W
+                      *    and Z from F to B;
+                      * 1: stash only Z (F to W) and rebuild A from it
+                      *    before W: 8 T ffn bytes less per layer for every
+                      *    microbatch between F and B, one elementwise pass
+                      *    more per W (A then comes from the bf16 Z).      */
 } zb_stage_desc;
 
 /* One pass of a schedule.  kind: 'F', 'B', 'W', or 'U' = unsplit backward

@@ -42,7 +42,7 @@ class ZbError(RuntimeError):
 class zb_stage_desc(C.Structure):
     _fields_ = [("kind", C.c_int), ("dtype", C.c_int), ("n_layers", C.c_int), ("hidden", C.c_int),
                 ("ffn", C.c_int), ("n_heads", C.c_int), ("seq", C.c_int), ("micro_batch", C.c_int),
-                ("n_micro", C.c_int), ("gelu", C.c_int)]
+                ("n_micro", C.c_int), ("gelu", C.c_int), ("recompute_act", C.c_int)]
 
 
 class zb_op(C.Structure):
@@ -266,8 +266,9 @@ def zb_events_inspect(tasks: Sequence[dict], stage_count: int):
 # -------------------------------------------------------------- stage layer
 
 def make_desc(kind: int, dtype: int, n_layers: int, hidden: int, ffn: int, n_heads: int, seq: int,
-              micro_batch: int, n_micro: int, gelu: int = ZB_GELU_ERF) -> zb_stage_desc:
-    return zb_stage_desc(kind, dtype, n_layers, hidden, ffn, n_heads, seq, micro_batch, n_micro, gelu)
+              micro_batch: int, n_micro: int, gelu: int = ZB_GELU_ERF, recompute_act: int = 0) -> zb_stage_desc:
+    return zb_stage_desc(kind, dtype, n_layers, hidden, ffn, n_heads, seq, micro_batch, n_micro, gelu,
+                         recompute_act)
 
 
 def zb_stage_create(desc: zb_stage_desc, stage_index: int, weights: Sequence, dw: Sequence, stream=None) -> int:

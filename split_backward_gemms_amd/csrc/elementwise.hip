@@ -1,9 +1,13 @@
 // Small memory-bound kernels of the stage path: strided zero fill (the Q and
 // K columns of dQKV when attention is the identity), the non-finite check of
-// the gradient buffers at the step boundary, and flag clearing.  Fills are
+// the gradient buffers at the step boundary, flag clearing, and the GeLU that
+// rebuilds the MLP activation A = gelu(Z) from the saved pre-activation for W.  Fills are
 // kernels rather than hipMemsetAsync so that the path can be graph-captured.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
+#include "device_common.h"
 #include "zb_internal.h"
 
 namespace zb {
@@ -38,7 +42,47 @@ __global__ void nonfinite_kernel(const float* __restrict__ p, int64_t n, int* fl
 
 __global__ void zero_int_kernel(int* p) { *p = 0; }
 
+// A = gelu(Z), bf16: 8 elements per thread (n % 8 == 0, 16-byte aligned), with
+// the GeLU of the forward epilogue.  The forward took GeLU of the fp32
+// pre-activation, this takes it of the stored bf16 Z: the two activations
+// agree to within one bf16 rounding, and every schedule order rebuilds the
+// same bits.
+__global__ void gelu_bf16_kernel(const uint4* __restrict__ z, uint4* __restrict__ a, int64_t n8, int kind) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+    const uint4 v = z[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = dev::pack_bf16x2(dev::gelu_f(__uint_as_float(w[e] << 16), kind),
+                              dev::gelu_f(__uint_as_float(w[e] & 0xffff0000u), kind));
+    a[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+__global__ void gelu_f32_kernel(const float* __restrict__ z, float* __restrict__ a, int64_t n, int kind) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    a[i] = dev::gelu_f(z[i], kind);
+}
+
 }  // namespace
+
+zb_status launch_gelu(const void* z, void* a, int64_t n, int dtype, int kind, hipStream_t s) {
+  if (n <= 0) return ZB_OK;
+  const int64_t units = dtype == ZB_DTYPE_BF16 ? n / 8 : n;
+  if (dtype == ZB_DTYPE_BF16 && (n % 8 || (reinterpret_cast<uintptr_t>(z) | reinterpret_cast<uintptr_t>(a)) & 15))
+    return set_error(ZB_E_UNSUPPORTED, "gelu: bf16 needs a multiple of 8 elements, 16-byte aligned");
+  const int64_t blocks = std::min<int64_t>((units + 255) / 256, 4096);
+  ProfScope ps("gelu_recompute", 0.0, (dtype == ZB_DTYPE_BF16 ? 4.0 : 8.0) * n, s);
+  if (dtype == ZB_DTYPE_BF16)
+    hipLaunchKernelGGL(gelu_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const uint4*>(z),
+                       static_cast<uint4*>(a), units, kind);
+  else
+    hipLaunchKernelGGL(gelu_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const float*>(z),
+                       static_cast<float*>(a), units, kind);
+  ZB_HIP_CHECK(hipGetLastError());
+  return ZB_OK;
+}
 
 zb_status launch_zero2d(void* p, int64_t rows, int64_t cols, int64_t ld, int elem_bytes, hipStream_t s) {
   if (rows <= 0 || cols <= 0) return ZB_OK;

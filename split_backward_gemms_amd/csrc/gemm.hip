@@ -29,10 +29,14 @@
 #include <cstdio>
 #include <type_traits>
 
+#include "device_common.h"
 #include "zb_internal.h"
 
 namespace zb {
 namespace {
+
+using dev::gelu_f;
+using dev::gelu_grad_f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -79,51 +83,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)pack_bf16x2(f, 0.0f); }
-
-// Standard normal CDF Phi(z) and exp(-z^2/2) without branches: erf(x) for
-// x >= 0 by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
-// 7.1.26 (absolute error <= 1.5e-7),
-//   erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),  t = 1 / (1 + p x),
-// with erf(-x) = -erf(x); the reciprocal and exp2 run on the hardware
-// transcendental unit.  At x = |z| / sqrt(2), exp(-x^2) is exp(-z^2 / 2).
-struct NormalParts {
-  float cdf;  // Phi(z)
-  float e;    // exp(-z^2 / 2)
-};
-__device__ __forceinline__ NormalParts normal_parts(float z) {
-  const float x = fabsf(z) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
-  float poly = fmaf(1.061405429f, t, -1.453152027f);
-  poly = fmaf(poly, t, 1.421413741f);
-  poly = fmaf(poly, t, -0.284496736f);
-  poly = fmaf(poly, t, 0.254829592f);
-  poly *= t;
-  const float e = __builtin_amdgcn_exp2f(-(x * x) * 1.4426950408889634f);
-  const float erf_z = copysignf(1.0f - poly * e, z);
-  return {fmaf(0.5f, erf_z, 0.5f), e};
-}
-
-// gelu(z) = z Phi(z); the tanh form is kept for callers that ask for it.
-__device__ __forceinline__ float gelu_f(float z, int kind) {
-  if (kind == ZB_GELU_TANH) {
-    const float c = 0.7978845608028654f;  // sqrt(2/pi)
-    float u = c * (z + 0.044715f * z * z * z);
-    return 0.5f * z * (1.0f + tanhf(u));
-  }
-  return z * normal_parts(z).cdf;
-}
-
-// gelu'(z) = Phi(z) + z phi(z), phi(z) = exp(-z^2 / 2) / sqrt(2 pi).
-__device__ __forceinline__ float gelu_grad_f(float z, int kind) {
-  if (kind == ZB_GELU_TANH) {
-    const float c = 0.7978845608028654f;
-    float u = c * (z + 0.044715f * z * z * z);
-    float t = tanhf(u);
-    return 0.5f * (1.0f + t) + 0.5f * z * (1.0f - t * t) * c * (1.0f + 3.0f * 0.044715f * z * z);
-  }
-  const NormalParts n = normal_parts(z);
-  return fmaf(z * n.e, 0.3989422804014327f, n.cdf);
-}
 
 template <typename T>
 __device__ __forceinline__ float ld_elem(const void* p, int64_t i);

@@ -191,9 +191,9 @@ struct Pool {
 };
 
 struct LayerOff {
-  // FW
+  // FW (a: the MLP activation, stashed unless it is rebuilt from z for W)
   size_t x = 0, qkv_fw = 0, o = 0, xup = 0, a = 0;
-  // FB
+  // FB, or FW when A is rebuilt (z: the MLP pre-activation)
   size_t z = 0, qkv_fb = 0, lse = 0;
   // BW
   size_t dy = 0, dz = 0, dp = 0, dqkv = 0;
@@ -217,6 +217,7 @@ struct zb_stage {
   std::vector<LayerOff> off;
   size_t fw_bytes = 0, fb_bytes = 0, bw_bytes = 0, scratch_bytes = 0;
   size_t scratch_do = 0, scratch_flag = 0, scratch_dsum = 0;
+  size_t scratch_act = 0, act_bytes = 0;  // A = gelu(Z) per layer: forward hand-off, W operand
   size_t scratch_part = 0, part_bytes = 0;  // split-K arena of the F/B GEMMs
   // plan
   bool planned = false;
@@ -265,9 +266,12 @@ void compute_layout(zb_stage* S) {
       o.o = fw; fw += align_up(T * h * es);
       o.xup = fw; fw += align_up(T * h * es);
     }
-    o.a = fw; fw += align_up(T * f * es);
-
-    o.z = fb; fb += align_up(T * f * es);
+    if (S->d.recompute_act) {
+      o.z = fw; fw += align_up(T * f * es);
+    } else {
+      o.a = fw; fw += align_up(T * f * es);
+      o.z = fb; fb += align_up(T * f * es);
+    }
     if (S->d.kind == ZB_KIND_FULL) {
       o.qkv_fb = fb; fb += align_up(T * 3 * h * es);
       o.lse = fb; fb += align_up(a * T * 4);
@@ -289,6 +293,9 @@ void compute_layout(zb_stage* S) {
   if (S->d.kind == ZB_KIND_FULL) sc += align_up(T * h * es);
   S->scratch_dsum = sc;
   if (S->d.kind == ZB_KIND_FULL) sc += align_up(a * T * 4);
+  S->act_bytes = align_up(T * f * es);
+  S->scratch_act = sc;
+  if (S->d.recompute_act) sc += (size_t)S->L * S->act_bytes;
   // Split-K arena: the largest any F or B GEMM of the stage asks for (bf16 only).
   size_t part = 0;
   if (S->d.dtype == ZB_DTYPE_BF16) {
@@ -420,6 +427,25 @@ char* elem(char* base, size_t off, int64_t col, size_t es) { return base + off +
 
 // ---------------------------------------------------------------- passes
 
+// Where layer l's MLP activation A = gelu(Z) and pre-activation Z live for
+// microbatch slots (fwb, fbb).  With recompute_act, A is not stashed: the
+// forward writes it to stage scratch for the down projection, and W (or the
+// unsplit backward) rebuilds it there from the stashed bf16 Z, which B needs
+// anyway for GeLU'.  That keeps 8 T f bytes per layer out of every microbatch
+// between F and B.
+char* act(zb_stage* S, char* fwb, int l) {
+  return S->d.recompute_act ? S->scratch + S->scratch_act + (size_t)l * S->act_bytes : fwb + S->off[l].a;
+}
+char* pre(zb_stage* S, char* fwb, char* fbb, int l) {
+  return (S->d.recompute_act ? fwb : fbb) + S->off[l].z;
+}
+// A for W: rebuilt from Z when it was not stashed.
+zb_status act_for_w(zb_stage* S, char* fwb, int l, char** A) {
+  *A = act(S, fwb, l);
+  if (!S->d.recompute_act) return ZB_OK;
+  return launch_gelu(fwb + S->off[l].z, *A, (int64_t)S->T * S->f, S->d.dtype, S->d.gelu, S->stream);
+}
+
 zb_status run_forward(zb_stage* S, int mb, void* y) {
   char* fwb = S->fw.at(S->s_fw[mb]);
   char* fbb = S->fb.at(S->s_fb[mb]);
@@ -427,12 +453,14 @@ zb_status run_forward(zb_stage* S, int mb, void* y) {
   const size_t es = S->es;
   for (int l = 0; l < S->L; ++l) {
     const LayerOff& o = S->off[l];
+    char* A = act(S, fwb, l);
+    char* Z = pre(S, fwb, fbb, l);
     void* out = (l + 1 < S->L) ? (void*)(fwb + S->off[l + 1].x) : y;
     char* X = fwb + o.x;
     switch (S->d.kind) {
       case ZB_KIND_TINY_MLP:
-        ZB_TRY(gemm_f(S, X, h, lin_index(S, l, LIN_UP), fwb + o.a, f, EPI_GELU, nullptr, 0, fbb + o.z, f));
-        ZB_TRY(gemm_f(S, fwb + o.a, f, lin_index(S, l, LIN_DOWN), out, h, EPI_STORE));
+        ZB_TRY(gemm_f(S, X, h, lin_index(S, l, LIN_UP), A, f, EPI_GELU, nullptr, 0, Z, f));
+        ZB_TRY(gemm_f(S, A, f, lin_index(S, l, LIN_DOWN), out, h, EPI_STORE));
         break;
       case ZB_KIND_MLP_LINEARS: {
         char* qkv = fwb + o.qkv_fw;
@@ -440,8 +468,8 @@ zb_status run_forward(zb_stage* S, int mb, void* y) {
         // identity attention: proj reads the V columns of qkv in place
         ZB_TRY(gemm_f(S, elem(fwb, o.qkv_fw, 2 * h, es), 3 * h, lin_index(S, l, LIN_PROJ), fwb + o.xup, h,
                       EPI_STORE));
-        ZB_TRY(gemm_f(S, fwb + o.xup, h, lin_index(S, l, LIN_UP), fwb + o.a, f, EPI_GELU, nullptr, 0, fbb + o.z, f));
-        ZB_TRY(gemm_f(S, fwb + o.a, f, lin_index(S, l, LIN_DOWN), out, h, EPI_STORE));
+        ZB_TRY(gemm_f(S, fwb + o.xup, h, lin_index(S, l, LIN_UP), A, f, EPI_GELU, nullptr, 0, Z, f));
+        ZB_TRY(gemm_f(S, A, f, lin_index(S, l, LIN_DOWN), out, h, EPI_STORE));
         break;
       }
       default: {  // FULL
@@ -452,8 +480,8 @@ zb_status run_forward(zb_stage* S, int mb, void* y) {
         at.heads = S->d.n_heads; at.seq = S->d.seq; at.nseq = S->d.micro_batch;
         ZB_TRY(launch_attention_fwd(at, S->stream));
         ZB_TRY(gemm_f(S, fwb + o.o, h, lin_index(S, l, LIN_PROJ), fwb + o.xup, h, EPI_RESID, X, h));
-        ZB_TRY(gemm_f(S, fwb + o.xup, h, lin_index(S, l, LIN_UP), fwb + o.a, f, EPI_GELU, nullptr, 0, fbb + o.z, f));
-        ZB_TRY(gemm_f(S, fwb + o.a, f, lin_index(S, l, LIN_DOWN), out, h, EPI_RESID, fwb + o.xup, h));
+        ZB_TRY(gemm_f(S, fwb + o.xup, h, lin_index(S, l, LIN_UP), A, f, EPI_GELU, nullptr, 0, Z, f));
+        ZB_TRY(gemm_f(S, A, f, lin_index(S, l, LIN_DOWN), out, h, EPI_RESID, fwb + o.xup, h));
         break;
       }
     }
@@ -475,8 +503,12 @@ zb_status run_backward(zb_stage* S, int mb, void* dx, bool unsplit, int beta) {
     switch (S->d.kind) {
       case ZB_KIND_TINY_MLP: {
         const int up = lin_index(S, l, LIN_UP), down = lin_index(S, l, LIN_DOWN);
-        ZB_TRY(gemm_b(S, dY, h, down, bwb + o.dz, f, EPI_DGELU, fbb + o.z, f));
-        if (unsplit) ZB_TRY(gemm_w(S, fwb + o.a, f, dY, h, down, beta));
+        ZB_TRY(gemm_b(S, dY, h, down, bwb + o.dz, f, EPI_DGELU, pre(S, fwb, fbb, l), f));
+        if (unsplit) {
+          char* A;
+          ZB_TRY(act_for_w(S, fwb, l, &A));
+          ZB_TRY(gemm_w(S, A, f, dY, h, down, beta));
+        }
         ZB_TRY(gemm_b(S, bwb + o.dz, f, up, out, h, EPI_STORE));
         if (unsplit) ZB_TRY(gemm_w(S, fwb + o.x, h, bwb + o.dz, f, up, beta));
         break;
@@ -484,8 +516,12 @@ zb_status run_backward(zb_stage* S, int mb, void* dx, bool unsplit, int beta) {
       case ZB_KIND_MLP_LINEARS: {
         const int qkv = lin_index(S, l, LIN_QKV), proj = lin_index(S, l, LIN_PROJ);
         const int up = lin_index(S, l, LIN_UP), down = lin_index(S, l, LIN_DOWN);
-        ZB_TRY(gemm_b(S, dY, h, down, bwb + o.dz, f, EPI_DGELU, fbb + o.z, f));
-        if (unsplit) ZB_TRY(gemm_w(S, fwb + o.a, f, dY, h, down, beta));
+        ZB_TRY(gemm_b(S, dY, h, down, bwb + o.dz, f, EPI_DGELU, pre(S, fwb, fbb, l), f));
+        if (unsplit) {
+          char* A;
+          ZB_TRY(act_for_w(S, fwb, l, &A));
+          ZB_TRY(gemm_w(S, A, f, dY, h, down, beta));
+        }
         ZB_TRY(gemm_b(S, bwb + o.dz, f, up, bwb + o.dp, h, EPI_STORE));
         if (unsplit) ZB_TRY(gemm_w(S, fwb + o.xup, h, bwb + o.dz, f, up, beta));
         // identity attention backward: dV = dO, dQ = dK = 0
@@ -500,8 +536,12 @@ zb_status run_backward(zb_stage* S, int mb, void* dx, bool unsplit, int beta) {
         const int qkv = lin_index(S, l, LIN_QKV), proj = lin_index(S, l, LIN_PROJ);
         const int up = lin_index(S, l, LIN_UP), down = lin_index(S, l, LIN_DOWN);
         char* dO = S->scratch + S->scratch_do;
-        ZB_TRY(gemm_b(S, dY, h, down, bwb + o.dz, f, EPI_DGELU, fbb + o.z, f));
-        if (unsplit) ZB_TRY(gemm_w(S, fwb + o.a, f, dY, h, down, beta));
+        ZB_TRY(gemm_b(S, dY, h, down, bwb + o.dz, f, EPI_DGELU, pre(S, fwb, fbb, l), f));
+        if (unsplit) {
+          char* A;
+          ZB_TRY(act_for_w(S, fwb, l, &A));
+          ZB_TRY(gemm_w(S, A, f, dY, h, down, beta));
+        }
         ZB_TRY(gemm_b(S, bwb + o.dz, f, up, bwb + o.dp, h, EPI_RESID, dY, h));
         if (unsplit) ZB_TRY(gemm_w(S, fwb + o.xup, h, bwb + o.dz, f, up, beta));
         ZB_TRY(gemm_b(S, bwb + o.dp, h, proj, dO, h, EPI_STORE));
@@ -530,22 +570,24 @@ zb_status run_weight(zb_stage* S, int mb, int beta) {
   std::vector<GemmDesc> gs;
   for (int l = 0; l < S->L; ++l) {
     const LayerOff& o = S->off[l];
+    char* A;
+    ZB_TRY(act_for_w(S, fwb, l, &A));
     switch (S->d.kind) {
       case ZB_KIND_TINY_MLP:
         gs.push_back(w_desc(S, fwb + o.x, h, bwb + o.dz, f, lin_index(S, l, LIN_UP), beta));
-        gs.push_back(w_desc(S, fwb + o.a, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
+        gs.push_back(w_desc(S, A, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
         break;
       case ZB_KIND_MLP_LINEARS:
         gs.push_back(w_desc(S, fwb + o.x, h, bwb + o.dqkv, 3 * h, lin_index(S, l, LIN_QKV), beta));
         gs.push_back(w_desc(S, elem(fwb, o.qkv_fw, 2 * h, es), 3 * h, bwb + o.dp, h, lin_index(S, l, LIN_PROJ), beta));
         gs.push_back(w_desc(S, fwb + o.xup, h, bwb + o.dz, f, lin_index(S, l, LIN_UP), beta));
-        gs.push_back(w_desc(S, fwb + o.a, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
+        gs.push_back(w_desc(S, A, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
         break;
       default:  // FULL
         gs.push_back(w_desc(S, fwb + o.x, h, bwb + o.dqkv, 3 * h, lin_index(S, l, LIN_QKV), beta));
         gs.push_back(w_desc(S, fwb + o.o, h, bwb + o.dp, h, lin_index(S, l, LIN_PROJ), beta));
         gs.push_back(w_desc(S, fwb + o.xup, h, bwb + o.dz, f, lin_index(S, l, LIN_UP), beta));
-        gs.push_back(w_desc(S, fwb + o.a, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
+        gs.push_back(w_desc(S, A, f, bwb + o.dy, h, lin_index(S, l, LIN_DOWN), beta));
         break;
     }
   }
@@ -658,6 +700,7 @@ extern "C" zb_status zb_stage_create(const zb_stage_desc* d, int stage_index, co
   if (d->kind < ZB_KIND_TINY_MLP || d->kind > ZB_KIND_FULL) return set_error(ZB_E_ARG, "kind");
   if (d->dtype != ZB_DTYPE_BF16 && d->dtype != ZB_DTYPE_FP32) return set_error(ZB_E_ARG, "dtype");
   if (d->gelu != ZB_GELU_ERF && d->gelu != ZB_GELU_TANH) return set_error(ZB_E_ARG, "gelu");
+  if (d->recompute_act != 0 && d->recompute_act != 1) return set_error(ZB_E_ARG, "recompute_act must be 0 or 1");
   if (d->n_layers < 1 || d->hidden < 1 || d->ffn < 1 || d->seq < 1 || d->micro_batch < 1 || d->n_micro < 1)
     return set_error(ZB_E_ARG, "sizes must be >= 1");
   if (stage_index < 0) return set_error(ZB_E_ARG, "stage_index must be >= 0");

@@ -98,6 +98,9 @@ zb_status launch_zero2d(void* p, int64_t rows, int64_t cols, int64_t ld, int ele
 // Sets *flag (device int) to 1 if any of n fp32 values is NaN/Inf (flag must be pre-zeroed).
 zb_status launch_nonfinite(const float* p, int64_t n, int* flag, hipStream_t s);
 zb_status launch_zero_int(int* flag, hipStream_t s);
+// a[i] = gelu(z[i]) for n elements of dtype (bf16: n % 8 == 0, 16-byte aligned):
+// the MLP activation rebuilt from the stored pre-activation.
+zb_status launch_gelu(const void* z, void* a, int64_t n, int dtype, int kind, hipStream_t s);
 
 // --------------------------------------------------------- kernel timing
 bool prof_on();

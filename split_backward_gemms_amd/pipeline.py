@@ -20,10 +20,11 @@ def torch_dtype(dtype: str):
     return torch.bfloat16 if dtype == "bf16" else torch.float32
 
 
-def desc_of(w) -> "zb.zb_stage_desc":
+def desc_of(w, recompute_act: int = 0) -> "zb.zb_stage_desc":
     """Stage descriptor of a synthetic_inputs.Workload."""
     return zb.make_desc(KIND_OF[w.kind], zb.ZB_DTYPE_BF16 if w.dtype == "bf16" else zb.ZB_DTYPE_FP32,
-                        w.n_layers, w.hidden, w.ffn, max(w.n_heads, 0), w.seq, w.micro_batch, w.n_micro)
+                        w.n_layers, w.hidden, w.ffn, max(w.n_heads, 0), w.seq, w.micro_batch, w.n_micro,
+                        zb.ZB_GELU_ERF, recompute_act)
 
 
 def upload(a: np.ndarray, dtype: str, device) -> torch.Tensor:
@@ -32,13 +33,19 @@ def upload(a: np.ndarray, dtype: str, device) -> torch.Tensor:
 
 
 class EmulatedPipeline:
-    """P stages of one workload, each with its own weights, on one device and one stream."""
+    """P stages of one workload, each with its own weights, on one device."""
+
+    # Free device memory kept out of the stash when the layout is picked.
+    HEADROOM = 6 << 30
 
     def __init__(self, w, weights: Sequence[Sequence[Dict[str, np.ndarray]]], ops: Optional[Sequence] = None,
                  device: str = "cuda", stream: Optional[torch.cuda.Stream] = None,
-                 stage_streams: bool = False):
+                 stage_streams: bool = False, recompute_act: Optional[int] = None):
         """stage_streams=True gives every emulated stage its own HIP stream (default
-        priority), so independent stages' passes run concurrently."""
+        priority), so independent stages' passes run concurrently.  recompute_act
+        0 / 1 fixes the stash layout (see zb_stage_desc); None stashes the MLP
+        activation when that plan fits in free device memory and rebuilds it for W
+        otherwise."""
         self.w = w
         self.device = torch.device(device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
@@ -49,18 +56,29 @@ class EmulatedPipeline:
         self.weights: List[List[torch.Tensor]] = []
         self.grads: List[List[torch.Tensor]] = []
         self.workspaces: List[torch.Tensor] = []
-        desc = desc_of(w)
         names = [nm for nm, _, _ in w.linears()]
         shapes = {nm: (k, n) for nm, k, n in w.linears()}
         for s in range(self.P):
-            wt = [upload(weights[s][l][nm], w.dtype, self.device) for l in range(w.n_layers) for nm in names]
-            gr = [torch.empty(shapes[nm], dtype=torch.float32, device=self.device)
-                  for _ in range(w.n_layers) for nm in names]
-            h = zb.zb_stage_create(desc, s, wt, gr, self.streams[s].cuda_stream)
-            self.handles.append(h)
-            self.weights.append(wt)
-            self.grads.append(gr)
+            self.weights.append([upload(weights[s][l][nm], w.dtype, self.device)
+                                 for l in range(w.n_layers) for nm in names])
+            self.grads.append([torch.empty(shapes[nm], dtype=torch.float32, device=self.device)
+                               for _ in range(w.n_layers) for nm in names])
+        if recompute_act is None:
+            self._create(0)
+            need = sum(zb.zb_stage_workspace_bytes(h, ops) for h in self.handles)
+            free = torch.cuda.mem_get_info(self.device)[0]
+            if need + self.HEADROOM > free:
+                self.close()
+                self._create(1)
+        else:
+            self._create(int(recompute_act))
         self.plan(ops)
+
+    def _create(self, recompute_act: int) -> None:
+        self.recompute_act = recompute_act
+        desc = desc_of(self.w, recompute_act)
+        self.handles = [zb.zb_stage_create(desc, s, self.weights[s], self.grads[s], self.streams[s].cuda_stream)
+                        for s in range(self.P)]
 
     def plan(self, ops: Optional[Sequence]) -> None:
         """(Re)size and bind every stage's workspace for the given order (None = all m live)."""

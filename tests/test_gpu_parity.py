@@ -126,10 +126,10 @@ def _inputs(w):
     return ws, xs, dys
 
 
-def _run(w, ws, xs, dys, order, pipe=None):
+def _run(w, ws, xs, dys, order, pipe=None, recompute_act=None):
     ops, _ = zb.zb_schedule_build(order, w.n_stages, w.n_micro)
     if pipe is None:
-        pipe = EmulatedPipeline(w, ws, ops=ops)
+        pipe = EmulatedPipeline(w, ws, ops=ops, recompute_act=recompute_act)
     X = [upload(x, w.dtype, "cuda") for x in xs]
     DY = [upload(d, w.dtype, "cuda") for d in dys]
     y, dx = pipe.io_buffers()
@@ -158,13 +158,12 @@ REDUCED = {
 }
 
 
-@pytest.mark.parametrize("name", list(REDUCED))
-@pytest.mark.parametrize("order", ["zbh1", "1f1b"])
-def test_pipeline_matches_oracle(name, order):
+def _pipeline_vs_oracle(name, order, recompute_act):
     w = REDUCED[name]
-    print(f"pipeline parity {name} {order}", flush=True)
+    print(f"pipeline parity {name} {order} recompute_act={recompute_act}", flush=True)
     ws, xs, dys = _inputs(w)
-    pipe, y, dx, dw, _ = _run(w, ws, xs, dys, order)
+    pipe, y, dx, dw, _ = _run(w, ws, xs, dys, order, recompute_act=recompute_act)
+    assert pipe.recompute_act == recompute_act
     pipe.close()
     ref = ost.pipeline(w, ws, xs, dys)
     P = w.n_stages
@@ -181,11 +180,26 @@ def test_pipeline_matches_oracle(name, order):
     assert max(errs) <= bound
 
 
+@pytest.mark.parametrize("name", list(REDUCED))
+@pytest.mark.parametrize("order", ["zbh1", "1f1b"])
+def test_pipeline_matches_oracle(name, order):
+    _pipeline_vs_oracle(name, order, 0)
+
+
+# The stash layout that keeps only the MLP pre-activation and rebuilds A = GeLU(Z) for W.
+@pytest.mark.parametrize("name", ["tiny_bf16", "tiny_fp32", "mlp_linears_ragged", "full_reduced",
+                                  "full_ragged_two_seqs"])
+@pytest.mark.parametrize("order", ["zbh1", "1f1b"])
+def test_pipeline_matches_oracle_rebuilt_activation(name, order):
+    _pipeline_vs_oracle(name, order, 1)
+
+
+@pytest.mark.parametrize("recompute_act", [0, 1])
 @pytest.mark.parametrize("name", ["tiny_bf16", "mlp_linears_reduced", "full_reduced"])
-def test_deferred_w_bit_exact_across_orders(name):
+def test_deferred_w_bit_exact_across_orders(name, recompute_act):
     w = REDUCED[name]
     ws, xs, dys = _inputs(w)
-    pipe = EmulatedPipeline(w, ws, ops=None)  # every microbatch may be live: any order fits
+    pipe = EmulatedPipeline(w, ws, ops=None, recompute_act=recompute_act)  # every microbatch may be live
     results = {}
     orders = ["1f1b", "zbh1", "wlast", "gpipe"] + (["zbh2"] if w.n_micro >= 2 * w.n_stages - 1 else [])
     for order in orders:
