@@ -557,40 +557,67 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
                                              (uint32_t)(((int64_t)(p.M - 1) * p.ldr + p.N) * 2));
     __amdgpu_buffer_rsrc_t zrsrc = make_rsrc(EPI == EPI_GELU ? p.Z : p.C,
                                              (uint32_t)(((int64_t)(p.M - 1) * p.ldz + p.N) * 2));
+    // The GeLU form is fixed per launch: one branch here, none per element.
+    // Column groups g = 2q and 2q+1 of a 32x32 block are stored together: lane
+    // l < 32 holds columns 8g..8g+3 of both, lane l+32 columns 8g+4..8g+7;
+    // v_permlane32_swap gives lane l all eight columns of group 2q and lane
+    // l+32 all eight of group 2q+1, so every store is 16 bytes per lane and 32
+    // contiguous bytes per row.
+    const int h32 = lane >> 5;
+    const int sn = n0 + wn * WTN + 8 * h32;  // this lane's stored column, before 32 j + 16 q
+    auto swap_store = [&](const __amdgpu_buffer_rsrc_t& rs, int64_t ld, int m, int n, u32x2 a, u32x2 b) {
+      const auto s0 = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
+      const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
+      const uint32_t off = (m < p.M && n < p.N) ? (uint32_t)(((int64_t)m * ld + n) * 2) : kOOB;
+      __builtin_amdgcn_raw_buffer_store_b128(w, rs, (int)off, 0, 0);
+    };
+    auto store_all = [&](auto kind_c) {
+      constexpr int KIND = decltype(kind_c)::value;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int m = em + i * 32, n = en + j * 32 + 8 * g;
-          const bool ok = m < p.M && n < p.N;
-          float v[4];
+          for (int q = 0; q < 2; ++q) {
+            const int m = em + i * 32;
+            u32x2 cv[2], zv[2];
 #pragma unroll
-          for (int t2 = 0; t2 < 4; ++t2) v[t2] = acc[i][j][4 * g + t2];
-          if constexpr (EPI == EPI_RESID || EPI == EPI_DGELU) {
-            const uint32_t roff = ok ? (uint32_t)(((int64_t)m * p.ldr + n) * 2) : kOOB;
-            const u32x2 rv = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rrsrc, (int)roff, 0, 0));
-            const float r0 = __uint_as_float(rv[0] << 16), r1 = __uint_as_float(rv[0] & 0xffff0000u);
-            const float r2 = __uint_as_float(rv[1] << 16), r3 = __uint_as_float(rv[1] & 0xffff0000u);
-            if constexpr (EPI == EPI_RESID) {
-              v[0] += r0; v[1] += r1; v[2] += r2; v[3] += r3;
-            } else {
-              v[0] *= gelu_grad_f(r0, p.gelu); v[1] *= gelu_grad_f(r1, p.gelu);
-              v[2] *= gelu_grad_f(r2, p.gelu); v[3] *= gelu_grad_f(r3, p.gelu);
+            for (int gg = 0; gg < 2; ++gg) {
+              const int g = 2 * q + gg;
+              const int n = en + j * 32 + 8 * g;  // this lane's four computed columns
+              const bool ok = m < p.M && n < p.N;
+              float v[4];
+#pragma unroll
+              for (int t2 = 0; t2 < 4; ++t2) v[t2] = acc[i][j][4 * g + t2];
+              if constexpr (EPI == EPI_RESID || EPI == EPI_DGELU) {
+                const uint32_t roff = ok ? (uint32_t)(((int64_t)m * p.ldr + n) * 2) : kOOB;
+                const u32x2 rv =
+                    __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rrsrc, (int)roff, 0, 0));
+                const float r[4] = {__uint_as_float(rv[0] << 16), __uint_as_float(rv[0] & 0xffff0000u),
+                                    __uint_as_float(rv[1] << 16), __uint_as_float(rv[1] & 0xffff0000u)};
+#pragma unroll
+                for (int t2 = 0; t2 < 4; ++t2) {
+                  if constexpr (EPI == EPI_RESID) v[t2] += r[t2];
+                  else v[t2] *= gelu_grad_f(r[t2], KIND);
+                }
+              }
+              if constexpr (EPI == EPI_GELU) {
+                zv[gg] = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+#pragma unroll
+                for (int t2 = 0; t2 < 4; ++t2) v[t2] = gelu_f(v[t2], KIND);
+              }
+              cv[gg] = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
             }
+            const int n = sn + j * 32 + 16 * q;
+            if constexpr (EPI == EPI_GELU) swap_store(zrsrc, p.ldz, m, n, zv[0], zv[1]);
+            swap_store(crsrc, p.ldc, m, n, cv[0], cv[1]);
           }
-          if constexpr (EPI == EPI_GELU) {
-            const uint32_t zoff = ok ? (uint32_t)(((int64_t)m * p.ldz + n) * 2) : kOOB;
-            const u32x2 zv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-            __builtin_amdgcn_raw_buffer_store_b64(zv, zrsrc, (int)zoff, 0, 0);
-#pragma unroll
-            for (int t2 = 0; t2 < 4; ++t2) v[t2] = gelu_f(v[t2], p.gelu);
-          }
-          const uint32_t off = ok ? (uint32_t)(((int64_t)m * p.ldc + n) * 2) : kOOB;
-          const u32x2 cv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          __builtin_amdgcn_raw_buffer_store_b64(cv, crsrc, (int)off, 0, 0);
-        }
+    };
+    if ((EPI == EPI_GELU || EPI == EPI_DGELU) && p.gelu == ZB_GELU_TANH)
+      store_all(std::integral_constant<int, ZB_GELU_TANH>{});
+    else
+      store_all(std::integral_constant<int, ZB_GELU_ERF>{});
   }
 }
 
@@ -872,6 +899,11 @@ zb_status launch_gemm(const GemmDesc& g, hipStream_t s) {
     return set_error(ZB_E_UNSUPPORTED, "gemm: contiguous extents and leading dims must be multiples of 8 "
                                        "(M=%d N=%d K=%d lda=%lld ldb=%lld)", g.M, g.N, g.K,
                      (long long)g.lda, (long long)g.ldb);
+  if (g.epi != EPI_ACC && (g.N % 8 || g.ldc % 8 || reinterpret_cast<uintptr_t>(g.C) % 16 ||
+                           ((g.epi == EPI_RESID || g.epi == EPI_DGELU) && (g.ldr % 8 || !aligned16(g.R))) ||
+                           (g.epi == EPI_GELU && (g.ldz % 8 || !aligned16(g.Z)))))
+    return set_error(ZB_E_UNSUPPORTED, "gemm: bf16 outputs need N and leading dims that are multiples of 8 "
+                                       "and 16-byte aligned rows (N=%d ldc=%lld)", g.N, (long long)g.ldc);
   {
     // Buffer offsets are 32-bit with out-of-range lanes placed at 2 GiB.
     const double lim = 2147483648.0 - 256.0;
