@@ -221,12 +221,24 @@ def main() -> int:
     top = kern[0]
     avg_ms = top["total_ms"] / top["launches"]
     per_launch_flops = top["flops"] / top["launches"]
-    achieved = per_launch_flops / (avg_ms / 1e3) / 1e12
-    roofline = {"bound": "mfma", "kernel": top["name"], "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": pmc_traffic(w.name, top["name"]),
-                "avg_launch_us": avg_ms * 1e3, "flops_per_launch": per_launch_flops,
-                "measured_on": "one stream, hipEvent pair per launch"}
+    per_launch_bytes = top["bytes"] / top["launches"]
+    # The dominant kernel's bound: MFMA when its algorithmic intensity is above
+    # the ridge point (peak FLOP/s over peak HBM bytes/s), HBM below it.
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    intensity = per_launch_flops / per_launch_bytes if per_launch_bytes > 0 else float("inf")
+    if intensity >= ridge:
+        achieved = per_launch_flops / (avg_ms / 1e3) / 1e12
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / PEAK_BF16_TFLOPS}
+    else:
+        achieved = per_launch_bytes / (avg_ms / 1e3) / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": achieved / PEAK_HBM_GBS}
+    roofline.update({"traffic": pmc_traffic(w.name, top["name"]), "kernel": top["name"],
+                     "avg_launch_us": avg_ms * 1e3, "flops_per_launch": per_launch_flops,
+                     "bytes_per_launch": per_launch_bytes, "flop_per_byte": intensity, "ridge": ridge,
+                     "tflops": per_launch_flops / (avg_ms / 1e3) / 1e12,
+                     "measured_on": "one stream, hipEvent pair per launch"})
     kernels = [{"name": r["name"], "launches_per_step": r["launches"] / prof_steps,
                 "ms_per_step": r["total_ms"] / prof_steps,
                 "tflops": r["flops"] / r["total_ms"] / 1e9} for r in kern]
