@@ -143,6 +143,22 @@ zb_status zb_schedule_simulate(int P, int m, const zb_op* ops, int n_ops,
 zb_status zb_schedule_build(int order, int P, int m, const int64_t* times, int64_t t_comm,
                             zb_op* linear_out, int cap, int* n_out, zb_sim_stats* stats);
 
+/* Automatic schedule (Zero Bubble Pipeline Parallelism, section 3.1, the
+ * heuristic): builds every stage's order from profiled times[3] = {T_F, T_B,
+ * T_W} (>= 1) and t_comm, keeping each stage's activation memory within
+ * m_limit when F adds m_b, B adds m_w - m_b and W adds -m_w (charged at the
+ * start of a pass).  m_limit = P * m_b is ZB-1p (1F1B's peak), 2 * P * m_b is
+ * ZB-2p.  Two binary choices (warm-up fill, warm-up balance) are searched and
+ * the order with the smallest simulated makespan kept; *choice_out (host, may
+ * be NULL) receives 2 * fill + balance.  Emits split B and W passes with each
+ * stage's W in ascending microbatch order, linearized like zb_schedule_build
+ * into linear_out (host, cap >= 3*P*m); stats (host, may be NULL).
+ * Errors: ZB_E_ARG (sizes, times < 1, m_limit < max(m_b, m_w), cap),
+ * ZB_E_DEADLOCK. */
+zb_status zb_schedule_heuristic(int P, int m, const int64_t* times, int64_t t_comm, int64_t m_b,
+                                int64_t m_w, int64_t m_limit, zb_op* linear_out, int cap, int* n_out,
+                                zb_sim_stats* stats, int* choice_out);
+
 /* Interleaved pipeline with v chunks per device (simulation only): forwards
  * group by group of P microbatches over chunks 0..v-1, unsplit backwards over
  * chunks v-1..0.  times are per chunk.  Needs m % P == 0. */

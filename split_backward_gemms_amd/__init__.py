@@ -98,6 +98,8 @@ def lib():
                                          C.POINTER(I64), C.POINTER(zb_sim_stats)]),
             "zb_schedule_build": (I, [I, I, I, C.POINTER(I64), I64, op_p, I, C.POINTER(I),
                                       C.POINTER(zb_sim_stats)]),
+            "zb_schedule_heuristic": (I, [I, I, C.POINTER(C.c_int64), C.c_int64, C.c_int64, C.c_int64, C.c_int64,
+                                               op_p, I, C.POINTER(I), C.POINTER(zb_sim_stats), C.POINTER(I)]),
             "zb_schedule_simulate_interleaved": (I, [I, I, I, C.POINTER(I64), C.POINTER(zb_sim_stats)]),
             "zb_schedule_validate": (I, [I, I, op_p, I, C.POINTER(I)]),
             "zb_schedule_peak_memory": (I, [op_p, I, I, I64, I64, C.POINTER(I64)]),
@@ -136,7 +138,7 @@ def lib():
 
 def exported_symbols() -> List[str]:
     """Names of the C entry points this binding expects (all declared in zb.h)."""
-    return ["zb_schedule_stage_order", "zb_schedule_simulate", "zb_schedule_build",
+    return ["zb_schedule_stage_order", "zb_schedule_simulate", "zb_schedule_build", "zb_schedule_heuristic",
             "zb_schedule_simulate_interleaved", "zb_schedule_validate", "zb_schedule_peak_memory",
             "zb_events_inspect", "zb_stage_create", "zb_stage_class_bytes", "zb_stage_workspace_bytes",
             "zb_stage_bind_workspace", "zb_stage_input_slot", "zb_stage_grad_slot", "zb_forward",
@@ -212,6 +214,19 @@ def zb_schedule_build(order, P: int, m: int, times=(1, 1, 1), t_comm: int = 0):
     st = zb_sim_stats()
     _check(lib().zb_schedule_build(o, P, m, _times(times), t_comm, arr, cap, C.byref(n), C.byref(st)))
     return ops_from_c(arr, n.value), st.as_dict()
+
+
+def zb_schedule_heuristic(P: int, m: int, times, m_b: int, m_w: int, m_limit: int, t_comm: int = 0):
+    """Automatic schedule within an activation-memory budget.  Returns (one-device
+    order, stats dict, (fill, balance) choice)."""
+    cap = 3 * P * m
+    arr = (zb_op * cap)()
+    n = C.c_int(0)
+    st = zb_sim_stats()
+    ch = C.c_int(-1)
+    _check(lib().zb_schedule_heuristic(P, m, _times(times), t_comm, m_b, m_w, m_limit, arr, cap, C.byref(n),
+                                       C.byref(st), C.byref(ch)))
+    return ops_from_c(arr, n.value), st.as_dict(), (ch.value >> 1, ch.value & 1)
 
 
 def zb_schedule_simulate_interleaved(P: int, m: int, v: int, times=(1, 1, 1)) -> dict:

@@ -301,6 +301,219 @@ extern "C" zb_status zb_schedule_build(int order, int P, int m, const int64_t* t
   return ZB_OK;
 }
 
+// ------------------------------------------------------ automatic scheduler
+//
+// The heuristic of "Zero Bubble Pipeline Parallelism", section 3.1 (the
+// structured summary's "The Heuristic Scheduling Algorithm"): warm-up forwards
+// within the activation-memory budget, a steady state that alternates F and B
+// and fills gaps with W, a forward-count balance between neighbouring stages,
+// a cool-down that drains the remaining W, and a search over two binary
+// choices.  Readings where the description is open:
+//  - list scheduling in time: the stage that is free first (ties: lower stage)
+//    picks among passes whose producers are placed; stages free at the same
+//    moment re-decide until none places another pass;
+//  - primary pass: F while warming up (no B yet), then B and F alternate, B
+//    first (a W does not break the alternation);
+//  - memory is charged at the start of a pass: F +M_B, B +(M_W - M_B), W -M_W;
+//    a forward also leaves room for its own B; a blocked F yields to B, a
+//    blocked B to W, else the stage waits;
+//  - fill: during warm-up, a forward that would end after the first B could
+//    start is placed anyway (1) or the stage switches to B (0);
+//  - balance: during warm-up a forward on stage s > 0 needs stage s-1 to stay
+//    at least one forward ahead (unless s-1 has placed all forwards); the
+//    first forward of a stage is exempt, so a small budget cannot deadlock;
+//  - a pending W (ascending microbatch) fills the wait for the primary pass if
+//    the wait is at least T_W, if the primary pass cannot run at all, or if
+//    waiting would make this stage's accumulated idle time the largest;
+//  - the four (fill, balance) choices are tried in the order (0,0), (0,1),
+//    (1,0), (1,1), scored by the simulator's makespan; the first best wins.
+namespace {
+
+constexpr int64_t kInf = INT64_MAX / 4;
+
+zb_status heuristic_build(int P, int m, const int64_t* t, int64_t t_comm, int64_t m_b, int64_t m_w,
+                          int64_t m_limit, int fill, int balance, std::vector<std::vector<zb_op>>& orders) {
+  const int64_t dF = m_b, dB = m_w - m_b, dW = -m_w;
+  const int64_t reserve = std::max<int64_t>(0, m_w - m_b);
+  orders.assign(P, {});
+  std::vector<int> nf(P, 0), nb(P, 0), wq_head(P, 0);
+  std::vector<std::vector<int>> wq(P);
+  std::vector<int64_t> mem(P, 0), freet(P, 0), idle(P, 0);
+  std::vector<char> last(P, 0);
+  std::vector<int64_t> end_f((size_t)P * m, -1), end_b((size_t)P * m, -1);
+  const int64_t total = 3LL * P * m;
+  int64_t placed = 0;
+  auto active = [&](int s) { return (int)orders[s].size() < 3 * m; };
+  auto ready_f = [&](int s) -> int64_t {
+    if (s == 0) return 0;
+    const int64_t e = end_f[(size_t)(s - 1) * m + nf[s]];
+    return e < 0 ? kInf : e + t_comm;
+  };
+  auto ready_b = [&](int s) -> int64_t {
+    const int j = nb[s];
+    int64_t r = end_f[(size_t)s * m + j];
+    if (r < 0) return kInf;
+    if (s < P - 1) {
+      const int64_t e = end_b[(size_t)(s + 1) * m + j];
+      if (e < 0) return kInf;
+      r = std::max(r, e + t_comm);
+    }
+    return r;
+  };
+  auto primary = [&](int s) -> char {
+    const bool f_left = nf[s] < m, b_avail = nb[s] < nf[s];
+    if (nb[s] == 0) return f_left ? 'F' : (b_avail ? 'B' : 0);
+    if (!f_left) return nb[s] < m ? 'B' : 0;
+    if (last[s] == 'B' || !b_avail) return 'F';
+    return 'B';
+  };
+  auto place = [&](int s, char kind, int64_t now) {
+    int j;
+    int64_t start = now;
+    if (kind == 'F') {
+      j = nf[s];
+      start = std::max(now, ready_f(s));
+      ++nf[s];
+      end_f[(size_t)s * m + j] = start + t[0];
+    } else if (kind == 'B') {
+      j = nb[s];
+      start = std::max(now, ready_b(s));
+      ++nb[s];
+      end_b[(size_t)s * m + j] = start + t[1];
+      wq[s].push_back(j);
+    } else {
+      j = wq[s][wq_head[s]++];
+    }
+    if (!orders[s].empty()) idle[s] += start - now;
+    mem[s] += kind == 'F' ? dF : (kind == 'B' ? dB : dW);
+    freet[s] = start + t[kind == 'F' ? 0 : (kind == 'B' ? 1 : 2)];
+    zb_op o{};
+    o.stage = s;
+    o.mb = j;
+    o.kind = kind;
+    orders[s].push_back(o);
+    if (kind != 'W') last[s] = kind;
+    ++placed;
+  };
+  // 0: place `kind`; 1: wait until `until`; 2: defer to the next event.
+  auto decide = [&](int s, int64_t now, char& kind, int64_t& until) -> int {
+    char p = primary(s);
+    if (p == 'F') {
+      bool blocked = mem[s] + dF + reserve > m_limit;
+      if (balance && nb[s] == 0 && nf[s] > 0 && s > 0 && nf[s - 1] < m && nf[s - 1] < nf[s] + 2) blocked = true;
+      if (blocked) {
+        p = nb[s] < nf[s] ? 'B' : 0;
+      } else if (nb[s] == 0 && nb[s] < nf[s] && !fill) {
+        const int64_t rb = ready_b(s);
+        if (rb < kInf && std::max(now, ready_f(s)) + t[0] > rb) p = 'B';
+      }
+    }
+    if (p == 'B' && mem[s] + dB > m_limit) p = 0;
+    const int64_t r = p == 'F' ? ready_f(s) : (p == 'B' ? ready_b(s) : kInf);
+    if (p && r <= now) {
+      kind = p;
+      return 0;
+    }
+    if (wq_head[s] < (int)wq[s].size()) {
+      const int64_t gap = r >= kInf ? kInf : r - now;
+      const int64_t worst = *std::max_element(idle.begin(), idle.end());
+      if (!p || gap >= t[2] || (!orders[s].empty() && gap < kInf && idle[s] + gap > worst)) {
+        kind = 'W';
+        return 0;
+      }
+    }
+    if (p && r < kInf) {
+      until = r;
+      return 1;
+    }
+    return 2;
+  };
+
+  while (placed < total) {
+    int64_t now = kInf;
+    for (int s = 0; s < P; ++s)
+      if (active(s)) now = std::min(now, freet[s]);
+    bool progress = true;
+    while (progress) {
+      progress = false;
+      for (int s = 0; s < P; ++s) {
+        if (!active(s) || freet[s] != now) continue;
+        char kind = 0;
+        int64_t until = 0;
+        const int what = decide(s, now, kind, until);
+        if (what == 0) {
+          place(s, kind, now);
+          progress = true;
+        } else if (what == 1) {
+          if (!orders[s].empty()) idle[s] += until - now;
+          freet[s] = until;
+        }
+      }
+    }
+    int64_t nxt = kInf;
+    bool stuck = false;
+    for (int q = 0; q < P; ++q) {
+      if (!active(q)) continue;
+      if (freet[q] > now) nxt = std::min(nxt, freet[q]);
+      else stuck = true;
+    }
+    if (stuck) {
+      if (nxt >= kInf) return set_error(ZB_E_DEADLOCK, "heuristic: no stage can progress");
+      for (int s = 0; s < P; ++s)
+        if (active(s) && freet[s] == now) {
+          if (!orders[s].empty()) idle[s] += nxt - now;
+          freet[s] = nxt;
+        }
+    }
+  }
+  return ZB_OK;
+}
+
+}  // namespace
+
+extern "C" zb_status zb_schedule_heuristic(int P, int m, const int64_t* times, int64_t t_comm, int64_t m_b,
+                                           int64_t m_w, int64_t m_limit, zb_op* linear_out, int cap,
+                                           int* n_out, zb_sim_stats* stats, int* choice_out) {
+  clear_error();
+  if (!times || !linear_out || !n_out) return set_error(ZB_E_ARG, "null argument");
+  if (P < 1 || m < 1) return set_error(ZB_E_ARG, "P and m must be >= 1");
+  if ((int64_t)P * m > (1 << 24)) return set_error(ZB_E_ARG, "P * m too large");
+  if (times[0] < 1 || times[1] < 1 || times[2] < 1 || t_comm < 0)
+    return set_error(ZB_E_ARG, "times must be >= 1 and t_comm >= 0");
+  if (m_b < 0 || m_w < 0 || m_limit < std::max(m_b, m_w))
+    return set_error(ZB_E_ARG, "M_limit %lld holds no microbatch (M_B %lld, M_W %lld)", (long long)m_limit,
+                     (long long)m_b, (long long)m_w);
+  if (cap < 3 * P * m) return set_error(ZB_E_ARG, "cap %d < %d ops", cap, 3 * P * m);
+  std::vector<zb_op> best_all;
+  std::vector<SimPass> best_passes;
+  zb_sim_stats best{};
+  int best_choice = -1;
+  for (int c = 0; c < 4; ++c) {
+    std::vector<std::vector<zb_op>> orders;
+    zb_status st = heuristic_build(P, m, times, t_comm, m_b, m_w, m_limit, c >> 1, c & 1, orders);
+    if (st != ZB_OK) return st;
+    std::vector<zb_op> all;
+    for (auto& o : orders) all.insert(all.end(), o.begin(), o.end());
+    std::vector<SimPass> passes;
+    zb_sim_stats ss{};
+    st = schedule_simulate(P, m, all.data(), (int)all.size(), times, t_comm, passes, &ss);
+    if (st != ZB_OK) return st;
+    if (best_choice < 0 || ss.makespan < best.makespan) {
+      best = ss;
+      best_choice = c;
+      best_all = std::move(all);
+      best_passes = std::move(passes);
+    }
+  }
+  std::vector<int> lin;
+  schedule_linearize(best_passes, lin);
+  for (size_t i = 0; i < lin.size(); ++i) linear_out[i] = best_all[lin[i]];
+  *n_out = (int)best_all.size();
+  if (stats) *stats = best;
+  if (choice_out) *choice_out = best_choice;
+  return ZB_OK;
+}
+
 extern "C" zb_status zb_schedule_simulate_interleaved(int P, int m, int v, const int64_t* t,
                                                       zb_sim_stats* stats) {
   clear_error();

@@ -189,3 +189,38 @@ def test_events_inspect_matches_oracle_on_simulated_schedules():
         assert st == zb.ZB_OK
         assert got["span"] == want["span"] and got["busy"] == want["busy"]
         assert abs(got["bubble_ratio"] - float(want["bubble_ratio"])) < 1e-12
+
+
+# ------------------------------------------------ automatic (heuristic) scheduler
+
+def test_heuristic_matches_oracle():
+    from oracle import heuristic as heu
+    rng = random.Random(11)
+    for _ in range(300):
+        P, m = rng.randint(1, 6), rng.randint(1, 12)
+        t = {"F": rng.randint(1, 5), "B": rng.randint(1, 6), "W": rng.randint(1, 4)}
+        m_b, m_w = rng.randint(1, 5), rng.randint(1, 5)
+        m_limit = rng.randint(max(m_b, m_w), (2 * P + 1) * m_b + m_w)
+        comm = rng.choice([0, 0, 1, 2])
+        orders, ms, fill, balance = heu.schedule(P, m, t, m_b, m_w, m_limit, comm)
+        sim = sch.simulate(orders, t, comm)
+        ops, st, choice = zb.zb_schedule_heuristic(P, m, (t["F"], t["B"], t["W"]), m_b, m_w, m_limit, comm)
+        assert ops == sch.linearize(orders, sim)
+        assert st["makespan"] == ms
+        assert choice == (fill, balance)
+
+
+@pytest.mark.parametrize("P,m", [(4, 8), (8, 24)])
+def test_heuristic_order_runs_through_validator(P, m):
+    for lim in (P * 2, 2 * P * 2):
+        ops, st, _ = zb.zb_schedule_heuristic(P, m, (1, 1, 1), 2, 1, lim)
+        assert zb.zb_schedule_validate(P, m, ops) == (zb.ZB_OK, -1)
+        for s in range(P):
+            assert zb.zb_schedule_peak_memory(ops, s, 2, 1) <= lim
+
+
+def test_heuristic_rejects_small_budget():
+    with pytest.raises(zb.ZbError):
+        zb.zb_schedule_heuristic(4, 8, (1, 1, 1), 2, 3, 2)
+    with pytest.raises(zb.ZbError):
+        zb.zb_schedule_heuristic(0, 8, (1, 1, 1), 2, 1, 8)
