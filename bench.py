@@ -2,9 +2,12 @@
 """Throughput of one zero-bubble pipeline stage's hot path on one MI355X.
 
 A step is one whole schedule: every emulated stage's F, B and W passes for
-every microbatch (ZB-H1 order by default), run through zb_run_schedule on one
-stream, then the step boundary (zb_grad_flush) of every stage.  Inputs,
-weights and gradient buffers are resident in HBM before timing starts.
+every microbatch (the workload's handcrafted order by default), run through
+zb_run_schedule with one HIP stream per emulated stage, then the step boundary
+(zb_grad_flush) of every stage.  Inputs, weights and gradient buffers are
+resident in HBM before timing starts.  --order zb1p / zb2p runs the automatic
+scheduler's order, built from pass times measured on this device and the
+stages' own stash sizes, with 1F1B's activation budget or twice it.
 
 Reported value: stage F+B+W TFLOP/s = algorithmic GEMM (+ attention) FLOPs of
 the step / wall time.  Also reported: % of the bf16 dense MFMA peak, the
@@ -12,7 +15,7 @@ split-backward overhead against the same step in 1F1B order with unsplit
 backwards, the dominant kernel's roofline and the fp64 CPU oracle's rate on a
 bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--order zbh1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--order zbh1|zb1p|zb2p|...]
 """
 from __future__ import annotations
 
@@ -27,6 +30,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+# Automatic orders: activation budget in units of P microbatches' stash (ZB-1p, ZB-2p).
+HEURISTIC = {"zb1p": 1, "zb2p": 2}
 
 
 def log(msg: str) -> None:
@@ -118,7 +125,7 @@ def main() -> int:
 
     import split_backward_gemms_amd as zb
     import synthetic_inputs as si
-    from split_backward_gemms_amd.pipeline import EmulatedPipeline, upload
+    from split_backward_gemms_amd.pipeline import EmulatedPipeline, heuristic_ops, pass_times_us, upload
 
     w = si.WORKLOADS[a.workload]
     order = a.order or w.order
@@ -131,8 +138,10 @@ def main() -> int:
     dys = [si.last_stage_grad(w, j) for j in range(w.n_micro)]
     log(f"inputs drawn in {time.perf_counter() - t0:.1f} s")
 
-    ops, sim = zb.zb_schedule_build(order, w.n_stages, w.n_micro)
-    ops_fused, sim_fused = zb.zb_schedule_build("1f1b", w.n_stages, w.n_micro)
+    P, m = w.n_stages, w.n_micro
+    hand = w.order if order in HEURISTIC else order
+    ops, sim = zb.zb_schedule_build(hand, P, m)
+    ops_fused, sim_fused = zb.zb_schedule_build("1f1b", P, m)
     torch.cuda.synchronize()
 
     def timed(pipe, o, X, DY, y, dx, steps, warmup):
@@ -148,12 +157,33 @@ def main() -> int:
     X = [upload(x, w.dtype, dev) for x in xs]
     DY = [upload(d, w.dtype, dev) for d in dys]
     flops = gpu_step_flops(w)
+    heur = {}
+    probe_recompute = None
+    if order in HEURISTIC:
+        # The automatic scheduler takes the passes' measured times (one stream,
+        # hipEvents) and the stages' own stash sizes.
+        probe = EmulatedPipeline(w, ws, ops=ops, device=dev)
+        y, dx = probe.io_buffers()
+        probe.run(ops, X, DY, y, dx)
+        tr, _ = probe.run(ops, X, DY, y, dx, trace=True)
+        times = pass_times_us(tr)
+        ops, hstats, choice, m_limit = heuristic_ops(probe.handles, P, m, times, HEURISTIC[order] * P)
+        sim = hstats
+        probe_recompute = probe.recompute_act
+        heur = {"pass_us": times, "m_limit_bytes": m_limit, "fill_balance": choice,
+                "sim_bubble_us": hstats["bubble"], "sim_makespan_us": hstats["makespan"]}
+        log(f"{order}: pass times {times} us, M_limit {m_limit / 2**30:.2f} GiB, choice {choice}, "
+            f"simulated bubble {hstats['bubble']} of {hstats['makespan']} us")
+        probe.close()
+        del probe, y, dx, tr
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     fused = {}
     ms_per_step = tflops = float("nan")
     if a.mode == "full":
         # Headline: one HIP stream per emulated stage, so independent stages overlap
         # the way pipeline stages on separate devices would.
-        pipe = EmulatedPipeline(w, ws, ops=ops, device=dev, stage_streams=True)
+        pipe = EmulatedPipeline(w, ws, ops=ops, device=dev, stage_streams=True, recompute_act=probe_recompute)
         y, dx = pipe.io_buffers()
         torch.cuda.synchronize()
         log(f"device ready: workspace {pipe.workspace_bytes() / 2**30:.2f} GiB, "
@@ -181,11 +211,23 @@ def main() -> int:
     del ws
     y, dx = pipe.io_buffers()
     t_split = {}
+    sim_measured = {}
     if a.mode == "full":
         single_ms = timed(pipe, ops, X, DY, y, dx, max(2, a.steps // 2), 1)
         tr, _ = pipe.run(ops, X, DY, y, dx, trace=True)
         t_split = {k: sum(ms for (op, ms, _) in tr if op[1] == k) for k in "FBW"}
         log(f"{order}, one stream: {single_ms:.3f} ms/step; passes {t_split}")
+        # Bubble rates the simulator gives for P devices at these measured pass times.
+        times = pass_times_us(tr)
+        names = ["1f1b", "zbh1"] + (["zbh2"] if m >= 2 * P - 1 else [])
+        for nm in names:
+            st = zb.zb_schedule_build(nm, P, m, times)[1]
+            sim_measured[nm] = st["bubble"] / st["makespan"]
+        for nm, k in HEURISTIC.items():
+            st = heuristic_ops(pipe.handles, P, m, times, k * P)[1]
+            sim_measured[nm] = st["bubble"] / st["makespan"]
+        log(f"simulated bubble rates at measured pass times {times} us: "
+            + ", ".join(f"{k} {100 * v:.1f}%" for k, v in sim_measured.items()))
     else:
         pipe.run(ops, X, DY, y, dx)  # one untimed step before the kernel-timing phase
     if a.mode == "full" and not a.no_fused:
@@ -265,11 +307,15 @@ def main() -> int:
         "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS if a.mode == "full" else None,
         "gemm_only_tflops": gemm_flops / (gemm_ms / 1e3) / 1e12 if gemm_ms > 0 else None,
         "pass_ms": t_split,
-        "sim_bubble_unit_times": {order: sim["bubble"], "1f1b": sim_fused["bubble"]},
+        "sim_bubble_unit_times": {hand: zb.zb_schedule_build(hand, P, m)[1]["bubble"],
+                                  "1f1b": sim_fused["bubble"]},
+        "sim_bubble_rate_measured_times": sim_measured,
         "roofline": roofline,
         "kernels": kernels,
     }
     out.update(fused)
+    if heur:
+        out["heuristic"] = heur
     if not a.no_cpu and a.mode == "full":
         log("timing the CPU oracle sample ...")
         out["cpu_baseline"] = cpu_baseline(w)

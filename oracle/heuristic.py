@@ -19,8 +19,10 @@ the plain reading (stated again in the design notes):
   yet), then B and F alternate, B first; F stops being primary once all m
   forwards are placed, B once all m backwards are.
 * Memory is charged at the start of a pass, as in the memory ledger: F adds
-  M_B, B adds M_W - M_B, W adds -M_W.  A primary F (or B) that would exceed
-  M_limit yields to a W (or, for F, to B), else the stage waits.
+  M_B, B adds M_W - M_B, W adds -M_W; a forward also keeps room for its own B
+  (max(0, M_W - M_B)).  A primary F that would exceed M_limit yields to a
+  pending W (the memory-triggered W), else to B; a B that would exceed it
+  yields to W; else the stage waits.
 * fill (first binary choice): during warm-up, a forward that would end after
   the first B could start is still placed (fill = 1) or the stage switches to
   B (fill = 0).
@@ -130,7 +132,10 @@ def build(P: int, m: int, t: Dict[str, int], m_b: int, m_w: int, m_limit: int, f
         """('place', kind) | ('wait', time) | ('defer', None): the next step of stage s at `now`."""
         p = primary(s)
         if p == "F":
-            blocked = mem[s] + delta["F"] + reserve > m_limit
+            full = mem[s] + delta["F"] + reserve > m_limit
+            if full and w_q[s]:
+                return ("place", "W")            # memory-triggered W: free a microbatch's stash first
+            blocked = full
             if balance and n_b[s] == 0 and 0 < n_f[s] and s > 0 and n_f[s - 1] < m and n_f[s - 1] < n_f[s] + 2:
                 blocked = True                   # warm-up: keep one forward of lead on the upstream stage
             if blocked:

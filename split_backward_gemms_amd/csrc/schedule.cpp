@@ -315,8 +315,9 @@ extern "C" zb_status zb_schedule_build(int order, int P, int m, const int64_t* t
 //  - primary pass: F while warming up (no B yet), then B and F alternate, B
 //    first (a W does not break the alternation);
 //  - memory is charged at the start of a pass: F +M_B, B +(M_W - M_B), W -M_W;
-//    a forward also leaves room for its own B; a blocked F yields to B, a
-//    blocked B to W, else the stage waits;
+//    a forward also leaves room for its own B; an F over the budget yields
+//    to a pending W (memory-triggered W), else to B; a B over it yields to W;
+//    else the stage waits;
 //  - fill: during warm-up, a forward that would end after the first B could
 //    start is placed anyway (1) or the stage switches to B (0);
 //  - balance: during warm-up a forward on stage s > 0 needs stage s-1 to stay
@@ -399,7 +400,12 @@ zb_status heuristic_build(int P, int m, const int64_t* t, int64_t t_comm, int64_
   auto decide = [&](int s, int64_t now, char& kind, int64_t& until) -> int {
     char p = primary(s);
     if (p == 'F') {
-      bool blocked = mem[s] + dF + reserve > m_limit;
+      const bool full = mem[s] + dF + reserve > m_limit;
+      if (full && wq_head[s] < (int)wq[s].size()) {  // memory-triggered W frees a stash first
+        kind = 'W';
+        return 0;
+      }
+      bool blocked = full;
       if (balance && nb[s] == 0 && nf[s] > 0 && s > 0 && nf[s - 1] < m && nf[s - 1] < nf[s] + 2) blocked = true;
       if (blocked) {
         p = nb[s] < nf[s] ? 'B' : 0;

@@ -6,7 +6,7 @@ arithmetic of the method itself.
 """
 from __future__ import annotations
 
-from typing import Dict, List, Optional, Sequence
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 import torch
@@ -30,6 +30,41 @@ def desc_of(w, recompute_act: int = 0) -> "zb.zb_stage_desc":
 def upload(a: np.ndarray, dtype: str, device) -> torch.Tensor:
     """fp32 array holding bf16-exact values -> device tensor (exact conversion)."""
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device).to(torch_dtype(dtype))
+
+
+def pass_times_us(trace) -> Tuple[int, int, int]:
+    """Median duration, in whole microseconds (at least 1), of the F, B and W
+    passes of a traced run: the per-pass times the automatic scheduler takes."""
+    out = []
+    for kind in "FBW":
+        ms = sorted(t for (op, t, _) in trace if op[1] == kind)
+        if not ms:
+            raise ValueError(f"trace holds no {kind} pass")
+        out.append(max(1, int(round(1000.0 * ms[len(ms) // 2]))))
+    return tuple(out)
+
+
+def stash_per_microbatch(handles: Sequence[int]) -> Tuple[int, int]:
+    """(M_B, M_W) in bytes: the stash one microbatch holds after its F and after
+    its B, the largest over the stages (the three slot classes of a stage)."""
+    m_b = m_w = 0
+    for h in handles:
+        fw, fb, bw = zb.zb_stage_class_bytes(h)
+        m_b, m_w = max(m_b, fw + fb), max(m_w, fw + bw)
+    return m_b, m_w
+
+
+def heuristic_ops(handles: Sequence[int], n_stages: int, n_micro: int, times: Sequence[int],
+                  budget_microbatches: int):
+    """One-device order from the automatic scheduler for the stages behind
+    `handles`.  The activation budget per stage is `budget_microbatches` times
+    M_B (P for ZB-1p, 2P for ZB-2p) plus max(0, M_W - M_B): 1F1B's own peak in a
+    ledger where a B adds memory, since the microbatch in its backward holds its
+    output gradients too.  Returns (ops, stats, (fill, balance), M_limit)."""
+    m_b, m_w = stash_per_microbatch(handles)
+    m_limit = max(budget_microbatches * m_b + max(0, m_w - m_b), m_b, m_w)
+    ops, stats, choice = zb.zb_schedule_heuristic(n_stages, n_micro, times, m_b, m_w, m_limit)
+    return ops, stats, choice, m_limit
 
 
 class EmulatedPipeline:

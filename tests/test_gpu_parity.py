@@ -17,7 +17,7 @@ import split_backward_gemms_amd as zb
 import synthetic_inputs as si
 from oracle import stage as ost
 from oracle import schedules as sch
-from split_backward_gemms_amd.pipeline import EmulatedPipeline, upload
+from split_backward_gemms_amd.pipeline import EmulatedPipeline, heuristic_ops, upload
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -127,7 +127,8 @@ def _inputs(w):
 
 
 def _run(w, ws, xs, dys, order, pipe=None, recompute_act=None):
-    ops, _ = zb.zb_schedule_build(order, w.n_stages, w.n_micro)
+    """order: a handcrafted order's name, or a one-device op list."""
+    ops = zb.zb_schedule_build(order, w.n_stages, w.n_micro)[0] if isinstance(order, str) else order
     if pipe is None:
         pipe = EmulatedPipeline(w, ws, ops=ops, recompute_act=recompute_act)
     X = [upload(x, w.dtype, "cuda") for x in xs]
@@ -217,6 +218,39 @@ def test_deferred_w_bit_exact_across_orders(name, recompute_act):
                 for nm in dw[s][l]:
                     assert np.array_equal(dw[s][l][nm].view(np.uint32), base_dw[s][l][nm].view(np.uint32)), \
                         (order, s, l, nm)
+
+
+# The automatic scheduler's orders (ZB-1p: 1F1B's memory, ZB-2p: twice that),
+# with stash sizes from the stages' own ledger, run through the executor: results
+# within the bound of the oracle and, since W stays in ascending microbatch order,
+# bit-identical to 1F1B.
+@pytest.mark.parametrize("name", ["tiny_bf16", "mlp_linears_ragged", "full_reduced"])
+def test_heuristic_orders_match_oracle_and_1f1b_bits(name):
+    w = REDUCED[name]
+    print(f"heuristic orders {name}", flush=True)
+    ws, xs, dys = _inputs(w)
+    pipe = EmulatedPipeline(w, ws, ops=None, recompute_act=0)
+    _, y0, dx0, dw0, _ = _run(w, ws, xs, dys, "1f1b", pipe)
+    for budget in (w.n_stages, 2 * w.n_stages):
+        for times in ((1, 1, 1), (2, 3, 1), (18, 18, 10)):
+            ops, stats, choice, m_limit = heuristic_ops(pipe.handles, w.n_stages, w.n_micro, times, budget)
+            assert zb.zb_schedule_validate(w.n_stages, w.n_micro, ops) == (zb.ZB_OK, -1)
+            _, y, dx, dw, _ = _run(w, ws, xs, dys, ops, pipe)
+            for j in range(w.n_micro):
+                assert np.array_equal(y[j], y0[j]) and np.array_equal(dx[j], dx0[j]), (budget, times, j)
+            for s in range(w.n_stages):
+                for l in range(w.n_layers):
+                    for nm in dw[s][l]:
+                        assert np.array_equal(dw[s][l][nm].view(np.uint32), dw0[s][l][nm].view(np.uint32)), \
+                            (budget, times, s, l, nm)
+    pipe.close()
+    ref = ost.pipeline(w, ws, xs, dys)
+    P = w.n_stages
+    errs = [_rel_err(y0[j], ref["y"][P - 1][j]) for j in range(w.n_micro)]
+    errs += [_rel_err(dx0[j], ref["dx"][0][j]) for j in range(w.n_micro)]
+    errs += [_rel_err(dw0[s][l][nm], ref["dw"][s][l][nm]) for s in range(P) for l in range(w.n_layers)
+             for nm in dw0[s][l]]
+    assert max(errs) <= TOL
 
 
 def test_single_stage_api_order_errors():

@@ -69,6 +69,54 @@ def test_zb1p_beats_1f1b_and_matches_zbh1(P, t):
         assert S.peak_memory(orders[0], m_b, m_w) <= P * m_b
 
 
+# Stash ledgers where B adds memory (M_W > M_B) or frees little (M_W close to
+# M_B): with 1F1B's own peak as the budget (P microbatches' M_B plus the growth
+# M_W - M_B of the one microbatch in its backward), the automatic order is never
+# worse than 1F1B, for any pass times.
+@pytest.mark.parametrize("m_b,m_w", [(34, 32), (28, 32), (22, 32), (1, 2)])
+@pytest.mark.parametrize("P,m", [(2, 4), (4, 8), (4, 12), (8, 24)])
+def test_zb1p_never_worse_than_1f1b_any_ledger(m_b, m_w, P, m):
+    budget = P * m_b + max(0, m_w - m_b)
+    for tf, tb, tw in itertools.product(range(1, 5), repeat=3):
+        t = {"F": tf, "B": tb, "W": tw}
+        orders, ms, _, _ = H.schedule(P, m, t, m_b, m_w, budget)
+        for o in orders:
+            assert S.peak_memory(o, m_b, m_w) <= budget
+        assert ms <= S.simulate(S.stage_orders("1f1b", P, m), t).makespan, t
+
+
+def _memory_triggered_w_holds(orders, m, m_b, m_w, budget):
+    """Whenever a stage's next primary pass is F, the forward would pass the
+    budget and a W is pending, the stage's next pass is that W."""
+    reserve = max(0, m_w - m_b)
+    for o in orders:
+        mem, n_f, n_b, pending, last = 0, 0, 0, 0, None
+        for k, _ in o:
+            primary_f = n_f < m and (n_b == 0 or last == "B" or n_b == n_f)
+            if primary_f and pending and mem + m_b + reserve > budget and k != "W":
+                return False
+            mem += {"F": m_b, "B": m_w - m_b, "W": -m_w}[k]
+            n_f += k == "F"
+            n_b += k == "B"
+            pending += {"F": 0, "B": 1, "W": -1}[k]
+            if k != "W":
+                last = k
+    return True
+
+
+def test_memory_triggered_w():
+    rng = random.Random(3)
+    for _ in range(200):
+        P, m = rng.randint(2, 6), rng.randint(2, 12)
+        t = {"F": rng.randint(1, 4), "B": rng.randint(1, 4), "W": rng.randint(1, 4)}
+        m_b, m_w = rng.randint(1, 4), rng.randint(1, 4)
+        budget = rng.randint(max(m_b, m_w), 2 * P * m_b)
+        for fill in (0, 1):
+            for balance in (0, 1):
+                orders = H.build(P, m, t, m_b, m_w, budget, fill, balance)
+                assert _memory_triggered_w_holds(orders, m, m_b, m_w, budget)
+
+
 @pytest.mark.parametrize("P", [2, 4, 8])
 @pytest.mark.parametrize("t", TIMES)
 def test_zb2p_never_worse_than_zbh2(P, t):
