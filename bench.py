@@ -7,7 +7,8 @@ zb_run_schedule with one HIP stream per emulated stage, then the step boundary
 (zb_grad_flush) of every stage.  Inputs, weights and gradient buffers are
 resident in HBM before timing starts.  --order zb1p / zb2p runs the automatic
 scheduler's order, built from pass times measured on this device and the
-stages' own stash sizes, with 1F1B's activation budget or twice it.
+stages' own stash sizes, with 1F1B's activation budget or twice it; --order
+zbv runs the model cut into 2P chunk stages in the V placement's order.
 
 Reported value: stage F+B+W TFLOP/s = algorithmic GEMM (+ attention) FLOPs of
 the step / wall time.  Also reported: % of the bf16 dense MFMA peak, the
@@ -15,7 +16,7 @@ split-backward overhead against the same step in 1F1B order with unsplit
 backwards, the dominant kernel's roofline and the fp64 CPU oracle's rate on a
 bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--order zbh1|zb1p|zb2p|...]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--order zbh1|zb1p|zb2p|zbv|...]
 """
 from __future__ import annotations
 
@@ -125,10 +126,14 @@ def main() -> int:
 
     import split_backward_gemms_amd as zb
     import synthetic_inputs as si
-    from split_backward_gemms_amd.pipeline import EmulatedPipeline, heuristic_ops, pass_times_us, upload
+    from split_backward_gemms_amd.pipeline import (EmulatedPipeline, heuristic_ops, pass_times_us,
+                                                   stash_per_microbatch, upload, zbv_ops)
 
-    w = si.WORKLOADS[a.workload]
-    order = a.order or w.order
+    w0 = si.WORKLOADS[a.workload]
+    order = a.order or w0.order
+    # ZB-V runs the same model cut into 2P chunk stages of half the layers.
+    w = si.v_chunks(w0) if order == "zbv" else w0
+    n_dev = w0.n_stages
     dev = "cuda:0"
     torch.cuda.set_device(0)
     log(f"workload {w.name}: P={w.n_stages} m={w.n_micro} layers={w.n_layers} h={w.hidden} T={w.tokens} {order}")
@@ -139,7 +144,7 @@ def main() -> int:
     log(f"inputs drawn in {time.perf_counter() - t0:.1f} s")
 
     P, m = w.n_stages, w.n_micro
-    hand = w.order if order in HEURISTIC else order
+    hand = w0.order if order in HEURISTIC else ("zbh1" if order == "zbv" else order)
     ops, sim = zb.zb_schedule_build(hand, P, m)
     ops_fused, sim_fused = zb.zb_schedule_build("1f1b", P, m)
     torch.cuda.synchronize()
@@ -159,20 +164,24 @@ def main() -> int:
     flops = gpu_step_flops(w)
     heur = {}
     probe_recompute = None
-    if order in HEURISTIC:
-        # The automatic scheduler takes the passes' measured times (one stream,
-        # hipEvents) and the stages' own stash sizes.
+    if order in HEURISTIC or order == "zbv":
+        # The automatic scheduler and ZB-V take the passes' measured times (one
+        # stream, hipEvents) and the stages' own stash sizes.
         probe = EmulatedPipeline(w, ws, ops=ops, device=dev)
         y, dx = probe.io_buffers()
         probe.run(ops, X, DY, y, dx)
         tr, _ = probe.run(ops, X, DY, y, dx, trace=True)
         times = pass_times_us(tr)
-        ops, hstats, choice, m_limit = heuristic_ops(probe.handles, P, m, times, HEURISTIC[order] * P)
+        if order == "zbv":
+            ops, hstats, m_limit = zbv_ops(probe.handles, m, times)
+            choice = None
+        else:
+            ops, hstats, choice, m_limit = heuristic_ops(probe.handles, P, m, times, HEURISTIC[order] * P)
         sim = hstats
         probe_recompute = probe.recompute_act
         heur = {"pass_us": times, "m_limit_bytes": m_limit, "fill_balance": choice,
                 "sim_bubble_us": hstats["bubble"], "sim_makespan_us": hstats["makespan"]}
-        log(f"{order}: pass times {times} us, M_limit {m_limit / 2**30:.2f} GiB, choice {choice}, "
+        log(f"{order}: pass times {times} us, M_limit {m_limit / 2**30:.2f} GiB per device, choice {choice}, "
             f"simulated bubble {hstats['bubble']} of {hstats['makespan']} us")
         probe.close()
         del probe, y, dx, tr
@@ -217,15 +226,22 @@ def main() -> int:
         tr, _ = pipe.run(ops, X, DY, y, dx, trace=True)
         t_split = {k: sum(ms for (op, ms, _) in tr if op[1] == k) for k in "FBW"}
         log(f"{order}, one stream: {single_ms:.3f} ms/step; passes {t_split}")
-        # Bubble rates the simulator gives for P devices at these measured pass times.
+        # Bubble rates the simulator gives across the devices at these measured
+        # pass times (a ZB-V chunk counts as half a stage, in time and stash).
         times = pass_times_us(tr)
-        names = ["1f1b", "zbh1"] + (["zbh2"] if m >= 2 * P - 1 else [])
-        for nm in names:
-            st = zb.zb_schedule_build(nm, P, m, times)[1]
+        cut = 2 if order == "zbv" else 1
+        st_times = tuple(cut * x for x in times)
+        ch_times = times if order == "zbv" else tuple(max(1, x // 2) for x in times)
+        m_b, m_w = (cut * v for v in stash_per_microbatch(pipe.handles))
+        for nm in ["1f1b", "zbh1"] + (["zbh2"] if m >= 2 * n_dev - 1 else []):
+            st = zb.zb_schedule_build(nm, n_dev, m, st_times)[1]
             sim_measured[nm] = st["bubble"] / st["makespan"]
         for nm, k in HEURISTIC.items():
-            st = heuristic_ops(pipe.handles, P, m, times, k * P)[1]
+            st = zb.zb_schedule_heuristic(n_dev, m, st_times, m_b, m_w, k * n_dev * m_b + max(0, m_w - m_b))[1]
             sim_measured[nm] = st["bubble"] / st["makespan"]
+        cb, cw = m_b // 2, m_w // 2
+        st = zb.zb_schedule_zbv(n_dev, m, ch_times, cb, cw, 2 * n_dev * cb + max(0, cw - cb))[1]
+        sim_measured["zbv"] = st["bubble"] / st["makespan"]
         log(f"simulated bubble rates at measured pass times {times} us: "
             + ", ".join(f"{k} {100 * v:.1f}%" for k, v in sim_measured.items()))
     else:
@@ -276,7 +292,7 @@ def main() -> int:
         achieved = per_launch_bytes / (avg_ms / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": achieved / PEAK_HBM_GBS}
-    roofline.update({"traffic": pmc_traffic(w.name, top["name"]), "kernel": top["name"],
+    roofline.update({"traffic": pmc_traffic(w0.name, top["name"]), "kernel": top["name"],
                      "avg_launch_us": avg_ms * 1e3, "flops_per_launch": per_launch_flops,
                      "bytes_per_launch": per_launch_bytes, "flop_per_byte": intensity, "ridge": ridge,
                      "tflops": per_launch_flops / (avg_ms / 1e3) / 1e12,
@@ -299,7 +315,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "stages_emulated": w.n_stages, "n_micro": w.n_micro,
+        "config": {"workload": w0.name, "devices": n_dev, "stages_emulated": w.n_stages, "n_micro": w.n_micro,
                    "layers_per_stage": w.n_layers, "hidden": w.hidden, "ffn": w.ffn, "seq": w.seq,
                    "micro_batch": w.micro_batch, "order": order, "executor": "one HIP stream per stage",
                    "recompute_act": recompute_act if recompute_act is not None else pipe.recompute_act,
@@ -307,8 +323,8 @@ def main() -> int:
         "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS if a.mode == "full" else None,
         "gemm_only_tflops": gemm_flops / (gemm_ms / 1e3) / 1e12 if gemm_ms > 0 else None,
         "pass_ms": t_split,
-        "sim_bubble_unit_times": {hand: zb.zb_schedule_build(hand, P, m)[1]["bubble"],
-                                  "1f1b": sim_fused["bubble"]},
+        "sim_bubble_unit_times": {hand: zb.zb_schedule_build(hand, n_dev, m)[1]["bubble"],
+                                  "1f1b": zb.zb_schedule_build("1f1b", n_dev, m)[1]["bubble"]},
         "sim_bubble_rate_measured_times": sim_measured,
         "roofline": roofline,
         "kernels": kernels,
@@ -318,7 +334,7 @@ def main() -> int:
         out["heuristic"] = heur
     if not a.no_cpu and a.mode == "full":
         log("timing the CPU oracle sample ...")
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w0)
     print(json.dumps(out), flush=True)
     return 0
 

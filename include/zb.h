@@ -147,8 +147,9 @@ zb_status zb_schedule_build(int order, int P, int m, const int64_t* times, int64
  * heuristic): builds every stage's order from profiled times[3] = {T_F, T_B,
  * T_W} (>= 1) and t_comm, keeping each stage's activation memory within
  * m_limit when F adds m_b, B adds m_w - m_b and W adds -m_w (charged at the
- * start of a pass).  m_limit = P * m_b is ZB-1p (1F1B's peak), 2 * P * m_b is
- * ZB-2p.  Two binary choices (warm-up fill, warm-up balance) are searched and
+ * start of a pass).  ZB-1p takes 1F1B's peak, P * m_b + max(0, m_w - m_b)
+ * (the microbatch in its backward also holds its gradients when a B adds
+ * memory), ZB-2p twice the P * m_b term.  Two binary choices (warm-up fill, warm-up balance) are searched and
  * the order with the smallest simulated makespan kept; *choice_out (host, may
  * be NULL) receives 2 * fill + balance.  Emits split B and W passes with each
  * stage's W in ascending microbatch order, linearized like zb_schedule_build
@@ -158,6 +159,22 @@ zb_status zb_schedule_build(int order, int P, int m, const int64_t* times, int64
 zb_status zb_schedule_heuristic(int P, int m, const int64_t* times, int64_t t_comm, int64_t m_b,
                                 int64_t m_w, int64_t m_limit, zb_op* linear_out, int cap, int* n_out,
                                 zb_sim_stats* stats, int* choice_out);
+
+/* ZB-V (Zero Bubble Pipeline Parallelism, section 6): 2P chunks, device d
+ * holding chunks d and 2P-1-d (a V: forwards run down the devices and back
+ * up).  times[3] = {T_F, T_B, T_W} per chunk pass (>= 1); t_comm per hand-off
+ * between chunks on different devices; m_b, m_w the stash of one chunk and
+ * microbatch; m_limit the budget per device (P M_B of a whole stage = 2P *
+ * m_b).  The order is list-scheduled within the budget (a forward of a
+ * device's earlier chunk keeps room for one later-chunk forward).  Emits the
+ * 6*P*m chunk passes (zb_op.stage = chunk index 0..2P-1, split B and W, each
+ * chunk's W ascending) into linear_out (host, cap >= 6*P*m) by start time,
+ * ties to the lower chunk: a one-device order for 2P chained stages.  stats
+ * (host, may be NULL): makespan = the largest per-device time (Eq. 3), ideal =
+ * 2m(T_F+T_B+T_W), bubble = makespan - ideal.  Errors: ZB_E_ARG (sizes, times,
+ * m_limit < 2 m_b + max(0, m_w - m_b) or < m_w, cap), ZB_E_DEADLOCK. */
+zb_status zb_schedule_zbv(int P, int m, const int64_t* times, int64_t t_comm, int64_t m_b, int64_t m_w,
+                          int64_t m_limit, zb_op* linear_out, int cap, int* n_out, zb_sim_stats* stats);
 
 /* Interleaved pipeline with v chunks per device (simulation only): forwards
  * group by group of P microbatches over chunks 0..v-1, unsplit backwards over

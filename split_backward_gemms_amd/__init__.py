@@ -100,6 +100,8 @@ def lib():
                                       C.POINTER(zb_sim_stats)]),
             "zb_schedule_heuristic": (I, [I, I, C.POINTER(C.c_int64), C.c_int64, C.c_int64, C.c_int64, C.c_int64,
                                                op_p, I, C.POINTER(I), C.POINTER(zb_sim_stats), C.POINTER(I)]),
+            "zb_schedule_zbv": (I, [I, I, C.POINTER(I64), I64, I64, I64, I64, op_p, I, C.POINTER(I),
+                                    C.POINTER(zb_sim_stats)]),
             "zb_schedule_simulate_interleaved": (I, [I, I, I, C.POINTER(I64), C.POINTER(zb_sim_stats)]),
             "zb_schedule_validate": (I, [I, I, op_p, I, C.POINTER(I)]),
             "zb_schedule_peak_memory": (I, [op_p, I, I, I64, I64, C.POINTER(I64)]),
@@ -139,7 +141,7 @@ def lib():
 def exported_symbols() -> List[str]:
     """Names of the C entry points this binding expects (all declared in zb.h)."""
     return ["zb_schedule_stage_order", "zb_schedule_simulate", "zb_schedule_build", "zb_schedule_heuristic",
-            "zb_schedule_simulate_interleaved", "zb_schedule_validate", "zb_schedule_peak_memory",
+            "zb_schedule_zbv", "zb_schedule_simulate_interleaved", "zb_schedule_validate", "zb_schedule_peak_memory",
             "zb_events_inspect", "zb_stage_create", "zb_stage_class_bytes", "zb_stage_workspace_bytes",
             "zb_stage_bind_workspace", "zb_stage_input_slot", "zb_stage_grad_slot", "zb_forward",
             "zb_backward_input", "zb_backward_weight", "zb_backward_unsplit", "zb_grad_flush",
@@ -227,6 +229,18 @@ def zb_schedule_heuristic(P: int, m: int, times, m_b: int, m_w: int, m_limit: in
     _check(lib().zb_schedule_heuristic(P, m, _times(times), t_comm, m_b, m_w, m_limit, arr, cap, C.byref(n),
                                        C.byref(st), C.byref(ch)))
     return ops_from_c(arr, n.value), st.as_dict(), (ch.value >> 1, ch.value & 1)
+
+
+def zb_schedule_zbv(P: int, m: int, times, m_b: int, m_w: int, m_limit: int, t_comm: int = 0):
+    """V-shaped placement: one-device order over the 2P chunk stages (stage
+    field = chunk index) and the per-device stats dict."""
+    cap = 6 * P * m
+    arr = (zb_op * cap)()
+    n = C.c_int(0)
+    st = zb_sim_stats()
+    _check(lib().zb_schedule_zbv(P, m, _times(times), t_comm, m_b, m_w, m_limit, arr, cap, C.byref(n),
+                                 C.byref(st)))
+    return ops_from_c(arr, n.value), st.as_dict()
 
 
 def zb_schedule_simulate_interleaved(P: int, m: int, v: int, times=(1, 1, 1)) -> dict:

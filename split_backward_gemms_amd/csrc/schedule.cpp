@@ -520,6 +520,169 @@ extern "C" zb_status zb_schedule_heuristic(int P, int m, const int64_t* times, i
   return ZB_OK;
 }
 
+// ---------------------------------------------------------------- ZB-V
+//
+// "Zero Bubble Pipeline Parallelism", section 6: 2P chunks, device d holding
+// chunks d and 2P-1-d, so every microbatch's forward runs down the devices and
+// back up and its backward retraces that path.  The pages fix the placement
+// and its properties, not the order; the order is built by list scheduling:
+//  - the device free first (ties: lower device) takes the candidate pass that
+//    can start earliest, ties in the order B of its earlier chunk, F of its
+//    later chunk, F of its earlier chunk, B of its later chunk;
+//  - its oldest pending W runs when nothing else can start at once, or when
+//    the next forward would pass the budget;
+//  - memory per chunk pass F +M_B, B +(M_W-M_B), W -M_W at the start; a
+//    forward of the earlier chunk keeps room for a later-chunk forward and a
+//    B's growth, a forward of the later chunk room for its B's growth;
+//  - hand-offs between chunks on different devices cost t_comm.
+namespace {
+
+zb_status zbv_build(int P, int m, const int64_t* t, int64_t t_comm, int64_t m_b, int64_t m_w, int64_t m_limit,
+                    std::vector<zb_op>& ops, std::vector<int64_t>& start) {
+  const int C = 2 * P;
+  const int64_t reserve = std::max<int64_t>(0, m_w - m_b);
+  auto dev = [P](int c) { return c < P ? c : 2 * P - 1 - c; };
+  auto hop = [&](int a, int b) { return dev(a) == dev(b) ? int64_t(0) : t_comm; };
+  std::vector<int> nf(C, 0), nb(C, 0), count(P, 0), wq_head(P, 0);
+  std::vector<std::vector<std::pair<int, int>>> wq(P);
+  std::vector<int64_t> end_f((size_t)C * m, -1), end_b((size_t)C * m, -1), mem(P, 0), freet(P, 0);
+  auto ready_f = [&](int c) -> int64_t {
+    const int j = nf[c];
+    if (j >= m) return -1;
+    if (c == 0) return 0;
+    const int64_t e = end_f[(size_t)(c - 1) * m + j];
+    return e < 0 ? -1 : e + hop(c - 1, c);
+  };
+  auto ready_b = [&](int c) -> int64_t {
+    const int j = nb[c];
+    if (j >= nf[c]) return -1;
+    int64_t r = end_f[(size_t)c * m + j];
+    if (c < C - 1) {
+      const int64_t e = end_b[(size_t)(c + 1) * m + j];
+      if (e < 0) return -1;
+      r = std::max(r, e + hop(c + 1, c));
+    }
+    return r;
+  };
+  struct Cand { int64_t st; int rank; char kind; int chunk; };
+  ops.clear();
+  start.clear();
+  const int64_t total = 6LL * P * m;
+  for (int64_t placed = 0; placed < total; ++placed) {
+    bool have = false;
+    Cand best{};
+    int best_d = -1;
+    for (int d = 0; d < P; ++d) {
+      if (count[d] == 6 * m) continue;
+      const int lo = d, hi = C - 1 - d;
+      const int64_t now = freet[d];
+      Cand c[5];
+      int n = 0;
+      int64_t r;
+      if ((r = ready_b(lo)) >= 0 && mem[d] + m_w - m_b <= m_limit) c[n++] = {std::max(now, r), 0, 'B', lo};
+      if ((r = ready_f(hi)) >= 0 && mem[d] + m_b + reserve <= m_limit) c[n++] = {std::max(now, r), 1, 'F', hi};
+      if ((r = ready_f(lo)) >= 0 && mem[d] + 2 * m_b + reserve <= m_limit) c[n++] = {std::max(now, r), 2, 'F', lo};
+      if ((r = ready_b(hi)) >= 0 && mem[d] + m_w - m_b <= m_limit) c[n++] = {std::max(now, r), 3, 'B', hi};
+      if (wq_head[d] < (int)wq[d].size()) {
+        int64_t first = -1;
+        for (int i = 0; i < n; ++i) first = first < 0 ? c[i].st : std::min(first, c[i].st);
+        const bool full = n == 0 || mem[d] + m_b + reserve > m_limit;
+        if (full || first > now) c[n++] = {now, 4, 'W', wq[d][wq_head[d]].first};
+      }
+      for (int i = 0; i < n; ++i) {
+        const bool better = !have || c[i].st < best.st || (c[i].st == best.st && d < best_d) ||
+                            (c[i].st == best.st && d == best_d && c[i].rank < best.rank);
+        if (better) {
+          best = c[i];
+          best_d = d;
+          have = true;
+        }
+      }
+    }
+    if (!have) return set_error(ZB_E_DEADLOCK, "zb-v: no device can progress");
+    const int d = best_d;
+    int ch = best.chunk, j;
+    if (best.kind == 'F') {
+      j = nf[ch]++;
+      end_f[(size_t)ch * m + j] = best.st + t[0];
+      mem[d] += m_b;
+      freet[d] = best.st + t[0];
+    } else if (best.kind == 'B') {
+      j = nb[ch]++;
+      end_b[(size_t)ch * m + j] = best.st + t[1];
+      wq[d].push_back({ch, j});
+      mem[d] += m_w - m_b;
+      freet[d] = best.st + t[1];
+    } else {
+      ch = wq[d][wq_head[d]].first;
+      j = wq[d][wq_head[d]].second;
+      ++wq_head[d];
+      mem[d] -= m_w;
+      freet[d] = best.st + t[2];
+    }
+    ++count[d];
+    zb_op o;
+    o.stage = ch;
+    o.mb = j;
+    o.kind = best.kind;
+    ops.push_back(o);
+    start.push_back(best.st);
+  }
+  return ZB_OK;
+}
+
+}  // namespace
+
+extern "C" zb_status zb_schedule_zbv(int P, int m, const int64_t* times, int64_t t_comm, int64_t m_b, int64_t m_w,
+                                     int64_t m_limit, zb_op* linear_out, int cap, int* n_out,
+                                     zb_sim_stats* stats) {
+  clear_error();
+  if (!times || !linear_out || !n_out) return set_error(ZB_E_ARG, "null argument");
+  if (P < 1 || m < 1) return set_error(ZB_E_ARG, "P and m must be >= 1");
+  if ((int64_t)P * m > (1 << 23)) return set_error(ZB_E_ARG, "P * m too large");
+  if (times[0] < 1 || times[1] < 1 || times[2] < 1 || t_comm < 0)
+    return set_error(ZB_E_ARG, "times must be >= 1 and t_comm >= 0");
+  const int64_t reserve = std::max<int64_t>(0, m_w - m_b);
+  if (m_b < 0 || m_w < 0 || m_limit < 2 * m_b + reserve || m_limit < m_w)
+    return set_error(ZB_E_ARG, "M_limit %lld holds no microbatch through both chunks (M_B %lld, M_W %lld)",
+                     (long long)m_limit, (long long)m_b, (long long)m_w);
+  if (cap < 6 * P * m) return set_error(ZB_E_ARG, "cap %d < %d ops", cap, 6 * P * m);
+  std::vector<zb_op> ops;
+  std::vector<int64_t> start;
+  zb_status st = zbv_build(P, m, times, t_comm, m_b, m_w, m_limit, ops, start);
+  if (st != ZB_OK) return st;
+  // Linearize over the 2P chunk stages by start time, ties to the lower chunk.
+  std::vector<int> idx(ops.size());
+  for (size_t i = 0; i < idx.size(); ++i) idx[i] = (int)i;
+  std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) {
+    if (start[a] != start[b]) return start[a] < start[b];
+    return ops[a].stage < ops[b].stage;
+  });
+  for (size_t i = 0; i < idx.size(); ++i) linear_out[i] = ops[idx[i]];
+  *n_out = (int)ops.size();
+  if (stats) {
+    auto dur = [&](char k) { return k == 'F' ? times[0] : (k == 'B' ? times[1] : times[2]); };
+    std::vector<int64_t> first(P, -1), last(P, 0);
+    int64_t span = 0, busy = 0;
+    for (size_t i = 0; i < ops.size(); ++i) {
+      const int c = ops[i].stage, d = c < P ? c : 2 * P - 1 - c;
+      const int64_t e = start[i] + dur(ops[i].kind);
+      if (first[d] < 0 || start[i] < first[d]) first[d] = start[i];
+      last[d] = std::max(last[d], e);
+      span = std::max(span, e);
+      busy += dur(ops[i].kind);
+    }
+    int64_t mk = 0;
+    for (int d = 0; d < P; ++d) mk = std::max(mk, last[d] - first[d]);
+    stats->makespan = mk;
+    stats->span = span;
+    stats->busy = busy;
+    stats->ideal = 2LL * m * (times[0] + times[1] + times[2]);
+    stats->bubble = mk - stats->ideal;
+  }
+  return ZB_OK;
+}
+
 extern "C" zb_status zb_schedule_simulate_interleaved(int P, int m, int v, const int64_t* t,
                                                       zb_sim_stats* stats) {
   clear_error();

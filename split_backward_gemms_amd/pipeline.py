@@ -67,6 +67,19 @@ def heuristic_ops(handles: Sequence[int], n_stages: int, n_micro: int, times: Se
     return ops, stats, choice, m_limit
 
 
+def zbv_ops(handles: Sequence[int], n_micro: int, times: Sequence[int], t_comm: int = 0):
+    """ZB-V order for the 2P chunk stages behind `handles` (chunk c is stage c),
+    with the budget of P whole-stage microbatches per device: 2P chunk M_B plus
+    max(0, M_W - M_B) for the B in flight.  Returns (ops, stats, M_limit)."""
+    if len(handles) % 2:
+        raise ValueError("ZB-V needs an even number of chunk stages")
+    P = len(handles) // 2
+    m_b, m_w = stash_per_microbatch(handles)
+    m_limit = max(2 * P * m_b + max(0, m_w - m_b), 2 * m_b + max(0, m_w - m_b), m_w)
+    ops, stats = zb.zb_schedule_zbv(P, n_micro, times, m_b, m_w, m_limit, t_comm)
+    return ops, stats, m_limit
+
+
 class EmulatedPipeline:
     """P stages of one workload, each with its own weights, on one device."""
 

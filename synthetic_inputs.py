@@ -112,6 +112,14 @@ def reduced(w: Workload, hidden: int = 256, heads: int = 2, seq: int = 128,
                      n_layers=w.n_layers if n_layers is None else n_layers)
 
 
+def v_chunks(w: Workload) -> Workload:
+    """The same model cut for the V placement: 2P chunk stages of half a stage's
+    layers each (chunk c is stage c of a 2P-stage chain)."""
+    if w.n_layers % 2:
+        raise ValueError(f"{w.name}: {w.n_layers} layers per stage do not split into two chunks")
+    return w.replace(name=w.name + "_v", n_stages=2 * w.n_stages, n_layers=w.n_layers // 2)
+
+
 # ---------------------------------------------------------------------------
 # bf16 encoding (round to nearest even); pure data preparation.
 

@@ -17,7 +17,7 @@ import split_backward_gemms_amd as zb
 import synthetic_inputs as si
 from oracle import stage as ost
 from oracle import schedules as sch
-from split_backward_gemms_amd.pipeline import EmulatedPipeline, heuristic_ops, upload
+from split_backward_gemms_amd.pipeline import EmulatedPipeline, heuristic_ops, upload, zbv_ops
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -243,6 +243,39 @@ def test_heuristic_orders_match_oracle_and_1f1b_bits(name):
                     for nm in dw[s][l]:
                         assert np.array_equal(dw[s][l][nm].view(np.uint32), dw0[s][l][nm].view(np.uint32)), \
                             (budget, times, s, l, nm)
+    pipe.close()
+    ref = ost.pipeline(w, ws, xs, dys)
+    P = w.n_stages
+    errs = [_rel_err(y0[j], ref["y"][P - 1][j]) for j in range(w.n_micro)]
+    errs += [_rel_err(dx0[j], ref["dx"][0][j]) for j in range(w.n_micro)]
+    errs += [_rel_err(dw0[s][l][nm], ref["dw"][s][l][nm]) for s in range(P) for l in range(w.n_layers)
+             for nm in dw0[s][l]]
+    assert max(errs) <= TOL
+
+
+# ZB-V: the model cut into 2P chunk stages, run in the V order through the
+# executor: within the bound of the oracle on the same chunked model and, with
+# every chunk's W ascending, bit-identical to 1F1B over the chunk stages.
+@pytest.mark.parametrize("name", ["mlp_linears_ragged", "full_two_layers"])
+def test_zbv_order_matches_oracle_and_1f1b_bits(name):
+    base = REDUCED[name] if name in REDUCED else si.reduced(si.WORKLOADS["gpt_full_h4096"], hidden=256, heads=2,
+                                                             seq=128, n_micro=4, n_stages=2, n_layers=2)
+    w = si.v_chunks(base)
+    print(f"zb-v {name}: {w.n_stages} chunk stages x {w.n_layers} layers", flush=True)
+    ws, xs, dys = _inputs(w)
+    pipe = EmulatedPipeline(w, ws, ops=None, recompute_act=0)
+    _, y0, dx0, dw0, _ = _run(w, ws, xs, dys, "1f1b", pipe)
+    for times in ((1, 1, 1), (2, 3, 1), (9, 9, 5)):
+        ops, stats, m_limit = zbv_ops(pipe.handles, w.n_micro, times)
+        assert zb.zb_schedule_validate(w.n_stages, w.n_micro, ops) == (zb.ZB_OK, -1)
+        _, y, dx, dw, _ = _run(w, ws, xs, dys, ops, pipe)
+        for j in range(w.n_micro):
+            assert np.array_equal(y[j], y0[j]) and np.array_equal(dx[j], dx0[j]), (times, j)
+        for s in range(w.n_stages):
+            for l in range(w.n_layers):
+                for nm in dw[s][l]:
+                    assert np.array_equal(dw[s][l][nm].view(np.uint32), dw0[s][l][nm].view(np.uint32)), \
+                        (times, s, l, nm)
     pipe.close()
     ref = ost.pipeline(w, ws, xs, dys)
     P = w.n_stages

@@ -224,3 +224,29 @@ def test_heuristic_rejects_small_budget():
         zb.zb_schedule_heuristic(4, 8, (1, 1, 1), 2, 3, 2)
     with pytest.raises(zb.ZbError):
         zb.zb_schedule_heuristic(0, 8, (1, 1, 1), 2, 1, 8)
+
+
+# ------------------------------------------------------------------- ZB-V
+
+def test_zbv_matches_oracle():
+    from oracle import vshape as vs
+    rng = random.Random(13)
+    for _ in range(300):
+        P, m = rng.randint(1, 6), rng.randint(1, 12)
+        t = {"F": rng.randint(1, 5), "B": rng.randint(1, 6), "W": rng.randint(1, 4)}
+        m_b, m_w = rng.randint(1, 5), rng.randint(1, 5)
+        m_limit = max(m_w, rng.randint(2 * m_b + max(0, m_w - m_b), 3 * P * m_b + m_w))
+        comm = rng.choice([0, 0, 1, 2])
+        orders = vs.build(P, m, t, m_b, m_w, m_limit, comm)
+        sim = vs.simulate(P, orders, t, comm)
+        ops, st = zb.zb_schedule_zbv(P, m, (t["F"], t["B"], t["W"]), m_b, m_w, m_limit, comm)
+        assert ops == vs.linearize(orders, sim)
+        assert (st["makespan"], st["ideal"], st["bubble"]) == (sim.makespan, sim.ideal, sim.bubble)
+        assert zb.zb_schedule_validate(2 * P, m, ops) == (zb.ZB_OK, -1)
+
+
+def test_zbv_rejects_small_budget():
+    with pytest.raises(zb.ZbError):
+        zb.zb_schedule_zbv(4, 8, (1, 1, 1), 2, 3, 4)
+    with pytest.raises(zb.ZbError):
+        zb.zb_schedule_zbv(4, 8, (0, 1, 1), 1, 1, 8)
