@@ -8,6 +8,10 @@ and holds none of the method's arithmetic.
 
 * ``oracle.stage``     -- forward (F), input gradient (B), weight gradient (W)
                           and the fused (unsplit) backward of a stage, in fp64.
+* ``oracle.optim``     -- staged reduce of the gradient state, optimistic AdamW
+                          step, post-update validation and exact rollback.
+* ``oracle.heuristic`` -- the automatic (ZB-1p / ZB-2p) scheduler.
+* ``oracle.vshape``    -- the V placement and its list-scheduled order (ZB-V).
 * ``oracle.schedules`` -- per-stage pass orders (GPipe, 1F1B, ZB-H1, ZB-H2,
                           interleaved), the list-scheduling simulator, bubble
                           and memory accounting, the order validator and the
