@@ -101,6 +101,8 @@ def main() -> int:
     ap.add_argument("--order", default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--no-optim", action="store_true",
+                    help="skip timing the optimizer step with post-update validation")
     ap.add_argument("--mode", choices=["full", "kernels"], default="full",
                     help="kernels: only the one-stream kernel-timing phase (the phase a kernel profile covers)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -301,6 +303,36 @@ def main() -> int:
                 "ms_per_step": r["total_ms"] / prof_steps,
                 "tflops": r["flops"] / r["total_ms"] / 1e9} for r in kern]
 
+    # Optimizer step with post-update validation (outside the step above): the
+    # staged gradient-state reduce and optimistic AdamW of every stage, then the
+    # validation, once where nothing rolls back and once where every stage but
+    # the last must roll back and step again.
+    optim = None
+    n_params = sum(int(t.numel()) for ws_ in pipe.weights for t in ws_)
+    if a.mode == "full" and not a.no_optim and 12 * n_params * 1.25 < torch.cuda.mem_get_info()[0]:
+        def ev_ms(fn):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1)
+        res = {}
+        for name, max_norm in (("no_rollback", 1e30), ("rollback", 1e-30)):
+            pipe.optim_init(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=max_norm)
+            pipe.run(ops, X, DY, y, dx)
+            torch.cuda.synchronize()
+            step_ms = ev_ms(lambda: pipe.optim_step(1))
+            val_ms = ev_ms(lambda: pipe.optim_validate(1))
+            rolled = int(pipe.rolled.sum().item())
+            res[name] = {"step_ms": step_ms, "validate_ms": val_ms, "stages_rolled_back": rolled}
+        step_bytes = 30.0 * n_params if w.dtype == "bf16" else 32.0 * n_params
+        optim = {"params": n_params, "bytes_per_update": step_bytes, **res,
+                 "step_gbs": step_bytes / (res["no_rollback"]["step_ms"] / 1e3) / 1e9}
+        log(f"optimizer: {n_params / 1e6:.0f} M params, step {res['no_rollback']['step_ms']:.2f} ms "
+            f"({optim['step_gbs']:.0f} GB/s), validate {res['no_rollback']['validate_ms']:.3f} ms, "
+            f"with rollback {res['rollback']['validate_ms']:.2f} ms ({res['rollback']['stages_rolled_back']} stages)")
+
     pipe.close()
     out = {
         "metric": "stage F+B+W TFLOP/s",
@@ -330,6 +362,8 @@ def main() -> int:
         "kernels": kernels,
     }
     out.update(fused)
+    if optim:
+        out["optimizer"] = optim
     if heur:
         out["heuristic"] = heur
     if not a.no_cpu and a.mode == "full":

@@ -297,6 +297,57 @@ zb_status zb_backward_weight(zb_stage* st, int mb);
  * the same bits as B followed by W. */
 zb_status zb_backward_unsplit(zb_stage* st, int mb, const void* dy, void* dx);
 
+/* ------------------------------------------------------------------------
+ * Optimizer step with post-update validation (Zero Bubble Pipeline
+ * Parallelism, section 4 "the optimizer synchronization bypass", and its
+ * Appendix C in-place AdamW rollback).  A stage's gradient state is two
+ * doubles in device memory: {sum of the squares of every dW element, 1.0 if any
+ * dW element is NaN/Inf else 0.0}.  The clip coefficient of a state is
+ * min(1, max_grad_norm / (sqrt(sum) + 1e-6)) (1 when max_grad_norm <= 0); a
+ * state with the flag set means "no update".  AdamW step t (1-based), with
+ * g = coefficient * dW:
+ *   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+ *   p = p - lr wd p - lr (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps),
+ * and the working copy the GEMMs read is refreshed from p (bf16: rounded to
+ * nearest even). */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay;
+  float max_grad_norm; /* <= 0: no clipping */
+} zb_adamw;
+
+/* Give the stage its optimizer state: per linear (the zb_stage_create order)
+ * fp32 device buffers of K*N elements — master parameters, first and second
+ * moments — all caller-owned, 16-byte aligned, plus weights_rw: the same
+ * pointers as the stage's weights, which the step rewrites.  ZB_E_ARG on null
+ * or misaligned buffers, weights_rw[i] differing from the stage's weights, or
+ * hyperparameters outside lr >= 0, 0 <= beta < 1, eps >= 0, 0 <= lr*wd < 1. */
+zb_status zb_stage_optim_bind(zb_stage* st, const zb_adamw* hp, float* const* master, float* const* exp_avg,
+                              float* const* exp_avg_sq, void* const* weights_rw);
+
+/* Staged reduce: partial_out (device, 2 doubles) = upstream (device, the
+ * previous stage's partial; NULL on the first stage) + this stage's gradient
+ * state, on the stage's stream.  Needs a flushed step (zb_grad_flush) whose
+ * gradients have not been overwritten yet, else ZB_E_STATE.  Deterministic:
+ * fixed reduction order. */
+zb_status zb_stage_grad_state(zb_stage* st, const double* upstream, double* partial_out);
+
+/* Optimistic step number `step` (>= 1) with the state `used` (device, 2
+ * doubles; normally this stage's partial).  Same preconditions. */
+zb_status zb_stage_optim_step(zb_stage* st, int step, const double* used);
+
+/* Post-update validation of step `step`: when the step taken with `used`
+ * differs from the one `global` (device, the last stage's partial) calls for —
+ * another clip coefficient or another skip decision — roll it back in place
+ * and step again with `global`.  *rolled_back (device int, may be NULL) = 1 if
+ * it did, else 0.  The decision is taken on the device; nothing synchronises.
+ * Must run before this stage's first W of the next step overwrites dW, else
+ * ZB_E_STATE. */
+zb_status zb_stage_optim_validate(zb_stage* st, int step, const double* used, const double* global,
+                                  int* rolled_back);
+
+/* Undo step `step` taken with `used` (the inverse update alone). */
+zb_status zb_stage_optim_rollback(zb_stage* st, int step, const double* used);
+
 /* Step boundary (the optimizer dependency): requires W (or U) of every
  * microbatch of the step, else ZB_E_MISSING.  If nonfinite_out (host) is not
  * NULL, synchronises the stream and stores 1 if any dW holds a NaN or Inf, else

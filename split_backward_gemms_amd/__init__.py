@@ -39,6 +39,11 @@ class ZbError(RuntimeError):
 
 # ---------------------------------------------------------------- C structs
 
+class zb_adamw(C.Structure):
+    _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
+                ("weight_decay", C.c_float), ("max_grad_norm", C.c_float)]
+
+
 class zb_stage_desc(C.Structure):
     _fields_ = [("kind", C.c_int), ("dtype", C.c_int), ("n_layers", C.c_int), ("hidden", C.c_int),
                 ("ffn", C.c_int), ("n_heads", C.c_int), ("seq", C.c_int), ("micro_batch", C.c_int),
@@ -118,6 +123,12 @@ def lib():
             "zb_backward_weight": (I, [P, I]),
             "zb_backward_unsplit": (I, [P, I, P, P]),
             "zb_grad_flush": (I, [P, C.POINTER(I)]),
+            "zb_stage_optim_bind": (I, [P, C.POINTER(zb_adamw), C.POINTER(P), C.POINTER(P), C.POINTER(P),
+                                        C.POINTER(P)]),
+            "zb_stage_grad_state": (I, [P, P, P]),
+            "zb_stage_optim_step": (I, [P, I, P]),
+            "zb_stage_optim_validate": (I, [P, I, P, P, P]),
+            "zb_stage_optim_rollback": (I, [P, I, P]),
             "zb_run_schedule": (I, [C.POINTER(P), I, op_p, I, C.POINTER(P), C.POINTER(P), C.POINTER(P),
                                     C.POINTER(P), C.POINTER(zb_trace_rec)]),
             "zb_last_error": (C.c_char_p, []),
@@ -145,6 +156,8 @@ def exported_symbols() -> List[str]:
             "zb_events_inspect", "zb_stage_create", "zb_stage_class_bytes", "zb_stage_workspace_bytes",
             "zb_stage_bind_workspace", "zb_stage_input_slot", "zb_stage_grad_slot", "zb_forward",
             "zb_backward_input", "zb_backward_weight", "zb_backward_unsplit", "zb_grad_flush",
+            "zb_stage_optim_bind", "zb_stage_grad_state", "zb_stage_optim_step", "zb_stage_optim_validate",
+            "zb_stage_optim_rollback",
             "zb_run_schedule", "zb_last_error", "zb_stage_destroy", "zb_prof_enable", "zb_prof_reset",
             "zb_prof_read", "zb_version", "zb_linear_forward", "zb_linear_backward_input",
             "zb_linear_backward_weight"]
@@ -364,6 +377,30 @@ def zb_grad_flush(stage: int, check_finite: bool = False) -> Optional[int]:
         return flag.value
     _check(lib().zb_grad_flush(stage, None))
     return None
+
+
+def zb_stage_optim_bind(stage: int, hp: "zb_adamw", master: Sequence, exp_avg: Sequence, exp_avg_sq: Sequence,
+                        weights_rw: Sequence) -> None:
+    def arr(xs):
+        return (C.c_void_p * len(xs))(*[_ptr(x) for x in xs])
+    _check(lib().zb_stage_optim_bind(stage, C.byref(hp), arr(master), arr(exp_avg), arr(exp_avg_sq),
+                                     arr(weights_rw)))
+
+
+def zb_stage_grad_state(stage: int, upstream, partial_out) -> None:
+    _check(lib().zb_stage_grad_state(stage, _ptr(upstream), _ptr(partial_out)))
+
+
+def zb_stage_optim_step(stage: int, step: int, used) -> None:
+    _check(lib().zb_stage_optim_step(stage, step, _ptr(used)))
+
+
+def zb_stage_optim_validate(stage: int, step: int, used, glob, rolled_back=None) -> None:
+    _check(lib().zb_stage_optim_validate(stage, step, _ptr(used), _ptr(glob), _ptr(rolled_back)))
+
+
+def zb_stage_optim_rollback(stage: int, step: int, used) -> None:
+    _check(lib().zb_stage_optim_rollback(stage, step, _ptr(used)))
 
 
 def zb_run_schedule(stages: Sequence[int], ops: Sequence[Op], x0: Sequence, dy_last: Sequence,

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -219,6 +220,7 @@ struct zb_stage {
   size_t scratch_do = 0, scratch_flag = 0, scratch_dsum = 0;
   size_t scratch_act = 0, act_bytes = 0;  // A = gelu(Z) per layer: forward hand-off, W operand
   size_t scratch_part = 0, part_bytes = 0;  // split-K arena of the F/B GEMMs
+  size_t scratch_opt = 0;                   // per-workgroup partial gradient states
   // plan
   bool planned = false;
   int plan_fw = 0, plan_fb = 0, plan_bw = 0;
@@ -231,6 +233,11 @@ struct zb_stage {
   // per microbatch
   std::vector<int> st, s_fw, s_fb, s_bw;
   int w_count = 0;
+  bool grads_ready = false;  // a flushed step's dW, not yet overwritten by the next step's first W
+  // optimizer state (zb_stage_optim_bind)
+  bool opt_bound = false;
+  zb_adamw opt{};
+  std::vector<float*> opt_p, opt_m, opt_v;
   // multi-stream schedules: stages on different streams
   bool multi = false;
   std::vector<hipEvent_t> f_done, b_done;  // per microbatch, created on first use
@@ -307,6 +314,8 @@ void compute_layout(zb_stage* S) {
   S->scratch_part = sc;
   S->part_bytes = part;
   sc += align_up(part);
+  S->scratch_opt = sc;
+  sc += align_up((size_t)S->L * S->nlin * kSumsqBlocks * 2 * sizeof(double));
   S->scratch_bytes = sc;
   S->fw.bytes = fw;
   S->fb.bytes = fb;
@@ -671,6 +680,7 @@ zb_status do_backward(zb_stage* S, int mb, const void* dy, void* dx, bool unspli
     ZB_TRY(release_all(S, mb));
     S->st[mb] = MB_DONE;
     S->w_count += 1;
+    S->grads_ready = false;
   } else {
     S->st[mb] = MB_B;
   }
@@ -685,6 +695,7 @@ zb_status do_weight(zb_stage* S, int mb) {
   ZB_TRY(release_all(S, mb));
   S->st[mb] = MB_DONE;
   S->w_count += 1;
+  S->grads_ready = false;
   return ZB_OK;
 }
 
@@ -869,7 +880,104 @@ extern "C" zb_status zb_grad_flush(zb_stage* S, int* nonfinite_out) {
   }
   std::fill(S->st.begin(), S->st.end(), (int)MB_IDLE);
   S->w_count = 0;
+  S->grads_ready = true;
   return ZB_OK;
+}
+
+// ------------------------------------------------------------ optimizer
+
+extern "C" zb_status zb_stage_optim_bind(zb_stage* S, const zb_adamw* hp, float* const* master,
+                                         float* const* exp_avg, float* const* exp_avg_sq,
+                                         void* const* weights_rw) {
+  clear_error();
+  if (!S || !hp || !master || !exp_avg || !exp_avg_sq || !weights_rw) return set_error(ZB_E_ARG, "null argument");
+  if (!(hp->lr >= 0.0f) || !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f) ||
+      !(hp->eps >= 0.0f) || !(hp->weight_decay >= 0.0f) || !(hp->lr * hp->weight_decay < 1.0f))
+    return set_error(ZB_E_ARG, "AdamW hyperparameters outside lr >= 0, 0 <= beta < 1, eps >= 0, 0 <= lr*wd < 1");
+  if (hp->beta1 == 0.0f || hp->beta2 == 0.0f)
+    return set_error(ZB_E_ARG, "beta1 and beta2 must be > 0 for the step to be invertible");
+  const int nw = (int)S->w.size();
+  for (int i = 0; i < nw; ++i) {
+    const void* bufs[4] = {master[i], exp_avg[i], exp_avg_sq[i], weights_rw[i]};
+    for (const void* b : bufs)
+      if (!b || (reinterpret_cast<uintptr_t>(b) & 15))
+        return set_error(ZB_E_ARG, "linear %d: optimizer buffers must be non-null and 16-byte aligned", i);
+    if (weights_rw[i] != S->w[i])
+      return set_error(ZB_E_ARG, "linear %d: weights_rw must be the stage's own weight buffer", i);
+  }
+  S->opt = *hp;
+  S->opt_p.assign(master, master + nw);
+  S->opt_m.assign(exp_avg, exp_avg + nw);
+  S->opt_v.assign(exp_avg_sq, exp_avg_sq + nw);
+  S->opt_bound = true;
+  return ZB_OK;
+}
+
+namespace {
+zb_status optim_ready(const zb_stage* S, bool need_opt) {
+  if (!S) return set_error(ZB_E_ARG, "null stage");
+  if (!S->bound) return set_error(ZB_E_STATE, "stage %d: no workspace", S->index);
+  if (need_opt && !S->opt_bound) return set_error(ZB_E_STATE, "stage %d: no optimizer state bound", S->index);
+  if (!S->grads_ready)
+    return set_error(ZB_E_STATE, "stage %d: no flushed step gradients (flush first; a W of the next step "
+                     "overwrites them)", S->index);
+  return ZB_OK;
+}
+
+zb_status optim_launch(zb_stage* S, int mode, int step, const double* used, const double* glob, int* rolled) {
+  if (step < 1) return set_error(ZB_E_ARG, "step must be >= 1");
+  if (!used || (mode == 1 && !glob)) return set_error(ZB_E_ARG, "null state");
+  ZB_TRY(optim_ready(S, true));
+  for (size_t i = 0; i < S->w.size(); ++i) {
+    AdamwLaunch L;
+    L.theta = S->opt_p[i];
+    L.m = S->opt_m[i];
+    L.v = S->opt_v[i];
+    L.g = S->dw[i];
+    L.w = const_cast<void*>(S->w[i]);
+    L.w_bf16 = S->d.dtype == ZB_DTYPE_BF16;
+    L.n = S->wK[i] * S->wN[i];
+    L.hp = S->opt;
+    L.bc1 = 1.0 - std::pow((double)S->opt.beta1, step);
+    L.bc2 = 1.0 - std::pow((double)S->opt.beta2, step);
+    L.used = used;
+    L.glob = glob;
+    L.mode = mode;
+    L.rolled = rolled;
+    ZB_TRY(launch_adamw(L, S->stream));
+  }
+  return ZB_OK;
+}
+}  // namespace
+
+extern "C" zb_status zb_stage_grad_state(zb_stage* S, const double* upstream, double* partial_out) {
+  clear_error();
+  if (!partial_out) return set_error(ZB_E_ARG, "null partial_out");
+  ZB_TRY(optim_ready(S, false));
+  double* part = reinterpret_cast<double*>(S->scratch + S->scratch_opt);
+  int count = 0;
+  for (size_t i = 0; i < S->w.size(); ++i) {
+    int blocks = 0;
+    ZB_TRY(launch_grad_sumsq(S->dw[i], S->wK[i] * S->wN[i], part + 2 * count, &blocks, S->stream));
+    count += blocks;
+  }
+  return launch_state_combine(part, count, upstream, partial_out, S->stream);
+}
+
+extern "C" zb_status zb_stage_optim_step(zb_stage* S, int step, const double* used) {
+  clear_error();
+  return optim_launch(S, 0, step, used, nullptr, nullptr);
+}
+
+extern "C" zb_status zb_stage_optim_validate(zb_stage* S, int step, const double* used, const double* global,
+                                             int* rolled_back) {
+  clear_error();
+  return optim_launch(S, 1, step, used, global, rolled_back);
+}
+
+extern "C" zb_status zb_stage_optim_rollback(zb_stage* S, int step, const double* used) {
+  clear_error();
+  return optim_launch(S, 2, step, used, nullptr, nullptr);
 }
 
 namespace {

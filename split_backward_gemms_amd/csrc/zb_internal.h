@@ -102,6 +102,31 @@ zb_status launch_zero_int(int* flag, hipStream_t s);
 // the MLP activation rebuilt from the stored pre-activation.
 zb_status launch_gelu(const void* z, void* a, int64_t n, int dtype, int kind, hipStream_t s);
 
+// ------------------------------------------------ optimizer (section 4)
+// Workgroups of the sum-of-squares pass per gradient tensor (one fp64 pair each).
+constexpr int kSumsqBlocks = 1024;
+// part[2i], part[2i+1] = sum of squares, count of NaN/Inf over workgroup i's
+// share of g[0..n); *blocks_out = the number of pairs written.
+zb_status launch_grad_sumsq(const float* g, int64_t n, double* part, int* blocks_out, hipStream_t s);
+// out[0..1] = up[0..1] (may be null) + the sum of `count` pairs (flag as 0/1).
+zb_status launch_state_combine(const double* part, int count, const double* up, double* out, hipStream_t s);
+struct AdamwLaunch {
+  float* theta = nullptr;
+  float* m = nullptr;
+  float* v = nullptr;
+  const float* g = nullptr;
+  void* w = nullptr;          // working copy of the parameters the GEMMs read
+  int w_bf16 = 1;
+  int64_t n = 0;
+  zb_adamw hp{};
+  double bc1 = 1.0, bc2 = 1.0;  // 1 - beta^step
+  const double* used = nullptr;  // device state the step is (was) taken with
+  const double* glob = nullptr;  // device global state (validation)
+  int mode = 0;                  // 0 step, 1 validate, 2 rollback
+  int* rolled = nullptr;         // validation: device int, 1 if rolled back
+};
+zb_status launch_adamw(const AdamwLaunch& L, hipStream_t s);
+
 // --------------------------------------------------------- kernel timing
 bool prof_on();
 struct ProfScope {

@@ -165,6 +165,45 @@ class EmulatedPipeline:
                 cur.wait_stream(st)
         return tr, flags
 
+    # ---------------------------------------------------------- optimizer
+
+    def optim_init(self, **hp) -> None:
+        """fp32 master parameters (an exact copy of the working weights), zero
+        moments, bound to every stage.  hp: lr, beta1, beta2, eps, weight_decay,
+        max_grad_norm."""
+        self.hp = zb.zb_adamw(**hp)
+        self.master = [[w.detach().to(torch.float32, copy=True) for w in ws] for ws in self.weights]
+        self.exp_avg = [[torch.zeros_like(p) for p in ps] for ps in self.master]
+        self.exp_avg_sq = [[torch.zeros_like(p) for p in ps] for ps in self.master]
+        for s, h in enumerate(self.handles):
+            zb.zb_stage_optim_bind(h, self.hp, self.master[s], self.exp_avg[s], self.exp_avg_sq[s], self.weights[s])
+        self.opt_state = torch.zeros((self.P, 2), dtype=torch.float64, device=self.device)
+        self.rolled = torch.zeros(self.P, dtype=torch.int32, device=self.device)
+
+    def optim_step(self, step: int) -> None:
+        """Staged reduce of the gradient state, stage 0 first, each stage stepping
+        with its partial state as soon as it has it."""
+        cur = torch.cuda.current_stream(self.device)
+        for s, h in enumerate(self.handles):
+            self.streams[s].wait_stream(cur if s == 0 else self.streams[s - 1])
+            zb.zb_stage_grad_state(h, None if s == 0 else self.opt_state[s - 1], self.opt_state[s])
+            zb.zb_stage_optim_step(h, step, self.opt_state[s])
+        for st in {id(x): x for x in self.streams}.values():
+            cur.wait_stream(st)
+
+    def optim_validate(self, step: int) -> torch.Tensor:
+        """Post-update validation: the global state (the last stage's) travels
+        back stage by stage; returns the device flags of the stages that rolled
+        back and stepped again."""
+        cur = torch.cuda.current_stream(self.device)
+        for s in reversed(range(self.P)):
+            self.streams[s].wait_stream(cur if s == self.P - 1 else self.streams[s + 1])
+            zb.zb_stage_optim_validate(self.handles[s], step, self.opt_state[s], self.opt_state[self.P - 1],
+                                       self.rolled[s:s + 1])
+        for st in {id(x): x for x in self.streams}.values():
+            cur.wait_stream(st)
+        return self.rolled
+
     def grads_host(self) -> List[List[Dict[str, np.ndarray]]]:
         names = [nm for nm, _, _ in self.w.linears()]
         out = []
