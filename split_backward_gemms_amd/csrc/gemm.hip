@@ -11,18 +11,22 @@
 //
 // bf16 path: 256 threads = 4 waves of 64 in a 2x2 grid; each wave owns a
 // (BM/2)x(BN/2) block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, fp32
-// accumulators).  K advances 64 at a time through two LDS buffers: the next
-// tile is fetched into registers while the current one feeds the MFMAs.  In
-// LDS every tile is stored k-contiguous ([row][64]) with its 16-byte chunks
-// XOR-swizzled by (row ^ row>>3) & 7, so both the MFMA operand reads and the
-// transposing writes of m/n-contiguous operands are free of bank conflicts.
-// m/n-contiguous operands (W's X and dY, F's weight) are loaded as 8x8 (or
-// 4x8) bf16 blocks with 16-byte global loads and transposed in registers.
+// accumulators).  K advances 64 at a time through a ring of 2 to 4 LDS stages
+// that global->LDS copies (buffer_load ... lds, 16 bytes per lane, hardware
+// range checks in place of bounds branches) keep filled ahead of the MFMAs;
+// every wait for them is an explicit vmcnt wait plus a barrier.  k-contiguous
+// operands sit in LDS as [rows][64] with 16-byte chunks XOR-ed by
+// (row ^ row/8) & 7 and are read 16 bytes at a time; m/n-contiguous operands
+// (F's weight, W's X and dY) stay untransposed as [64][rows] with chunks XOR-ed
+// by 4 (k % 4) and are read with the transposing ds_read_b64_tr_b16.
 //
-// The W epilogue is fused: the accumulators start from the fp32 gradient
-// buffer (or from zero for the first W of a step) and the MFMA chain simply
-// continues, so W of microbatches j, j+1, ... run in any slot give the same
-// bits as long as they are applied in the same order.  No split-K, no atomics.
+// Epilogues: bf16 store, residual add, GeLU (pre-activation stored beside),
+// GeLU' of a saved pre-activation, with lanes l and l+32 swapping halves so
+// every store is 16 bytes; W: dW = (first W of the step ? 0 : dW) + acc in
+// fp32 after the k loop, so W of microbatches j, j+1, ... give the same bits in
+// any slots as long as they run in the same order.  F and B may split K in
+// two or four: the splits write fp32 partials and a second kernel adds them in
+// split order (deterministic).  No atomics.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -533,25 +537,41 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), prsrc, (int)off, 0, 0);
         }
   } else if constexpr (EPI == EPI_ACC) {
-    // dW (+)= this GEMM's sum over k, in fp32.
+    // dW (+)= this GEMM's sum over k, in fp32.  The old values of one row of
+    // 32x32 blocks (TN * 4 16-byte loads per lane) are all requested before the
+    // first add, so the loads overlap instead of each waiting out its latency.
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) {
+      uint32_t off[TN][4];
+      f32x4 c[TN][4];
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int m = em + i * 32, n = en + j * 32 + 8 * g;
-          const uint32_t off = (m < p.M && n < p.N) ? (uint32_t)(((int64_t)m * p.ldc + n) * 4) : kOOB;
+          off[j][g] = (m < p.M && n < p.N) ? (uint32_t)(((int64_t)m * p.ldc + n) * 4) : kOOB;
+        }
+      if (p.beta) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            c[j][g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(crsrc, (int)off[j][g], 0, 0));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
           f32x4 v;
 #pragma unroll
           for (int t2 = 0; t2 < 4; ++t2) v[t2] = acc[i][j][4 * g + t2];
           if (p.beta) {
-            const f32x4 c = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(crsrc, (int)off, 0, 0));
 #pragma unroll
-            for (int t2 = 0; t2 < 4; ++t2) v[t2] = c[t2] + v[t2];
+            for (int t2 = 0; t2 < 4; ++t2) v[t2] = c[j][g][t2] + v[t2];
           }
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), crsrc, (int)off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), crsrc, (int)off[j][g], 0, 0);
         }
+    }
   } else {
     __amdgpu_buffer_rsrc_t rrsrc = make_rsrc(EPI == EPI_RESID || EPI == EPI_DGELU ? p.R : p.C,
                                              (uint32_t)(((int64_t)(p.M - 1) * p.ldr + p.N) * 2));
@@ -854,6 +874,8 @@ zb_status launch_gemm_w_group(const GemmDesc* gs, int n, hipStream_t s) {
       bytes += 2.0 * ((double)g.M * g.K + (double)g.K * g.N) + (g.beta ? 8.0 : 4.0) * g.M * g.N;
     }
     if (gp.n == 0) continue;
+    // 256x256 tiles, one workgroup per CU: measured against 128x128 tiles two
+    // to a CU in one process, it is faster at every size here (T = 1024 to 4096).
     ProfScope ps("gemm_w_group_256x256", flops, bytes, s);
     launch_w_group<256, 256>(gp, s);
     ZB_HIP_CHECK(hipGetLastError());
