@@ -39,8 +39,15 @@
 namespace zb {
 namespace {
 
+using dev::dma16;
 using dev::gelu_f;
 using dev::gelu_grad_f;
+using dev::kOOB;
+using dev::kRsrcWord3;
+using dev::lds_addr;
+using dev::make_rsrc4;
+using dev::pack_bf16x2;
+using dev::wait_vm_barrier;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -78,14 +85,6 @@ struct Params {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Round to nearest even, two at a time (v_cvt_pk_bf16_f32); NaN stays NaN.
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const f32x2 v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)pack_bf16x2(f, 0.0f); }
 
 template <typename T>
@@ -154,50 +153,18 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn, i
 // Global memory is read and written through buffer resources: an access whose
 // byte offset is at or past the operand's extent returns zero (loads) or is
 // dropped (stores).  Lanes outside the matrix get an offset of kOOB, so edge
-// tiles need no branches.  Every operand extent is below 2 GiB (checked on the
-// host), so kOOB plus any in-range step stays out of range without wrapping.
-constexpr uint32_t kOOB = 0x80000000u;
-constexpr int kRsrcWord3 = 0x00020000;
+// tiles need no branches.
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t extent_bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)extent_bytes, kRsrcWord3);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)extent_bytes, (int)kRsrcWord3);
 }
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// Global -> LDS copies are issued with inline assembly, so the compiler does
-// not track them: every wait for them is explicit.  WAIT_VM_BARRIER<N> lets
-// at most N of this wave's copies stay in flight, drains its LDS reads, and
-// meets the other waves at the barrier; after it, the copies each wave had
-// issued before its last N are visible to all.  The memory clobbers keep the
-// compiler from moving LDS reads across either statement.
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-// Buffer descriptor (gfx9): 48-bit base, stride 0, extent in bytes, raw
-// addressing with range checking against the extent.
-__device__ __forceinline__ u32x4 make_rsrc4(const void* base, uint32_t extent_bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  u32x4 r;
-  r[0] = (uint32_t)b;
-  r[1] = (uint32_t)(b >> 32) & 0xffffu;
-  r[2] = extent_bytes;
-  r[3] = (uint32_t)kRsrcWord3;
-  return r;
-}
-
-// 16 bytes per lane from rsrc at byte offset off (zero when out of range)
-// into LDS at lds + 16 * lane.  lds must be wave-uniform.
-__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t lds, uint32_t off) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc), "{m0}"(lds) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
-}
+// Global -> LDS copies (dev::dma16) are issued with inline assembly, so the
+// compiler does not track them: every wait for them is explicit
+// (dev::wait_vm_barrier), and its memory clobber keeps LDS reads from moving
+// across it.
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;

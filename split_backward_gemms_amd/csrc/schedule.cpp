@@ -1,12 +1,14 @@
 // Schedule layer: per-stage pass orders, ASAP simulation, one-device
-// linearization, order validation, the activation-memory ledger and the
-// timed-event inspector.  Host code only.
+// linearization, order validation, the activation-memory ledger, the
+// timed-event inspector, the automatic (ZB-1p / ZB-2p) scheduler and the
+// V-placement order (ZB-V).  Host code only.
 //
 // Sources: "Zero Bubble Pipeline Parallelism" section 3 (ZB-H1, ZB-H2, the
 // memory model, ILP appendix Eq. 3-7) and section 5 (bubble rate); the
 // tutorial "Pipeline Schedules: GPipe, 1F1B and Zero Bubble" (1F1B warm-up
 // P-1-p, interleaved stages); the audit "Zero-Bubble Pipeline Parallelism,
-// Proven", section "Validate the schedule as data".
+// Proven", section "Validate the schedule as data".  The automatic scheduler
+// follows section 3.1 of the first page, ZB-V its section 6.
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
