@@ -279,12 +279,19 @@ template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(OCC, OCC)))
 gemm_bf16_mfma_group(GroupParams gp) {
   ZB_GEMM_LDS(BM, BN, OCC);
-  int b = blockIdx.x;
   const int total = gp.tile_start[gp.n];
-  if (total % XCDS == 0) b = (b % XCDS) * (total / XCDS) + b / XCDS;  // one XCD works a GEMM's neighbours
-  int g = 0;
-  while (g + 1 < gp.n && b >= gp.tile_start[g + 1]) ++g;
-  gemm_tile<BM, BN, AK, BKC, EPI, OCC>(gp.p[g], b - gp.tile_start[g], 0, s0, s1, s2, s3);
+  // Persistent when the grid is smaller than the tile count: workgroup w takes
+  // tiles w, w + grid, ...; the barrier keeps the next tile's copies out of the
+  // ring until every wave is past the last one.  The grid is a multiple of the
+  // XCD count, so a workgroup's tiles stay on its XCD.
+  for (int b0 = blockIdx.x; b0 < total; b0 += gridDim.x) {
+    if (b0 != (int)blockIdx.x) __syncthreads();
+    int b = b0;
+    if (total % XCDS == 0) b = (b % XCDS) * (total / XCDS) + b / XCDS;  // one XCD works a GEMM's neighbours
+    int g = 0;
+    while (g + 1 < gp.n && b >= gp.tile_start[g + 1]) ++g;
+    gemm_tile<BM, BN, AK, BKC, EPI, OCC>(gp.p[g], b - gp.tile_start[g], 0, s0, s1, s2, s3);
+  }
 }
 
 // 32x16 bf16 MFMA operand (lane l: row l % 32, k = 8 (l / 32) .. +7) read
@@ -767,6 +774,19 @@ void launch_mfma(Params p, hipStream_t s) {
   hipLaunchKernelGGL((gemm_bf16_mfma<BM, BN, AK, BKC, EPI>), dim3(p.nbm * p.nbn * p.splits), dim3(NT), 0, s, p);
 }
 
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < XCDS) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int BM, int BN, int OCC = 1>
 void launch_w_group(GroupParams gp, hipStream_t s) {
   int total = 0;
@@ -780,7 +800,10 @@ void launch_w_group(GroupParams gp, hipStream_t s) {
     total += gp.p[g].nbm * gp.p[g].nbn;
   }
   gp.tile_start[gp.n] = total;
-  hipLaunchKernelGGL((gemm_bf16_mfma_group<BM, BN, false, false, EPI_ACC, OCC>), dim3(total), dim3(NT), 0, s, gp);
+  // One workgroup per CU (OCC per CU), each looping over its tiles: measured
+  // 3-4% faster than one workgroup per tile for the grouped W launch.
+  const int grid = std::min(total, cu_count() / XCDS * XCDS * OCC);
+  hipLaunchKernelGGL((gemm_bf16_mfma_group<BM, BN, false, false, EPI_ACC, OCC>), dim3(grid), dim3(NT), 0, s, gp);
 }
 
 template <bool AK, bool BKC, int EPI>
