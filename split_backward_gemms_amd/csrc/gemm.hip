@@ -176,7 +176,8 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 //   KCONTIG:   LDS [ROWS][64] bf16; chunk c (8 k values) of row r sits at
 //              position c ^ swz(r) of its 128-byte row.
 //   otherwise: LDS [64][ROWS] bf16; chunk c (8 m values) of k-row k sits at
-//              position c ^ 4 (k % 4) of its 2 ROWS-byte row.
+//              position c ^ 4 (k % 4) of its 2 ROWS-byte row (c ^ 4 (k % 2) when
+//              ROWS = 64).
 // The four waves of the workgroup each move a quarter of the tile.
 template <int ROWS, bool KCONTIG>
 struct DmaLoader {
@@ -203,13 +204,14 @@ struct DmaLoader {
       }
     } else {
       constexpr int CH = ROWS / 8;  // 16-byte chunks per k-row
+      constexpr int XM = ROWS >= 128 ? 3 : 1;  // 32-column blocks swapped by k % 4 (k % 2 at 64 rows)
       rsrc = make_rsrc4(base, (uint32_t)(((int64_t)(K - 1) * ld + rows_lim) * 2));
       kstep = (uint32_t)(ld * 2);
 #pragma unroll
       for (int q = 0; q < NI; ++q) {
         const int L = (wave * NI + q) * 64 + lane;
         const int k = L / CH;
-        const int c = (L % CH) ^ (4 * (k & 3));
+        const int c = (L % CH) ^ (4 * (k & XM));
         const int gm = row0 + 8 * c;
         voff[q] = gm < rows_lim ? (uint32_t)(((int64_t)k * ld + gm) * 2) : kOOB;
       }
@@ -356,10 +358,13 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
 
   // Fragment read offsets within an operand tile.
   //  k-contiguous: row = base + 32 i + lane % 32, chunk = 2 kk + lane / 32,
-  //    stored at P ^ 2 (kk ^ 2 (i % 2)) with P fixed per lane: ra[kk ^ 2 (i % 2)] + 4096 i.
+  //    stored at P ^ 2 (kk ^ 2 (i % 2)) with P fixed per lane: ra[kk ^ 2 (i % 2)] + 4096 i
+  //    (P takes bit 5 of the wave's first row, set when a wave holds an odd number of
+  //    32-row blocks, as in a 64-wide tile).
   //  m/n-contiguous (transposing reads): lane l = 16 g + ii reads k-row
   //    16 kk + 8 (g / 2) + 4 h + ii / 4 at column base + 32 i + 16 (g % 2) + 4 (ii % 4);
-  //    with r = ii / 4 = k % 4 the chunk's position is ((base / 32 + i) ^ r) * 4 + s.
+  //    with r = ii / 4 = k % 4 the chunk's position is ((base / 32 + i) ^ r) * 4 + s (r % 2 in a
+  //    64-wide tile, which has two 32-column blocks).
   uint32_t ra[4], rb[4];
   {
     const int P = (lane >> 5) ^ (lane & 7) ^ ((lane >> 3) & 3);
@@ -368,16 +373,16 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if constexpr (AK) {
-        ra[q] = (wm * WTM + (lane & 31)) * 128 + ((P ^ (2 * q)) << 4);
+        ra[q] = (wm * WTM + (lane & 31)) * 128 + ((P ^ (2 * q) ^ (4 * ((wm * TM) & 1))) << 4);
       } else {
         const int blk = wm * WTM / 32 + q;
-        ra[q] = (8 * (g >> 1) + r) * (BM * 2) + 64 * (blk ^ r) + 16 * s + 8 * (ii & 1);
+        ra[q] = (8 * (g >> 1) + r) * (BM * 2) + 64 * (blk ^ (r & (BM >= 128 ? 3 : 1))) + 16 * s + 8 * (ii & 1);
       }
       if constexpr (BKC) {
-        rb[q] = (wn * WTN + (lane & 31)) * 128 + ((P ^ (2 * q)) << 4);
+        rb[q] = (wn * WTN + (lane & 31)) * 128 + ((P ^ (2 * q) ^ (4 * ((wn * TN) & 1))) << 4);
       } else {
         const int blk = wn * WTN / 32 + q;
-        rb[q] = (8 * (g >> 1) + r) * (BN * 2) + 64 * (blk ^ r) + 16 * s + 8 * (ii & 1);
+        rb[q] = (8 * (g >> 1) + r) * (BN * 2) + 64 * (blk ^ (r & (BN >= 128 ? 3 : 1))) + 16 * s + 8 * (ii & 1);
       }
     }
   }
@@ -726,7 +731,13 @@ struct TileCfg {
   int bm, bn;
   double rate;  // FLOP per microsecond of one workgroup with every CU busy (measured, MI355X)
 };
-constexpr TileCfg kTiles[] = {{256, 256, 5.4e6}, {256, 128, 4.75e6}, {128, 128, 4.1e6}};
+// The 128x64 rate is the one seen with operands that start outside the caches,
+// as in a pipeline whose other passes evict them: it moves 1.5x the bytes per
+// FLOP of 128x128 into LDS and loses more than the wider tiles when it
+// misses (1024x2048x8192: 3.4e6 warm, about 2.2e6 cold).  Its place is short
+// k loops on few output tiles, where it fills the chip without a split-K pass.
+constexpr TileCfg kTiles[] = {{256, 256, 5.4e6}, {256, 128, 4.75e6}, {128, 128, 4.1e6}, {128, 64, 2.4e6}};
+constexpr int kNarrowTile = 3;  // 128x64: F and B layouts only
 constexpr int kCUs = 256;
 constexpr double kFixedUs = 2.0;        // per workgroup: first copies in, epilogue out
 constexpr double kReduceFixedUs = 3.0;  // split-K: the second launch
@@ -742,12 +753,14 @@ struct GemmPlan {
 // of workgroups over the CUs, each taking its k tiles at the shape's rate plus
 // a fixed overhead; a split adds the pass that reads the fp32 partials back.
 // Splitting is only considered while the tiles alone leave CUs idle, and only
-// when the partials fit in `arena` bytes.
-GemmPlan plan_gemm(int M, int N, int K, bool can_split, size_t arena) {
+// when the partials fit in `arena` bytes.  The narrow 128x64 tile fills the
+// chip without a split where 128x128 tiles would leave CUs idle (T = 1024
+// token products with N = 2048: 256 workgroups instead of 128).
+GemmPlan plan_gemm(int M, int N, int K, bool can_split, size_t arena, bool narrow_ok) {
   const int nk = (K + BKT - 1) / BKT;
   GemmPlan best;
   best.kts = nk;
-  for (int t = 0; t < 3; ++t) {
+  for (int t = 0; t < (narrow_ok ? 4 : 3); ++t) {
     const TileCfg& c = kTiles[t];
     const int nb = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
     for (int S = 1; S <= 4; S *= 2) {
@@ -819,6 +832,12 @@ void launch_tile(int t, const Params& p, hipStream_t s) {
   switch (t) {
     case 0: launch_mfma<256, 256, AK, BKC, EPI>(p, s); break;
     case 1: launch_mfma<256, 128, AK, BKC, EPI>(p, s); break;
+    case kNarrowTile:
+      if constexpr (AK) {
+        launch_mfma<128, 64, AK, BKC, EPI>(p, s);
+        break;
+      }
+      [[fallthrough]];
     default: launch_mfma<128, 128, AK, BKC, EPI>(p, s); break;
   }
 }
@@ -883,7 +902,7 @@ zb_status launch_gemm_w_group(const GemmDesc* gs, int n, hipStream_t s) {
 
 size_t gemm_split_arena(int M, int N, int K) {
   if (N % 8) return 0;
-  const GemmPlan pl = plan_gemm(M, N, K, true, (size_t)-1);
+  const GemmPlan pl = plan_gemm(M, N, K, true, (size_t)-1, true);
   return pl.splits == 1 ? 0 : (size_t)pl.splits * M * N * 4;
 }
 
@@ -938,7 +957,7 @@ zb_status launch_gemm(const GemmDesc& g, hipStream_t s) {
   const bool z8 = g.epi != EPI_GELU || (g.ldz % 8 == 0 && aligned16(g.Z));
   const bool can_split = g.epi != EPI_ACC && g.part && g.N % 8 == 0 && g.ldc % 8 == 0 && aligned16(g.C) &&
                          aligned16(g.part) && rz8 && z8;
-  const GemmPlan pl = plan_gemm(g.M, g.N, g.K, can_split, g.part_bytes);
+  const GemmPlan pl = plan_gemm(g.M, g.N, g.K, can_split, g.part_bytes, g.a_kcontig != 0);
   const int t = pl.tile;
   p.splits = pl.splits;
   p.kts = pl.kts;

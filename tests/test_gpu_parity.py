@@ -9,6 +9,8 @@
 * Deferred W: flushed fp32 gradients are bit-identical across 1F1B, ZB-H1,
   ZB-H2 and W-last orders, and across steps.
 """
+import re
+
 import numpy as np
 import pytest
 import torch
@@ -42,7 +44,8 @@ INT_SHAPES = [
     (64, 64, 64),          # one partial tile
     (200, 136, 328),       # ragged M, N, K against every tile size
     (520, 264, 392),       # several tiles + ragged tails
-    (1024, 2048, 1024),    # 128x128 / 256x128 tiles
+    (1024, 2048, 1024),    # 128x64 tiles
+    (2040, 2056, 2024),    # F 128x128, B 256x128 tiles, ragged
     (4096, 4096, 256),     # B picks 256x256 tiles
     (4096, 256, 4096),     # F picks 256x256 tiles
     (8, 8, 8),             # smallest legal shape
@@ -96,6 +99,49 @@ def test_linear_passes_random_within_tolerance(T, K, N):
     assert _rel_err(_host(Y), ost.linear_forward(x64, w64)) < 1e-2
     assert _rel_err(_host(DX), ost.linear_backward_input(dy64, w64)) < 1e-2
     assert _rel_err(DW.cpu().numpy(), ost.linear_backward_weight(x64, dy64)) < 1e-5
+
+
+def _gemm_plans(fn):
+    """Names of the GEMM launches `fn` makes (tag, tile, split, epilogue)."""
+    zb.zb_prof_reset()
+    zb.zb_prof_enable(True)
+    try:
+        fn()
+        torch.cuda.synchronize()
+    finally:
+        zb.zb_prof_enable(False)
+    names = {r["name"] for r in zb.zb_prof_read() if r["name"].startswith("gemm_")}
+    zb.zb_prof_reset()
+    return names
+
+
+def test_parity_cases_cover_every_gemm_plan():
+    """The tile shapes and split-K plans the planner can pick all occur in the
+    parity cases above: the exact linear shapes cover every tile, a reduced
+    stage covers split-K partials with their reduction."""
+    def linears():
+        for T, K, N in INT_SHAPES:
+            X = torch.zeros((T, K), dtype=torch.bfloat16, device="cuda")
+            Wt = torch.zeros((K, N), dtype=torch.bfloat16, device="cuda")
+            DY = torch.zeros((T, N), dtype=torch.bfloat16, device="cuda")
+            zb.zb_linear_forward(X, Wt, torch.empty((T, N), dtype=torch.bfloat16, device="cuda"), _stream())
+            zb.zb_linear_backward_input(DY, Wt, torch.empty((T, K), dtype=torch.bfloat16, device="cuda"),
+                                        _stream())
+    names = _gemm_plans(linears)
+    print(sorted(names), flush=True)
+    for tile in ("128x64", "128x128", "256x128", "256x256"):
+        assert any(f"_{tile}_" in n for n in names), tile
+
+    w = REDUCED["mlp_linears_reduced"]
+    ws, xs, dys = _inputs(w)
+    holder = {}
+
+    def stage():
+        holder["pipe"] = _run(w, ws, xs, dys, "zbh1")[0]
+    names = _gemm_plans(stage)
+    holder["pipe"].close()
+    print(sorted(names), flush=True)
+    assert any(re.search(r"_\d+x\d+k[24]_", n) for n in names)
 
 
 def test_linear_fp32_mode_exact_on_integers():
