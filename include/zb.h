@@ -399,6 +399,10 @@ void zb_stage_destroy(zb_stage* st);
  * dw (device) is fp32 [K, N].  Asynchronous on stream (hipStream_t or NULL).
  * Errors: ZB_E_ARG (null pointer, negative size), ZB_E_UNSUPPORTED (bf16
  * with K, N or T not a multiple of 8, or a pointer not 16-byte aligned).
+ * Zero sizes are legal: an empty output is left alone, and an empty
+ * contraction (K = 0 in F, N = 0 in B, T = 0 in W) gives zeros (W with
+ * accumulate != 0 leaves dw unchanged); the operands of an empty contraction
+ * may be NULL.
  * ---------------------------------------------------------------------- */
 
 /* F: y[T, N] = x[T, K] . w[K, N] */

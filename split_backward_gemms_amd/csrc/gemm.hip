@@ -435,7 +435,7 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
 
   // Ring: tiles t+1 .. t+NS-1 are in flight while tile t feeds the MFMAs;
   // tile t+NS goes into tile t's stage once every wave has read it.
-  dma(std::integral_constant<int, 0>{}, 0);
+  if (0 < nk) dma(std::integral_constant<int, 0>{}, 0);  // K == 0: no copies (none would be waited for)
   if (NS > 1 && 1 < nk) dma(std::integral_constant<int, 1>{}, 1);
   if (NS > 2 && 2 < nk) dma(std::integral_constant<int, (NS > 2 ? 2 : 0)>{}, 2);
   if (NS > 3 && 3 < nk) dma(std::integral_constant<int, (NS > 3 ? 3 : 0)>{}, 3);
@@ -909,7 +909,7 @@ size_t gemm_split_arena(int M, int N, int K) {
 zb_status launch_gemm(const GemmDesc& g, hipStream_t s) {
   if (g.M < 0 || g.N < 0 || g.K < 0) return set_error(ZB_E_ARG, "gemm: negative size");
   if (g.M == 0 || g.N == 0) return ZB_OK;
-  if (!g.A || !g.B || !g.C) return set_error(ZB_E_ARG, "gemm: null operand");
+  if (!g.C || (g.K > 0 && (!g.A || !g.B))) return set_error(ZB_E_ARG, "gemm: null operand");  // K = 0: C = 0
   if ((g.epi == EPI_RESID || g.epi == EPI_DGELU) && !g.R) return set_error(ZB_E_ARG, "gemm: null R");
   if (g.epi == EPI_GELU && !g.Z) return set_error(ZB_E_ARG, "gemm: null Z");
   Params p{};

@@ -101,6 +101,31 @@ def test_linear_passes_random_within_tolerance(T, K, N):
     assert _rel_err(DW.cpu().numpy(), ost.linear_backward_weight(x64, dy64)) < 1e-5
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("T,K,N", [(0, 64, 64), (64, 0, 64), (64, 64, 0), (0, 0, 0)])
+def test_linear_passes_with_empty_dimensions(T, K, N, dtype):
+    """An empty output is left alone; an empty contraction (K in F, N in B,
+    T in W) gives zeros, and W accumulating over no tokens leaves dW as it was."""
+    print(f"linear empty T={T} K={K} N={N} {dtype}", flush=True)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    X = torch.ones((T, K), dtype=tdt, device="cuda")
+    Wt = torch.ones((K, N), dtype=tdt, device="cuda")
+    DY = torch.ones((T, N), dtype=tdt, device="cuda")
+    Y = torch.full((T, N), 7.0, dtype=tdt, device="cuda")
+    DX = torch.full((T, K), 7.0, dtype=tdt, device="cuda")
+    DW = torch.full((K, N), 5.0, dtype=torch.float32, device="cuda")
+    zb.zb_linear_forward(X, Wt, Y, _stream())
+    zb.zb_linear_backward_input(DY, Wt, DX, _stream())
+    zb.zb_linear_backward_weight(X, DY, DW, True, _stream())
+    torch.cuda.synchronize()
+    assert torch.all(Y == 0).item()    # K = 0: sum over nothing (vacuous when Y is empty)
+    assert torch.all(DX == 0).item()   # N = 0
+    assert torch.all(DW == 5.0).item() # T = 0, accumulate: unchanged
+    zb.zb_linear_backward_weight(X, DY, DW, False, _stream())
+    torch.cuda.synchronize()
+    assert torch.all(DW == 0).item()
+
+
 def _gemm_plans(fn):
     """Names of the GEMM launches `fn` makes (tag, tile, split, epilogue)."""
     zb.zb_prof_reset()
