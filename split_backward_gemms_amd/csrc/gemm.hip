@@ -169,19 +169,20 @@ __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// One operand tile (ROWS m/n rows by 64 k) copied global -> LDS by the
+// One operand tile (ROWS m/n rows by BK k) copied global -> LDS by the
 // buffer unit, without passing through registers.  One instruction moves 64
 // lanes x 16 bytes into 1 KiB of consecutive LDS (lane l at byte 16 l); the
 // swizzle is applied by choosing which global chunk each lane fetches.
-//   KCONTIG:   LDS [ROWS][64] bf16; chunk c (8 k values) of row r sits at
-//              position c ^ swz(r) of its 128-byte row.
-//   otherwise: LDS [64][ROWS] bf16; chunk c (8 m values) of k-row k sits at
+//   KCONTIG:   LDS [ROWS][64] bf16 (BK = 64 only); chunk c (8 k values) of row
+//              r sits at position c ^ swz(r) of its 128-byte row.
+//   otherwise: LDS [BK][ROWS] bf16; chunk c (8 m values) of k-row k sits at
 //              position c ^ 4 (k % 4) of its 2 ROWS-byte row (c ^ 4 (k % 2) when
 //              ROWS = 64).
 // The four waves of the workgroup each move a quarter of the tile.
-template <int ROWS, bool KCONTIG>
+template <int ROWS, bool KCONTIG, int BK = BKT>
 struct DmaLoader {
-  static constexpr int NI = ROWS / 32;  // instructions per wave per tile
+  static_assert(BK == BKT || !KCONTIG, "k-contiguous operands use 64-deep tiles");
+  static constexpr int NI = ROWS * BK / 2048;  // instructions per wave per tile
   u32x4 rsrc;
   uint32_t voff[NI];                    // lane's byte offset at k0 = 0 (kOOB outside the matrix)
   int kofs[KCONTIG ? NI : 1];           // KCONTIG: lane's first k within the tile
@@ -243,12 +244,12 @@ struct GroupParams {
   int n;
 };
 
-// LDS ring depth per tile shape: as many 64-deep stages (up to 4) as fit in a
-// CU's 160 KiB shared by OCC workgroups (a 256x256 stage is 64 KiB, 256x128
-// 48 KiB, 128x128 32 KiB).
-template <int BM, int BN, int OCC = 1>
+// LDS ring depth per tile shape: as many BK-deep stages (up to 4) as fit in a
+// CU's 160 KiB shared by OCC workgroups (64 deep: a 256x256 stage is 64 KiB,
+// 256x128 48 KiB, 128x128 32 KiB; 32 deep: half of that).
+template <int BM, int BN, int OCC = 1, int BK = BKT>
 struct Ring {
-  static constexpr int STAGE = (BM + BN) * BKT * 2;
+  static constexpr int STAGE = (BM + BN) * BK * 2;
   static constexpr int FIT = (160 * 1024 / OCC) / STAGE;  // OCC workgroups share a CU's 160 KiB
   static constexpr int NS = FIT < 4 ? FIT : 4;
   static_assert(NS >= 2, "the ring needs two stages");
@@ -256,22 +257,22 @@ struct Ring {
   static constexpr int S3 = NS > 3 ? STAGE : 16;
 };
 
-template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC = 1>
+template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC = 1, int BK = BKT>
 __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, char* s0, char* s1, char* s2,
                                           char* s3);
 
 // The ring stages are separate LDS objects (so the code that addresses each
 // one is fixed at compile time).
-#define ZB_GEMM_LDS(BM, BN, OCC)                                                  \
-  __shared__ __attribute__((aligned(1024))) char s0[Ring<BM, BN, OCC>::STAGE];  \
-  __shared__ __attribute__((aligned(1024))) char s1[Ring<BM, BN, OCC>::STAGE];  \
-  __shared__ __attribute__((aligned(1024))) char s2[Ring<BM, BN, OCC>::S2];     \
-  __shared__ __attribute__((aligned(1024))) char s3[Ring<BM, BN, OCC>::S3]
+#define ZB_GEMM_LDS(BM, BN, OCC, BK)                                                  \
+  __shared__ __attribute__((aligned(1024))) char s0[Ring<BM, BN, OCC, BK>::STAGE];  \
+  __shared__ __attribute__((aligned(1024))) char s1[Ring<BM, BN, OCC, BK>::STAGE];  \
+  __shared__ __attribute__((aligned(1024))) char s2[Ring<BM, BN, OCC, BK>::S2];     \
+  __shared__ __attribute__((aligned(1024))) char s3[Ring<BM, BN, OCC, BK>::S3]
 
 template <int BM, int BN, bool AK, bool BKC, int EPI>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_mfma(Params p) {
-  ZB_GEMM_LDS(BM, BN, 1);
+  ZB_GEMM_LDS(BM, BN, 1, BKT);
   const int total = p.nbm * p.nbn * p.splits;
   for (int b0 = blockIdx.x; b0 < total; b0 += gridDim.x) {  // persistent when the grid is smaller
     if (b0 != (int)blockIdx.x) __syncthreads();
@@ -281,10 +282,10 @@ gemm_bf16_mfma(Params p) {
   }
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC>
+template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC, int BK>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(OCC, OCC)))
 gemm_bf16_mfma_group(GroupParams gp) {
-  ZB_GEMM_LDS(BM, BN, OCC);
+  ZB_GEMM_LDS(BM, BN, OCC, BK);
   const int total = gp.tile_start[gp.n];
   // Persistent when the grid is smaller than the tile count: workgroup w takes
   // tiles w, w + grid, ...; the barrier keeps the next tile's copies out of the
@@ -296,7 +297,7 @@ gemm_bf16_mfma_group(GroupParams gp) {
     if (total % XCDS == 0) b = (b % XCDS) * (total / XCDS) + b / XCDS;  // one XCD works a GEMM's neighbours
     int g = 0;
     while (g + 1 < gp.n && b >= gp.tile_start[g + 1]) ++g;
-    gemm_tile<BM, BN, AK, BKC, EPI, OCC>(gp.p[g], b - gp.tile_start[g], 0, s0, s1, s2, s3);
+    gemm_tile<BM, BN, AK, BKC, EPI, OCC, BK>(gp.p[g], b - gp.tile_start[g], 0, s0, s1, s2, s3);
   }
 }
 
@@ -314,12 +315,13 @@ __device__ __forceinline__ bf16x8 frag_t(const char* tile, uint32_t off) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC>
+template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC, int BK>
 __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, char* s0, char* s1, char* s2,
                                           char* s3) {
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int NS = Ring<BM, BN, OCC>::NS;
+  constexpr int NS = Ring<BM, BN, OCC, BK>::NS;
+  constexpr int AT = BM * BK * 2;  // bytes of the A tile in a ring stage (the B tile follows)
   char* const bufs[4] = {s0, s1, s2, s3};
 
   int tm, tn;
@@ -347,14 +349,14 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
   __amdgpu_buffer_rsrc_t crsrc = make_rsrc(p.C, (uint32_t)(((int64_t)(p.M - 1) * p.ldc + p.N) *
                                                            (EPI == EPI_ACC ? 4 : 2)));
 
-  DmaLoader<BM, AK> la(static_cast<const uint16_t*>(p.A), p.lda, m0, p.M, p.K, wave, lane);
-  DmaLoader<BN, BKC> lb(static_cast<const uint16_t*>(p.B), p.ldb, n0, p.N, p.K, wave, lane);
-  constexpr int NI = DmaLoader<BM, AK>::NI + DmaLoader<BN, BKC>::NI;  // copies per wave per tile
-  // This workgroup's k tiles: [kt0, kt0 + nk) of the product's ceil(K / 64).
-  const int nk_all = (p.K + BKT - 1) / BKT;
+  DmaLoader<BM, AK, BK> la(static_cast<const uint16_t*>(p.A), p.lda, m0, p.M, p.K, wave, lane);
+  DmaLoader<BN, BKC, BK> lb(static_cast<const uint16_t*>(p.B), p.ldb, n0, p.N, p.K, wave, lane);
+  constexpr int NI = DmaLoader<BM, AK, BK>::NI + DmaLoader<BN, BKC, BK>::NI;  // copies per wave per tile
+  // This workgroup's k tiles: [kt0, kt0 + nk) of the product's ceil(K / BK).
+  const int nk_all = (p.K + BK - 1) / BK;
   const int kt0 = split * p.kts;
   const int nk = min(nk_all - kt0, p.kts);
-  const bool k_ragged = (p.K % BKT) != 0;  // only the product's last tile straddles K
+  const bool k_ragged = (p.K % BK) != 0;  // only the product's last tile straddles K
 
   // Fragment read offsets within an operand tile.
   //  k-contiguous: row = base + 32 i + lane % 32, chunk = 2 kk + lane / 32,
@@ -395,7 +397,7 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
     }
   };
   auto read_b = [&](const char* buf, int kk, int fb) {
-    const char* bt = buf + BM * 128;
+    const char* bt = buf + AT;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       if constexpr (BKC) bfr[fb][j] = frag_k(bt, rb[kk ^ (2 * (j & 1))] + j * 32 * 128);
@@ -418,14 +420,14 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
   // Copies of tile t into ring stage BI: operand A (which = 0) or B (1).
   auto dma_op = [&](auto bi, int which, int t) {
     const uint32_t b = __builtin_amdgcn_readfirstlane(lds_addr(bufs[decltype(bi)::value]));
-    const int k0 = (kt0 + t) * BKT;
+    const int k0 = (kt0 + t) * BK;
     const bool rag = k_ragged && kt0 + t == nk_all - 1;
     if (which == 0) {
       if (rag) la.template load<true>(b, k0, p.K);
       else la.template load<false>(b, k0, p.K);
     } else {
-      if (rag) lb.template load<true>(b + BM * 128, k0, p.K);
-      else lb.template load<false>(b + BM * 128, k0, p.K);
+      if (rag) lb.template load<true>(b + AT, k0, p.K);
+      else lb.template load<false>(b + AT, k0, p.K);
     }
   };
   auto dma = [&](auto bi, int t) {
@@ -456,7 +458,7 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
     constexpr int NXT = (CUR + 1) % NS;
     const char* cur = bufs[CUR];
 #pragma unroll
-    for (int kk = 0; kk < BKT / 16 - 1; ++kk) {
+    for (int kk = 0; kk < BK / 16 - 1; ++kk) {
       read_frags(cur, kk + 1, (kk + 1) & 1);  // all reads go out ahead of the step's MFMAs
       __builtin_amdgcn_sched_barrier(0);
       mfmas(kk & 1);
@@ -808,7 +810,7 @@ void launch_mfma(Params p, hipStream_t s) {
   hipLaunchKernelGGL((gemm_bf16_mfma<BM, BN, AK, BKC, EPI>), dim3(grid), dim3(NT), 0, s, p);
 }
 
-template <int BM, int BN, int OCC = 1>
+template <int BM, int BN, int OCC = 1, int BK = BKT>
 void launch_w_group(GroupParams gp, hipStream_t s) {
   int total = 0;
   for (int g = 0; g < gp.n; ++g) {
@@ -816,7 +818,7 @@ void launch_w_group(GroupParams gp, hipStream_t s) {
     gp.p[g].nbn = (gp.p[g].N + BN - 1) / BN;
     gp.p[g].xcd_remap = 0;
     gp.p[g].splits = 1;
-    gp.p[g].kts = (gp.p[g].K + BKT - 1) / BKT;
+    gp.p[g].kts = (gp.p[g].K + BK - 1) / BK;
     gp.tile_start[g] = total;
     total += gp.p[g].nbm * gp.p[g].nbn;
   }
@@ -824,7 +826,7 @@ void launch_w_group(GroupParams gp, hipStream_t s) {
   // One workgroup per CU (OCC per CU), each looping over its tiles: measured
   // 3-4% faster than one workgroup per tile for the grouped W launch.
   const int grid = std::min(total, cu_count() / XCDS * XCDS * OCC);
-  hipLaunchKernelGGL((gemm_bf16_mfma_group<BM, BN, false, false, EPI_ACC, OCC>), dim3(grid), dim3(NT), 0, s, gp);
+  hipLaunchKernelGGL((gemm_bf16_mfma_group<BM, BN, false, false, EPI_ACC, OCC, BK>), dim3(grid), dim3(NT), 0, s, gp);
 }
 
 template <bool AK, bool BKC, int EPI>
@@ -891,10 +893,13 @@ zb_status launch_gemm_w_group(const GemmDesc* gs, int n, hipStream_t s) {
       bytes += 2.0 * ((double)g.M * g.K + (double)g.K * g.N) + (g.beta ? 8.0 : 4.0) * g.M * g.N;
     }
     if (gp.n == 0) continue;
-    // 256x256 tiles, one workgroup per CU: measured against 128x128 tiles two
-    // to a CU in one process, it is faster at every size here (T = 1024 to 4096).
+    // 256x256 tiles, one workgroup per CU, 32-deep k tiles in a four-stage
+    // ring (three in flight).  Measured in one process against 64-deep tiles
+    // in a two-stage ring: 3.6% faster at T = 1024 and 2048, 7.8% at 4096;
+    // 128x128 and 256x128 tiles two to a CU, and 128x256 tiles one or two to a
+    // CU, were slower at T >= 2048 and no faster at T = 1024.
     ProfScope ps("gemm_w_group_256x256", flops, bytes, s);
-    launch_w_group<256, 256>(gp, s);
+    launch_w_group<256, 256, 1, 32>(gp, s);
     ZB_HIP_CHECK(hipGetLastError());
   }
   return ZB_OK;
