@@ -11,14 +11,16 @@
 //
 // bf16 path: 256 threads = 4 waves of 64 in a 2x2 grid; each wave owns a
 // (BM/2)x(BN/2) block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, fp32
-// accumulators).  K advances 64 at a time through a ring of 2 to 4 LDS stages
-// that global->LDS copies (buffer_load ... lds, 16 bytes per lane, hardware
-// range checks in place of bounds branches) keep filled ahead of the MFMAs;
-// every wait for them is an explicit vmcnt wait plus a barrier.  k-contiguous
-// operands sit in LDS as [rows][64] with 16-byte chunks XOR-ed by
-// (row ^ row/8) & 7 and are read 16 bytes at a time; m/n-contiguous operands
-// (F's weight, W's X and dY) stay untransposed as [64][rows] with chunks XOR-ed
-// by 4 (k % 4) and are read with the transposing ds_read_b64_tr_b16.
+// accumulators).  K advances 64 at a time (32 in the grouped W launch) through
+// a ring of 2 to 4 LDS stages that global->LDS copies (buffer_load ... lds, 16
+// bytes per lane, hardware range checks in place of bounds branches) keep
+// filled ahead of the MFMAs; every wait for them is an explicit vmcnt wait
+// plus a barrier.  k-contiguous operands sit in LDS as [rows][64] with 16-byte
+// chunks XOR-ed by (row ^ row/8) & 7 and are read 16 bytes at a time;
+// m/n-contiguous operands (F's weight, W's X and dY) stay untransposed as
+// [k][rows] with chunks XOR-ed by 4 (k % 4) and are read with the transposing
+// ds_read_b64_tr_b16.  Launches with more tiles than CUs run one persistent
+// workgroup per CU looping over its tiles.
 //
 // Epilogues: bf16 store, residual add, GeLU (pre-activation stored beside),
 // GeLU' of a saved pre-activation, with lanes l and l+32 swapping halves so
