@@ -581,26 +581,36 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
     };
     auto store_all = [&](auto kind_c) {
       constexpr int KIND = decltype(kind_c)::value;
+      // One row of 32x32 blocks at a time: its residual / pre-activation
+      // values (TN * 4 8-byte loads per lane) are all requested first, then
+      // used; the barriers keep rows from interleaving (shorter live ranges).
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
+        const int m = em + i * 32;
+        u32x2 rr[TN][4];
+        if constexpr (EPI == EPI_RESID || EPI == EPI_DGELU) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int n = en + j * 32 + 8 * g;
+              const uint32_t roff = (m < p.M && n < p.N) ? (uint32_t)(((int64_t)m * p.ldr + n) * 2) : kOOB;
+              rr[j][g] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rrsrc, (int)roff, 0, 0));
+            }
+        }
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            const int m = em + i * 32;
             u32x2 cv[2], zv[2];
 #pragma unroll
             for (int gg = 0; gg < 2; ++gg) {
               const int g = 2 * q + gg;
-              const int n = en + j * 32 + 8 * g;  // this lane's four computed columns
-              const bool ok = m < p.M && n < p.N;
               float v[4];
 #pragma unroll
               for (int t2 = 0; t2 < 4; ++t2) v[t2] = acc[i][j][4 * g + t2];
               if constexpr (EPI == EPI_RESID || EPI == EPI_DGELU) {
-                const uint32_t roff = ok ? (uint32_t)(((int64_t)m * p.ldr + n) * 2) : kOOB;
-                const u32x2 rv =
-                    __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rrsrc, (int)roff, 0, 0));
+                const u32x2 rv = rr[j][g];
                 const float r[4] = {__uint_as_float(rv[0] << 16), __uint_as_float(rv[0] & 0xffff0000u),
                                     __uint_as_float(rv[1] << 16), __uint_as_float(rv[1] & 0xffff0000u)};
 #pragma unroll
@@ -620,6 +630,8 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
             if constexpr (EPI == EPI_GELU) swap_store(zrsrc, p.ldz, m, n, zv[0], zv[1]);
             swap_store(crsrc, p.ldc, m, n, cv[0], cv[1]);
           }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     };
     if ((EPI == EPI_GELU || EPI == EPI_DGELU) && p.gelu == ZB_GELU_TANH)
       store_all(std::integral_constant<int, ZB_GELU_TANH>{});
