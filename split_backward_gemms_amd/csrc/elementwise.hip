@@ -14,20 +14,19 @@ namespace zb {
 namespace {
 
 // rows x cols elements of elem_bytes (2 or 4) each, row stride ld elements.
-// 16-byte stores where the row segment allows, scalar stores otherwise.
+// 16-byte stores where the row segment allows, 2-byte stores for its tail.
+// Rows go over blockIdx.y and chunks of a row over x, so no thread divides.
 __global__ void zero2d_kernel(char* p, int64_t rows, int64_t row_bytes, int64_t ld_bytes) {
-  const int64_t vec_per_row = row_bytes / 16;
-  const int64_t tail = row_bytes - vec_per_row * 16;
-  const int64_t total = rows * (vec_per_row + tail / 2);
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t per = vec_per_row + tail / 2;
-    const int64_t r = i / per, c = i % per;
+  const int64_t vec = row_bytes / 16;
+  const int64_t per = vec + (row_bytes - vec * 16) / 2;
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
     char* row = p + r * ld_bytes;
-    if (c < vec_per_row)
-      *reinterpret_cast<uint4*>(row + c * 16) = make_uint4(0u, 0u, 0u, 0u);
-    else
-      *reinterpret_cast<uint16_t*>(row + vec_per_row * 16 + (c - vec_per_row) * 2) = 0;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < per; c += (int64_t)gridDim.x * blockDim.x) {
+      if (c < vec)
+        *reinterpret_cast<uint4*>(row + c * 16) = make_uint4(0u, 0u, 0u, 0u);
+      else
+        *reinterpret_cast<uint16_t*>(row + vec * 16 + (c - vec) * 2) = 0;
+    }
   }
 }
 
@@ -90,12 +89,11 @@ zb_status launch_zero2d(void* p, int64_t rows, int64_t cols, int64_t ld, int ele
   if ((reinterpret_cast<uintptr_t>(p) & 15u) || (ld_bytes & 15) || (row_bytes & 1))
     return set_error(ZB_E_UNSUPPORTED, "zero2d: rows must be 16-byte aligned");
   const int64_t per = row_bytes / 16 + (row_bytes % 16) / 2;
-  const int64_t total = rows * per;
   const int threads = 256;
-  const int64_t blocks = std::min<int64_t>((total + threads - 1) / threads, 4096);
+  const dim3 grid((unsigned)std::min<int64_t>((per + threads - 1) / threads, 64),
+                  (unsigned)std::min<int64_t>(rows, 4096));
   ProfScope ps("zero2d", 0.0, (double)rows * row_bytes, s);
-  hipLaunchKernelGGL(zero2d_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, static_cast<char*>(p), rows,
-                     row_bytes, ld_bytes);
+  hipLaunchKernelGGL(zero2d_kernel, grid, dim3(threads), 0, s, static_cast<char*>(p), rows, row_bytes, ld_bytes);
   ZB_HIP_CHECK(hipGetLastError());
   return ZB_OK;
 }
