@@ -104,3 +104,24 @@ def test_zbh2_with_one_warmup_forward_too_many_is_caught(monkeypatch):
     monkeypatch.setitem(sch.ORDERS, "zbh2", bad)
     with pytest.raises(AssertionError):
         pin_sched.test_zbh2_first_stage_runs_seven_forwards_before_first_b()
+
+
+def test_heuristic_memory_check_off_by_one_microbatch_is_caught(monkeypatch):
+    import test_oracle_heuristic as pin_heur
+    from oracle import heuristic as H
+    good = H.build
+
+    def bad(P, m, t, m_b, m_w, m_limit, *args, **kw):  # checks against one activation more than allowed
+        return good(P, m, t, m_b, m_w, m_limit + m_b, *args, **kw)
+    monkeypatch.setattr(H, "build", bad)
+    with pytest.raises(AssertionError):
+        for seed in range(6):
+            pin_heur.test_orders_valid_and_within_budget(seed)
+
+
+def test_v_placement_as_a_ring_is_caught(monkeypatch):
+    import test_oracle_vshape as pin_v
+    from oracle import vshape as V
+    monkeypatch.setattr(V, "device_of", lambda c, P: c % P)  # interleaved placement instead of the V
+    with pytest.raises(AssertionError):
+        pin_v.test_placement_is_a_v(2)
