@@ -88,9 +88,12 @@ class EmulatedPipeline:
 
     def __init__(self, w, weights: Sequence[Sequence[Dict[str, np.ndarray]]], ops: Optional[Sequence] = None,
                  device: str = "cuda", stream: Optional[torch.cuda.Stream] = None,
-                 stage_streams: bool = False, recompute_act: Optional[int] = None):
+                 stage_streams: bool = False, recompute_act: Optional[int] = None,
+                 n_streams: Optional[int] = None):
         """stage_streams=True gives every emulated stage its own HIP stream (default
-        priority), so independent stages' passes run concurrently.  recompute_act
+        priority), so independent stages' passes run concurrently; n_streams caps
+        the number of streams (stage s on stream s % n_streams: passes issued in
+        the linearized order stay valid on a shared stream).  recompute_act
         0 / 1 fixes the stash layout (see zb_stage_desc); None stashes the MLP
         activation when that plan fits in free device memory and rebuilds it for W
         otherwise."""
@@ -98,8 +101,12 @@ class EmulatedPipeline:
         self.device = torch.device(device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         self.P = w.n_stages
-        self.streams = ([torch.cuda.Stream(self.device) for _ in range(self.P)] if stage_streams
-                        else [self.stream] * self.P)
+        if stage_streams:
+            n = self.P if n_streams is None else max(1, min(self.P, n_streams))
+            pool = [torch.cuda.Stream(self.device) for _ in range(n)]
+            self.streams = [pool[s % n] for s in range(self.P)]
+        else:
+            self.streams = [self.stream] * self.P
         self.handles: List[int] = []
         self.weights: List[List[torch.Tensor]] = []
         self.grads: List[List[torch.Tensor]] = []

@@ -518,15 +518,18 @@ def test_full_layer_error_per_layer_is_small():
     assert max(errs) <= 6e-3, errs
 
 
+@pytest.mark.parametrize("n_streams", [None, 2])
 @pytest.mark.parametrize("name", ["mlp_linears_reduced", "full_reduced"])
-def test_stage_streams_match_single_stream_bitwise(name):
-    """One HIP stream per emulated stage (concurrent stages) gives the same bits
-    as one shared stream: only the overlap changes, not any summation order."""
+def test_stage_streams_match_single_stream_bitwise(name, n_streams):
+    """One HIP stream per emulated stage, or the stages spread over two streams
+    (concurrent stages) gives the same bits as one shared stream: only the
+    overlap changes, not any summation order."""
     w = REDUCED[name]
     ws, xs, dys = _inputs(w)
     _, y1, dx1, dw1, _ = _run(w, ws, xs, dys, "zbh1")
     ops, _ = zb.zb_schedule_build("zbh1", w.n_stages, w.n_micro)
-    pipe = EmulatedPipeline(w, ws, ops=ops, stage_streams=True)
+    pipe = EmulatedPipeline(w, ws, ops=ops, stage_streams=True, n_streams=n_streams)
+    assert len({id(s) for s in pipe.streams}) == (w.n_stages if n_streams is None else n_streams)
     X = [upload(x, w.dtype, "cuda") for x in xs]
     DY = [upload(d, w.dtype, "cuda") for d in dys]
     for step in range(2):
