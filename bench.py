@@ -3,7 +3,8 @@
 
 A step is one whole schedule: every emulated stage's F, B and W passes for
 every microbatch (the workload's handcrafted order by default), run through
-zb_run_schedule with one HIP stream per emulated stage, then the step boundary
+zb_run_schedule with the emulated stages spread over two HIP streams (stage s
+on stream s mod 2; --streams), then the step boundary
 (zb_grad_flush) of every stage.  Inputs, weights and gradient buffers are
 resident in HBM before timing starts.  --order zb1p / zb2p runs the automatic
 scheduler's order, built from pass times measured on this device and the
