@@ -237,6 +237,9 @@ def main() -> int:
         log(f"{order}, one stream: {single_ms:.3f} ms/step; passes {t_split}")
         # Bubble rates the simulator gives across the devices at these measured
         # pass times (a ZB-V chunk counts as half a stage, in time and stash).
+        # An order with unsplit backwards (1F1B, GPipe) has no separate B and W
+        # times to feed it.
+    if a.mode == "full" and any(k in ("B", "W") for (_, k, _) in ops):
         times = pass_times_us(tr)
         cut = 2 if order == "zbv" else 1
         st_times = tuple(cut * x for x in times)
@@ -253,7 +256,7 @@ def main() -> int:
         sim_measured["zbv"] = st["bubble"] / st["makespan"]
         log(f"simulated bubble rates at measured pass times {times} us: "
             + ", ".join(f"{k} {100 * v:.1f}%" for k, v in sim_measured.items()))
-    else:
+    if a.mode != "full":
         pipe.run(ops, X, DY, y, dx)  # one untimed step before the kernel-timing phase
     if a.mode == "full" and not a.no_fused:
         pipe.plan(ops_fused)
@@ -263,11 +266,14 @@ def main() -> int:
         t_f = {k: sum(ms for (op, ms, _) in trf if op[1] == k) for k in "FU"}
         fused.update({"ms_per_step_one_stream": single_ms,
                       "ms_per_step_1f1b_unsplit_one_stream": fused_ms,
-                      "split_overhead_pass": (t_split["B"] + t_split["W"]) / t_f["U"] - 1.0,
+                      # an order with unsplit backwards has no B + W to compare
+                      "split_overhead_pass": ((t_split["B"] + t_split["W"]) / t_f["U"] - 1.0
+                                              if t_split["B"] + t_split["W"] > 0 else None),
                       "split_overhead_wall_one_stream": single_ms / fused_ms - 1.0,
                       "pass_ms_1f1b": {"F": t_f["F"], "U": t_f["U"]}})
+        so = fused["split_overhead_pass"]
         log(f"1f1b unsplit, one stream: {fused_ms:.3f} ms/step; split overhead (B+W vs U) "
-            f"{100 * fused['split_overhead_pass']:.2f}%")
+            + (f"{100 * so:.2f}%" if so is not None else "n/a (unsplit order)"))
 
     # kernel-level timing over profiled steps of the measured order (one stream)
     zb.zb_prof_reset()
