@@ -263,8 +263,12 @@ zb_status zb_stage_workspace_bytes(zb_stage* st, const zb_op* ops, int n_ops, si
 /* Hand the stage a device buffer of at least the planned size (256-byte
  * aligned).  The stage sub-allocates its stash and the scratch of its kernels
  * (including the split-K partial sums of its GEMMs) from it; the caller keeps
- * ownership.  Only allowed while no microbatch is live.
- * Errors: ZB_E_ARG (null, misaligned), ZB_E_BUDGET (too small), ZB_E_STATE. */
+ * ownership and must not write to it while it is bound.  Only allowed while no
+ * microbatch is live.  For MLP-linears stages it enqueues, on the stage's
+ * stream, the clearing of the dQ and dK columns that identity attention keeps
+ * at zero in every B slot.
+ * Errors: ZB_E_ARG (null, misaligned), ZB_E_BUDGET (too small), ZB_E_STATE,
+ * ZB_E_HIP. */
 zb_status zb_stage_bind_workspace(zb_stage* st, void* dev_ptr, size_t bytes);
 
 /* Device address of the stage's input slot for microbatch mb (claimed on

@@ -533,8 +533,8 @@ zb_status run_backward(zb_stage* S, int mb, void* dx, bool unsplit, int beta) {
         }
         ZB_TRY(gemm_b(S, bwb + o.dz, f, up, bwb + o.dp, h, EPI_STORE));
         if (unsplit) ZB_TRY(gemm_w(S, fwb + o.xup, h, bwb + o.dz, f, up, beta));
-        // identity attention backward: dV = dO, dQ = dK = 0
-        ZB_TRY(launch_zero2d(bwb + o.dqkv, S->T, 2 * h, 3 * h, (int)es, S->stream));
+        // identity attention backward: dV = dO; dQ = dK = 0 stay in the slot from
+        // zb_stage_bind_workspace
         ZB_TRY(gemm_b(S, bwb + o.dp, h, proj, elem(bwb, o.dqkv, 2 * h, es), 3 * h, EPI_STORE));
         if (unsplit) ZB_TRY(gemm_w(S, elem(fwb, o.qkv_fw, 2 * h, es), 3 * h, bwb + o.dp, h, proj, beta));
         ZB_TRY(gemm_b(S, bwb + o.dqkv, 3 * h, qkv, out, h, EPI_STORE));
@@ -812,6 +812,13 @@ extern "C" zb_status zb_stage_bind_workspace(zb_stage* S, void* p, size_t bytes)
   S->fb.reset(q, S->plan_fb);
   q += (size_t)S->plan_fb * S->fb_bytes;
   S->bw.reset(q, S->plan_bw);
+  // Identity attention (MLP linears): the dQ and dK columns of every layer's
+  // dQKV in every B slot are zero for good and nothing else writes them, so
+  // they are cleared once here instead of in every backward.
+  if (S->d.kind == ZB_KIND_MLP_LINEARS)
+    for (int s = 0; s < S->plan_bw; ++s)
+      for (int l = 0; l < S->L; ++l)
+        ZB_TRY(launch_zero2d(S->bw.at(s) + S->off[l].dqkv, S->T, 2 * S->h, 3 * S->h, (int)S->es, S->stream));
   std::fill(S->s_fw.begin(), S->s_fw.end(), -1);
   std::fill(S->s_fb.begin(), S->s_fb.end(), -1);
   std::fill(S->s_bw.begin(), S->s_bw.end(), -1);
