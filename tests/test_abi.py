@@ -48,3 +48,42 @@ def test_stage_create_rejects_bad_descriptors_without_gpu():
         assert e.status == zb.ZB_E_UNSUPPORTED  # head_dim 64
     else:
         raise AssertionError("head_dim 64 must be rejected")
+
+
+def _status(fn, *args):
+    st = fn(*args)
+    return st, zb.lib().zb_last_error().decode()
+
+
+def test_linear_entry_points_reject_bad_arguments_before_any_launch():
+    """Host-side checks of the bf16 linear passes: each case below is refused
+    before the library makes its first HIP call (the addresses are never
+    dereferenced), so this runs without a GPU."""
+    L = zb.lib()
+    bf16, fp32 = zb.ZB_DTYPE_BF16, zb.ZB_DTYPE_FP32
+    p = 1 << 20  # 16-byte aligned stand-in address
+    # Buffer offsets are 32-bit: an operand whose extent reaches 2 GiB is refused.
+    st, msg = _status(L.zb_linear_forward, bf16, 1 << 20, 1024, 8, p, p, p, None)
+    assert st == zb.ZB_E_UNSUPPORTED and "2 GiB" in msg, msg           # x: 2^20 x 1024 bf16 = 2 GiB
+    st, msg = _status(L.zb_linear_backward_input, bf16, 8, 8, 1 << 27, p, p, p, None)
+    assert st == zb.ZB_E_UNSUPPORTED and "2 GiB" in msg, msg           # dy: 8 x 2^27 bf16 = 2 GiB
+    st, msg = _status(L.zb_linear_backward_weight, bf16, 8, 1 << 14, 1 << 15, p, p, p, 1, None)
+    assert st == zb.ZB_E_UNSUPPORTED and "2 GiB" in msg, msg           # dw: 2^14 x 2^15 fp32 = 2 GiB
+    # 16-byte vectors along every contiguous dimension.
+    st, msg = _status(L.zb_linear_forward, bf16, 64, 60, 64, p, p, p, None)
+    assert st == zb.ZB_E_UNSUPPORTED and "multiples of 8" in msg, msg  # K = 60
+    st, msg = _status(L.zb_linear_forward, bf16, 64, 64, 64, p + 8, p, p, None)
+    assert st == zb.ZB_E_UNSUPPORTED, msg                              # x 8-byte aligned only
+    st, msg = _status(L.zb_linear_backward_weight, bf16, 64, 64, 60, p, p, p, 0, None)
+    assert st == zb.ZB_E_UNSUPPORTED, msg                              # N = 60
+    # Argument errors.
+    for fn in (L.zb_linear_forward, L.zb_linear_backward_input):
+        assert _status(fn, bf16, -1, 64, 64, p, p, p, None)[0] == zb.ZB_E_ARG
+        assert _status(fn, bf16, 64, 64, 64, None, p, p, None)[0] == zb.ZB_E_ARG
+        assert _status(fn, bf16, 64, 64, 64, p, p, None, None)[0] == zb.ZB_E_ARG
+        assert _status(fn, 7, 64, 64, 64, p, p, p, None)[0] == zb.ZB_E_ARG
+    assert _status(L.zb_linear_backward_weight, bf16, 64, 64, -8, p, p, p, 0, None)[0] == zb.ZB_E_ARG
+    assert _status(L.zb_linear_backward_weight, fp32, 64, 64, 64, p, None, p, 0, None)[0] == zb.ZB_E_ARG
+    # Empty outputs are legal and launch nothing.
+    assert _status(L.zb_linear_forward, bf16, 0, 64, 64, None, None, None, None)[0] == zb.ZB_OK
+    assert _status(L.zb_linear_backward_weight, bf16, 64, 0, 64, None, None, None, 1, None)[0] == zb.ZB_OK
