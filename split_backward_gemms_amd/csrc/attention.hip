@@ -187,9 +187,12 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
   __shared__ __attribute__((aligned(1024))) char sV0[BLK];
   __shared__ __attribute__((aligned(1024))) char sK1[BLK];
   __shared__ __attribute__((aligned(1024))) char sV1[BLK];
+  // Grid (heads x sequences, query blocks).  Workgroups are handed out with x
+  // varying fastest, so every head's heaviest block (the last one, which sees
+  // all keys) goes out first and the light ones fill in behind them.
   const int nqb = (p.seq + 127) / 128;
-  const int qb = nqb - 1 - (int)blockIdx.x;  // heaviest blocks first
-  const int hd = blockIdx.y % p.heads, sq = blockIdx.y / p.heads;
+  const int qb = nqb - 1 - (int)blockIdx.y;
+  const int hd = blockIdx.x % p.heads, sq = blockIdx.x / p.heads;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, lc = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t ld3 = 3LL * p.h, base_row = (int64_t)sq * p.seq;
@@ -317,8 +320,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
   __shared__ __attribute__((aligned(1024))) char sK1[BLK];
   __shared__ __attribute__((aligned(1024))) char sV1[BLK];
   const int nqb = (p.seq + 127) / 128;
-  const int qb = nqb - 1 - (int)blockIdx.x;
-  const int hd = blockIdx.y % p.heads, sq = blockIdx.y / p.heads;
+  const int qb = nqb - 1 - (int)blockIdx.y;  // grid and order as in the forward
+  const int hd = blockIdx.x % p.heads, sq = blockIdx.x / p.heads;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, lc = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t ld3 = 3LL * p.h, base_row = (int64_t)sq * p.seq;
@@ -435,7 +438,10 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
   __shared__ __attribute__((aligned(1024))) char sG1[BLK];
   __shared__ __attribute__((aligned(1024))) char sLD0[1024];
   __shared__ __attribute__((aligned(1024))) char sLD1[1024];
-  const int hd = blockIdx.y % p.heads, sq = blockIdx.y / p.heads;
+  // Grid (heads x sequences, key blocks), heaviest first: key block 0 sees
+  // every query block, and workgroups are handed out with x varying fastest.
+  const int kb = (int)blockIdx.y;
+  const int hd = blockIdx.x % p.heads, sq = blockIdx.x / p.heads;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, lc = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t ld3 = 3LL * p.h, base_row = (int64_t)sq * p.seq;
@@ -444,13 +450,6 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv, ext3);
   const __amdgpu_buffer_rsrc_t rdq = make_rsrc(p.dqkv, ext3);
   const float c = p.scale * kLog2e;
-  // Key blocks x and nkb-1-x share a workgroup: together they see a fixed
-  // number of query blocks, so every workgroup has the same work.
-  const int nkb = (p.seq + 127) / 128;
-  for (int pass = 0; pass < 2; ++pass) {
-  const int kb = pass == 0 ? (int)blockIdx.x : nkb - 1 - (int)blockIdx.x;
-  if (pass == 1 && kb <= (int)blockIdx.x) break;
-
   const int kv = kb * 128 + 32 * w + lc;  // this lane's key row
   const bool kvv = kv < p.seq;
   bf16x8 kf[8], vf[8];
@@ -568,7 +567,6 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
       bstore8(rdq, offk, kv2);
       bstore8(rdq, offv, vv2);
     }
-  }  // pass
 }
 
 }  // namespace
@@ -582,7 +580,7 @@ zb_status launch_attention_fwd(const AttnArgs& a, hipStream_t s) {
   p.scale = 0.08838834764831845f;
   if (3.0 * p.T * p.h * 2 >= 2147483648.0) return set_error(ZB_E_UNSUPPORTED, "attention: QKV spans 2 GiB or more");
   if (a.seq <= 0 || a.heads <= 0 || a.nseq <= 0) return ZB_OK;
-  const dim3 grid((a.seq + 127) / 128, a.heads * a.nseq);
+  const dim3 grid(a.heads * a.nseq, (a.seq + 127) / 128);
   const double flops = 2.0 * a.nseq * (double)a.seq * a.seq * p.h;  // causal half of 4 s^2 h
   ProfScope ps("attn_fwd", flops, 2.0 * p.T * 4.0 * p.h, s);
   hipLaunchKernelGGL(attn_fwd, grid, dim3(NT), 0, s, p);
@@ -602,7 +600,7 @@ zb_status launch_attention_bwd(const AttnArgs& a, hipStream_t s) {
   p.scale = 0.08838834764831845f;
   if (3.0 * p.T * p.h * 2 >= 2147483648.0) return set_error(ZB_E_UNSUPPORTED, "attention: QKV spans 2 GiB or more");
   if (a.seq <= 0 || a.heads <= 0 || a.nseq <= 0) return ZB_OK;
-  const dim3 grid((a.seq + 127) / 128, a.heads * a.nseq);
+  const dim3 grid(a.heads * a.nseq, (a.seq + 127) / 128);  // 128-row query (dQ) or key (dK/dV) blocks
   // Algorithmic backward = causal half of 8 s^2 h = four s x s x d products; the
   // two passes execute seven (three in dQ, four in dK/dV) and share them out 3:4.
   const double alg = 4.0 * a.nseq * (double)a.seq * a.seq * p.h;
@@ -613,8 +611,7 @@ zb_status launch_attention_bwd(const AttnArgs& a, hipStream_t s) {
   }
   {
     ProfScope ps("attn_bwd_dkdv", alg * 4.0 / 7.0, 2.0 * p.T * 6.0 * p.h, s);
-    const dim3 grid2((a.seq + 255) / 256, a.heads * a.nseq);  // pairs of 128-key blocks
-    hipLaunchKernelGGL(attn_bwd_dkdv, grid2, dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(attn_bwd_dkdv, grid, dim3(NT), 0, s, p);
     ZB_HIP_CHECK(hipGetLastError());
   }
   return ZB_OK;
