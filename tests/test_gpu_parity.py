@@ -227,6 +227,10 @@ REDUCED = {
                                        n_micro=3, n_stages=2, n_layers=1),
     "full_long_seq": si.reduced(si.WORKLOADS["gpt_full_s4096"], hidden=128, heads=1, seq=320, n_micro=2,
                                 n_stages=2, n_layers=1),
+    # five 128-row causal blocks (the last one 8 rows), three heads, two sequences per microbatch:
+    # the attention grids order work by block weight across heads and sequences
+    "full_many_blocks": si.reduced(si.WORKLOADS["gpt_full_h6144"], hidden=384, heads=3, seq=520, n_micro=2,
+                                   n_stages=2, n_layers=1),
 }
 
 
