@@ -268,7 +268,8 @@ zb_status zb_stage_workspace_bytes(zb_stage* st, const zb_op* ops, int n_ops, si
  * stream, the clearing of the dQ and dK columns that identity attention keeps
  * at zero in every B slot.
  * Errors: ZB_E_ARG (null, misaligned), ZB_E_BUDGET (too small), ZB_E_STATE,
- * ZB_E_HIP. */
+ * ZB_E_HIP (that clearing failed to launch: the stage keeps its previous
+ * binding, and the new buffer may have been partly cleared). */
 zb_status zb_stage_bind_workspace(zb_stage* st, void* dev_ptr, size_t bytes);
 
 /* Device address of the stage's input slot for microbatch mb (claimed on

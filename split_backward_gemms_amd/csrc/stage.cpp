@@ -803,22 +803,24 @@ extern "C" zb_status zb_stage_bind_workspace(zb_stage* S, void* p, size_t bytes)
   const size_t need = ws_size(S, S->plan_fw, S->plan_fb, S->plan_bw);
   if (bytes < need) return set_error(ZB_E_BUDGET, "workspace %zu bytes < planned %zu", bytes, need);
   char* base = static_cast<char*>(p);
-  S->ws = base;
-  S->ws_bytes = bytes;
-  S->scratch = base;
-  char* q = base + S->scratch_bytes;
-  S->fw.reset(q, S->plan_fw);
-  q += (size_t)S->plan_fw * S->fw_bytes;
-  S->fb.reset(q, S->plan_fb);
-  q += (size_t)S->plan_fb * S->fb_bytes;
-  S->bw.reset(q, S->plan_bw);
+  char* const q_fw = base + S->scratch_bytes;
+  char* const q_fb = q_fw + (size_t)S->plan_fw * S->fw_bytes;
+  char* const q_bw = q_fb + (size_t)S->plan_fb * S->fb_bytes;
   // Identity attention (MLP linears): the dQ and dK columns of every layer's
   // dQKV in every B slot are zero for good and nothing else writes them, so
-  // they are cleared once here instead of in every backward.
+  // they are cleared once here instead of in every backward.  Enqueued before
+  // the stage takes the buffer, so a failed launch leaves the old binding.
   if (S->d.kind == ZB_KIND_MLP_LINEARS)
     for (int s = 0; s < S->plan_bw; ++s)
       for (int l = 0; l < S->L; ++l)
-        ZB_TRY(launch_zero2d(S->bw.at(s) + S->off[l].dqkv, S->T, 2 * S->h, 3 * S->h, (int)S->es, S->stream));
+        ZB_TRY(launch_zero2d(q_bw + (size_t)s * S->bw_bytes + S->off[l].dqkv, S->T, 2 * S->h, 3 * S->h,
+                             (int)S->es, S->stream));
+  S->ws = base;
+  S->ws_bytes = bytes;
+  S->scratch = base;
+  S->fw.reset(q_fw, S->plan_fw);
+  S->fb.reset(q_fb, S->plan_fb);
+  S->bw.reset(q_bw, S->plan_bw);
   std::fill(S->s_fw.begin(), S->s_fw.end(), -1);
   std::fill(S->s_fb.begin(), S->s_fb.end(), -1);
   std::fill(S->s_bw.begin(), S->s_bw.end(), -1);
