@@ -46,15 +46,35 @@ def normal_pdf(z):
     return _INV_SQRT_2PI * np.exp(-0.5 * z * z)
 
 
-def gelu(z):
-    """g(z) = z * Phi(z) (exact GeLU)."""
+_TANH_C = np.sqrt(2.0 / np.pi)
+_TANH_A = 0.044715
+
+
+def gelu(z, form: str = "erf"):
+    """g(z) = z * Phi(z) (exact GeLU).
+
+    form "tanh": the tanh approximation of Hendrycks & Gimpel, "Gaussian Error
+    Linear Units (GELUs)", section 2: Phi(z) is replaced by
+    (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))) / 2.  No workload uses it; it is
+    here to check the kernels' variant behind the GeLU flag."""
     z = np.asarray(z, dtype=np.float64)
+    if form == "tanh":
+        return 0.5 * z * (1.0 + np.tanh(_TANH_C * (z + _TANH_A * z ** 3)))
+    if form != "erf":
+        raise ValueError(form)
     return z * normal_cdf(z)
 
 
-def gelu_grad(z):
-    """g'(z) = Phi(z) + z * phi(z)."""
+def gelu_grad(z, form: str = "erf"):
+    """g'(z) = Phi(z) + z * phi(z); for the tanh form, with u = sqrt(2/pi) (z + 0.044715 z^3),
+    d/dz [z (1 + tanh u) / 2] = (1 + tanh u) / 2 + z (1 - tanh^2 u) u'(z) / 2."""
     z = np.asarray(z, dtype=np.float64)
+    if form == "tanh":
+        t = np.tanh(_TANH_C * (z + _TANH_A * z ** 3))
+        du = _TANH_C * (1.0 + 3.0 * _TANH_A * z * z)
+        return 0.5 * (1.0 + t) + 0.5 * z * (1.0 - t * t) * du
+    if form != "erf":
+        raise ValueError(form)
     return normal_cdf(z) + z * normal_pdf(z)
 
 
@@ -151,7 +171,7 @@ def layer_forward(wl: si.Workload, W: Dict[str, np.ndarray], x: np.ndarray):
     h = wl.hidden
     if wl.kind == si.TINY_MLP:
         z = linear_forward(x, W["up"])
-        a = gelu(z)
+        a = gelu(z, wl.gelu)
         y = linear_forward(a, W["down"])
         return y, {"x_up": x, "z": z, "a": a}
     if wl.kind == si.MLP_LINEARS:
@@ -159,14 +179,14 @@ def layer_forward(wl: si.Workload, W: Dict[str, np.ndarray], x: np.ndarray):
         o = qkv[:, 2 * h:3 * h].copy()
         p = linear_forward(o, W["proj"])
         z = linear_forward(p, W["up"])
-        a = gelu(z)
+        a = gelu(z, wl.gelu)
         y = linear_forward(a, W["down"])
         return y, {"x": x, "o": o, "x_up": p, "z": z, "a": a}
     qkv = linear_forward(x, W["qkv"])
     o, lse, probs = multihead_forward(qkv, h, wl.n_heads, wl.seq)
     x1 = x + linear_forward(o, W["proj"])
     z = linear_forward(x1, W["up"])
-    a = gelu(z)
+    a = gelu(z, wl.gelu)
     y = x1 + linear_forward(a, W["down"])
     return y, {"x": x, "qkv": qkv, "o": o, "lse": lse, "probs": probs,
                "x_up": x1, "z": z, "a": a}
@@ -176,7 +196,7 @@ def layer_backward_input(wl: si.Workload, W, saved, dy):
     """B of one layer: the input gradient dx, plus the output gradient of every
     linear (what its W pass consumes).  No weight gradient is formed here."""
     h = wl.hidden
-    dz = linear_backward_input(dy, W["down"]) * gelu_grad(saved["z"])
+    dz = linear_backward_input(dy, W["down"]) * gelu_grad(saved["z"], wl.gelu)
     if wl.kind == si.TINY_MLP:
         dx = linear_backward_input(dz, W["up"])
         return dx, {"up": dz, "down": dy}
@@ -215,7 +235,7 @@ def layer_backward_fused(wl: si.Workload, W, saved, dy):
     xs = linear_inputs(wl, saved)
     dws = {}
     dws["down"] = xs["down"].T @ dy
-    dz = (dy @ W["down"].T) * gelu_grad(saved["z"])
+    dz = (dy @ W["down"].T) * gelu_grad(saved["z"], wl.gelu)
     dws["up"] = xs["up"].T @ dz
     if wl.kind == si.TINY_MLP:
         return dz @ W["up"].T, dws

@@ -24,7 +24,7 @@ def desc_of(w, recompute_act: int = 0) -> "zb.zb_stage_desc":
     """Stage descriptor of a synthetic_inputs.Workload."""
     return zb.make_desc(KIND_OF[w.kind], zb.ZB_DTYPE_BF16 if w.dtype == "bf16" else zb.ZB_DTYPE_FP32,
                         w.n_layers, w.hidden, w.ffn, max(w.n_heads, 0), w.seq, w.micro_batch, w.n_micro,
-                        zb.ZB_GELU_ERF, recompute_act)
+                        zb.ZB_GELU_TANH if w.gelu == "tanh" else zb.ZB_GELU_ERF, recompute_act)
 
 
 def upload(a: np.ndarray, dtype: str, device) -> torch.Tensor:

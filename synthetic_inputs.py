@@ -55,6 +55,7 @@ class Workload:
     n_stages: int       # P (emulated on one GPU)
     order: str          # "1f1b", "zbh1", "zbh2"
     dtype: str = "bf16"  # "bf16" or "fp32"
+    gelu: str = "erf"    # "erf" (exact) or "tanh" (the tanh approximation)
 
     @property
     def tokens(self) -> int:

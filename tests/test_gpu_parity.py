@@ -234,9 +234,9 @@ REDUCED = {
 }
 
 
-def _pipeline_vs_oracle(name, order, recompute_act):
-    w = REDUCED[name]
-    print(f"pipeline parity {name} {order} recompute_act={recompute_act}", flush=True)
+def _pipeline_vs_oracle(name, order, recompute_act, gelu="erf"):
+    w = REDUCED[name].replace(gelu=gelu)
+    print(f"pipeline parity {name} {order} recompute_act={recompute_act} gelu={gelu}", flush=True)
     ws, xs, dys = _inputs(w)
     pipe, y, dx, dw, _ = _run(w, ws, xs, dys, order, recompute_act=recompute_act)
     assert pipe.recompute_act == recompute_act
@@ -268,6 +268,14 @@ def test_pipeline_matches_oracle(name, order):
 @pytest.mark.parametrize("order", ["zbh1", "1f1b"])
 def test_pipeline_matches_oracle_rebuilt_activation(name, order):
     _pipeline_vs_oracle(name, order, 1)
+
+
+@pytest.mark.parametrize("recompute_act", [0, 1])
+@pytest.mark.parametrize("name", ["tiny_bf16", "tiny_fp32", "mlp_linears_ragged"])
+def test_tanh_gelu_flag_matches_oracle(name, recompute_act):
+    """The kernels' tanh GeLU (the F epilogue, B's GeLU' epilogue and the rebuild
+    of A for W) against the oracle's tanh form; no workload uses this flag."""
+    _pipeline_vs_oracle(name, "zbh1", recompute_act, gelu="tanh")
 
 
 @pytest.mark.parametrize("recompute_act", [0, 1])

@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import test_oracle_attention as pin_attn
+import test_oracle_elementwise as pin_gelu
 import test_oracle_schedules as pin_sched
 from oracle import schedules as sch
 from oracle import stage as ost
@@ -125,3 +126,19 @@ def test_v_placement_as_a_ring_is_caught(monkeypatch):
     monkeypatch.setattr(V, "device_of", lambda c, P: c % P)  # interleaved placement instead of the V
     with pytest.raises(AssertionError):
         pin_v.test_placement_is_a_v(2)
+
+
+@pytest.mark.parametrize("a", [0.0, 0.04715])
+def test_gelu_tanh_without_or_with_a_mistyped_cubic_term_is_caught(monkeypatch, a):
+    monkeypatch.setattr(ost, "_TANH_A", a)
+    with pytest.raises(AssertionError):
+        pin_gelu.test_gelu_tanh_stays_within_the_approximation_band_of_exact_gelu()
+
+
+def test_gelu_tanh_grad_without_the_chain_factor_is_caught(monkeypatch):
+    def grad(z, form="erf"):
+        t = np.tanh(ost._TANH_C * (z + ost._TANH_A * np.asarray(z) ** 3))
+        return 0.5 * (1.0 + t) + 0.5 * z * (1.0 - t * t)
+    monkeypatch.setattr(ost, "gelu_grad", grad)
+    with pytest.raises(AssertionError):
+        pin_gelu.test_gelu_tanh_grad_central_differences()
