@@ -43,7 +43,7 @@ the plain reading (stated again in the design notes):
 """
 from __future__ import annotations
 
-from typing import Dict, List, Optional, Sequence, Tuple
+from typing import Dict, List, Optional, Tuple
 
 from .schedules import Op, simulate
 

@@ -24,7 +24,7 @@ Stage graphs (readings recorded in the design notes):
 """
 from __future__ import annotations
 
-from typing import Dict, List, Sequence, Tuple
+from typing import Dict, List, Sequence
 
 import numpy as np
 from scipy.special import erf

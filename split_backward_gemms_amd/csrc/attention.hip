@@ -491,7 +491,6 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
       else dma16(rd, __builtin_amdgcn_readfirstlane(lds_addr(sld)), off);
     }
   };
-  (void)kv_wave_max;
   fetch(sQ0, sG0, sLD0, 0);
   if (nqb > 1) fetch(sQ1, sG1, sLD1, 1);
   wait_vm_barrier<0>();
