@@ -3,8 +3,8 @@
 
 A step is one whole schedule: every emulated stage's F, B and W passes for
 every microbatch (the workload's handcrafted order by default), run through
-zb_run_schedule with the emulated stages spread over two HIP streams (stage s
-on stream s mod 2; --streams), then the step boundary
+zb_run_schedule with the emulated stages spread over two HIP streams (stages
+2k and 2k+1 on stream k mod 2; --streams), then the step boundary
 (zb_grad_flush) of every stage.  Inputs, weights and gradient buffers are
 resident in HBM before timing starts.  --order zb1p / zb2p runs the automatic
 scheduler's order, built from pass times measured on this device and the
@@ -101,7 +101,7 @@ def main() -> int:
     ap.add_argument("--workload", default="gpt_mlp_h2048")
     ap.add_argument("--order", default=None)
     ap.add_argument("--streams", type=int, default=2,
-                    help="HIP streams the emulated stages are spread over (stage s on stream s mod n; "
+                    help="HIP streams the emulated stages are spread over (stages 2k, 2k+1 on stream k mod n; "
                          "2 measured fastest on every workload, P gives one per stage)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
@@ -198,7 +198,7 @@ def main() -> int:
     if a.mode == "full":
         # Headline: the emulated stages spread over a few HIP streams, so independent
         # stages overlap the way pipeline stages on separate devices would.  Two
-        # streams (stage s on stream s mod 2) measured fastest on every workload:
+        # streams (stages 2k, 2k+1 on stream k mod 2) measured fastest on every workload:
         # one stream per stage runs more kernels at once than the chip gains from.
         pipe = EmulatedPipeline(w, ws, ops=ops, device=dev, stage_streams=True, recompute_act=probe_recompute,
                                 n_streams=a.streams)
@@ -363,7 +363,8 @@ def main() -> int:
         "config": {"workload": w0.name, "devices": n_dev, "stages_emulated": w.n_stages, "n_micro": w.n_micro,
                    "layers_per_stage": w.n_layers, "hidden": w.hidden, "ffn": w.ffn, "seq": w.seq,
                    "micro_batch": w.micro_batch, "order": order,
-                   "executor": f"{min(a.streams, P)} HIP streams, stage s on stream s mod {min(a.streams, P)}",
+                   "executor": (f"{P} HIP streams, one per stage" if a.streams >= P else
+                                f"{a.streams} HIP streams, stages 2k, 2k+1 on stream k mod {a.streams}"),
                    "recompute_act": recompute_act if recompute_act is not None else pipe.recompute_act,
                    "flops_per_step": flops},
         "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS if a.mode == "full" else None,
