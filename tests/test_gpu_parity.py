@@ -81,6 +81,40 @@ def test_linear_passes_exact_on_integers(T, K, N):
     assert np.array_equal(DW.cpu().numpy(), (dw_ref - dw0).astype(np.float32))
 
 
+def _random_shape(seed: int):
+    """A seeded shape: sizes multiples of 8, most of them ragged against every
+    tile, T * K * N at most 2e9 (the fp64 reference stays quick)."""
+    rng = np.random.default_rng([2024, seed])
+    while True:
+        T, K, N = (8 * int(v) for v in rng.integers(1, 513, size=3))
+        if T * K * N <= 2_000_000_000:
+            return T, K, N
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_linear_passes_exact_on_random_shapes(seed):
+    T, K, N = _random_shape(seed)
+    print(f"linear exact seed={seed} T={T} K={K} N={N}", flush=True)
+    x = si.integer_valued((T, K), -2, 2, seed=10 * seed + 1)
+    w = si.integer_valued((K, N), -2, 2, seed=10 * seed + 2)
+    dy = si.integer_valued((T, N), -2, 2, seed=10 * seed + 3)
+    dw0 = si.integer_valued((K, N), -100, 100, seed=10 * seed + 4)
+    X, Wt, DY = (upload(a, "bf16", "cuda") for a in (x, w, dy))
+    Y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    DX = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    DW = torch.from_numpy(dw0).cuda()
+    zb.zb_linear_forward(X, Wt, Y, _stream())
+    zb.zb_linear_backward_input(DY, Wt, DX, _stream())
+    zb.zb_linear_backward_weight(X, DY, DW, True, _stream())
+    torch.cuda.synchronize()
+    y_ref = ost.linear_forward(x.astype(np.float64), w.astype(np.float64))
+    dx_ref = ost.linear_backward_input(dy.astype(np.float64), w.astype(np.float64))
+    dw_ref = dw0 + ost.linear_backward_weight(x.astype(np.float64), dy.astype(np.float64))
+    assert np.array_equal(Y.view(torch.int16).cpu().numpy().view(np.uint16), si.to_bf16_bits(y_ref.astype(np.float32)))
+    assert np.array_equal(DX.view(torch.int16).cpu().numpy().view(np.uint16), si.to_bf16_bits(dx_ref.astype(np.float32)))
+    assert np.array_equal(DW.cpu().numpy(), dw_ref.astype(np.float32))
+
+
 @pytest.mark.parametrize("T,K,N", [(520, 264, 392), (1024, 2048, 1024)])
 def test_linear_passes_random_within_tolerance(T, K, N):
     rng = np.random.default_rng(5)
