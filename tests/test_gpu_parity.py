@@ -269,8 +269,11 @@ REDUCED = {
 
 
 def _pipeline_vs_oracle(name, order, recompute_act, gelu="erf"):
-    w = REDUCED[name].replace(gelu=gelu)
-    print(f"pipeline parity {name} {order} recompute_act={recompute_act} gelu={gelu}", flush=True)
+    _pipeline_vs_oracle_w(REDUCED[name].replace(gelu=gelu), order, recompute_act)
+
+
+def _pipeline_vs_oracle_w(w, order, recompute_act):
+    print(f"pipeline parity {w} {order} recompute_act={recompute_act}", flush=True)
     ws, xs, dys = _inputs(w)
     pipe, y, dx, dw, _ = _run(w, ws, xs, dys, order, recompute_act=recompute_act)
     assert pipe.recompute_act == recompute_act
@@ -302,6 +305,32 @@ def test_pipeline_matches_oracle(name, order):
 @pytest.mark.parametrize("order", ["zbh1", "1f1b"])
 def test_pipeline_matches_oracle_rebuilt_activation(name, order):
     _pipeline_vs_oracle(name, order, 1)
+
+
+def _random_workload(seed: int):
+    """A seeded small stage: full layers (1-3 heads) on even seeds, MLP linears
+    on odd ones; ragged sequence lengths, 1-3 sequences per microbatch; at most
+    four full layers in a chain (the bf16 residual stream's rounding grows with
+    depth)."""
+    rng = np.random.default_rng([77, seed])
+    if seed % 2 == 0:
+        heads = int(rng.integers(1, 4))
+        base, hidden = si.WORKLOADS["gpt_full_h4096"], 128 * heads
+        P, L = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    else:
+        heads = 0
+        base, hidden = si.WORKLOADS["gpt_mlp_h2048"], 8 * int(rng.integers(8, 49))
+        P, L = int(rng.integers(1, 4)), int(rng.integers(1, 3))
+    seq, mb = 8 * int(rng.integers(1, 81)), int(rng.integers(1, 4))
+    ffn = 8 * int(rng.integers(hidden // 8, 4 * hidden // 8 + 1))
+    return base.replace(name=f"{base.name}_random{seed}", hidden=hidden, ffn=ffn, n_heads=heads or base.n_heads,
+                        seq=seq, micro_batch=mb, n_micro=int(rng.integers(2, 6)), n_stages=P, n_layers=L)
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("order", ["zbh1", "1f1b"])
+def test_pipeline_matches_oracle_on_random_stages(seed, order):
+    _pipeline_vs_oracle_w(_random_workload(seed), order, 0)
 
 
 @pytest.mark.parametrize("recompute_act", [0, 1])
