@@ -132,10 +132,14 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   return total % XCDS == 0 ? (b % XCDS) * (total / XCDS) + b / XCDS : b;
 }
 
-// Logical tile index -> output tile.  Tiles go in groups of 8 tile-rows so
-// that neighbours reuse A rows and B columns.
+// Logical tile index -> output tile.  Tiles go in groups of 4 tile-rows, down
+// each column of the group and then across, so neighbours reuse A rows and B
+// columns; the 32 tiles an XCD works on at once then cover 4 tile-rows by 8
+// tile-columns, whose output rows are written in longer contiguous runs than
+// with 8 by 4 (measured 3-3.5% faster whole steps at T = 1024 and 2048; groups
+// of 2 lose at T = 4096, of 1 everywhere).
 __device__ __forceinline__ void tile_raster(const Params& p, int& tm, int& tn, int b) {
-  const int G = 8;
+  const int G = 4;
   const int per_group = G * p.nbn;
   const int group = b / per_group;
   const int first_m = group * G;
