@@ -6,16 +6,20 @@ every microbatch (the workload's handcrafted order by default), run through
 zb_run_schedule with the emulated stages spread over two HIP streams (stages
 2k and 2k+1 on stream k mod 2; --streams), then the step boundary
 (zb_grad_flush) of every stage.  Inputs, weights and gradient buffers are
-resident in HBM before timing starts.  --order zb1p / zb2p runs the automatic
+resident in HBM before timing starts.  The default workload is the largest
+single-GPU one: 8 emulated stages of 4 full layers (h = 4096, 32 heads,
+seq 4096), 32 microbatches, ZB-H2.  --order zb1p / zb2p runs the automatic
 scheduler's order, built from pass times measured on this device and the
 stages' own stash sizes, with 1F1B's activation budget or twice it; --order
 zbv runs the model cut into 2P chunk stages in the V placement's order.
 
 Reported value: stage F+B+W TFLOP/s = algorithmic GEMM (+ attention) FLOPs of
-the step / wall time.  Also reported: % of the bf16 dense MFMA peak, the
-split-backward overhead against the same step in 1F1B order with unsplit
-backwards, the dominant kernel's roofline and the fp64 CPU oracle's rate on a
-bounded sample of the same workload.
+the step / wall time.  Also reported: % of the bf16 dense MFMA peak; the
+split-backward overhead against the fused backward (1F1B order, unsplit
+passes) with the same W kernel issued once per linear on both sides, and with
+the split W pass grouped as it runs in the headline; the dominant kernel's
+roofline; a planned-versus-observed join of one traced headline step; and the
+fp64 CPU oracle's rate on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--order zbh1|zb1p|zb2p|zbv|...]
 """
@@ -26,6 +30,7 @@ import json
 import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -33,9 +38,12 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
-
 # Automatic orders: activation budget in units of P microbatches' stash (ZB-1p, ZB-2p).
 HEURISTIC = {"zb1p": 1, "zb2p": 2}
+# Secondary phases (one-stream passes, fused baseline, kernel timing) run a
+# fixed number of steps whatever --steps is, so the whole run stays within a
+# few minutes on the largest workload (about 5 s per step).
+SHORT_STEP_MS = 500.0
 
 
 def log(msg: str) -> None:
@@ -50,22 +58,27 @@ def gpu_step_flops(w) -> float:
 def pmc_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE / WRITE_SIZE, calibrated against a plain copy), or None
-    when there is none or the GEMM source changed since it was taken."""
+    when there is none or a kernel source changed since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"pmc_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    src = open(os.path.join(ROOT, d["source"]), "rb").read()
-    if hashlib.sha256(src).hexdigest()[:16] != d["source_sha256_16"]:
+    srcs = d["source"] if isinstance(d["source"], list) else [d["source"]]
+    h = hashlib.sha256()
+    for src in srcs:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if h.hexdigest()[:16] != d["source_sha256_16"]:
         return None
     k = d["kernels"].get(kernel)
     return None if k is None else k["hbm_bytes_per_launch"]
 
 
 def cpu_baseline(w, budget_s: float = 12.0) -> dict:
-    """The fp64 oracle (as it stands) on a bounded sample: whole F+B+W units of
-    one stage and one microbatch at full size, repeated until budget_s elapses."""
+    """The fp64 oracle (as it stands) on a bounded sample: F+B+W of whole
+    layers of one stage and one microbatch at full size (one layer at a time
+    for full layers, whose s x s attention probabilities the oracle keeps),
+    repeated until budget_s elapses."""
     import numpy as np
     import synthetic_inputs as si
     from oracle import stage as ost
@@ -74,31 +87,68 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
         cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
-    ws = ost.to64(si.stage_weights(w, 0))
-    x = si.stage_input(w, 0).astype(np.float64)
-    dy = si.last_stage_grad(w, 0).astype(np.float64)
+    unit = w.replace(n_layers=1) if w.kind == si.FULL else w
+    ws = ost.to64(si.stage_weights(unit, 0))
+    x = si.stage_input(unit, 0).astype(np.float64)
+    dy = si.last_stage_grad(unit, 0).astype(np.float64)
     units = 0
     t0 = time.perf_counter()
     while True:
-        _, saved = ost.stage_forward(w, ws, x)
-        _, grads = ost.stage_backward_input(w, ws, saved, dy)
-        ost.stage_backward_weight(w, saved, grads)
+        _, saved = ost.stage_forward(unit, ws, x)
+        _, grads = ost.stage_backward_input(unit, ws, saved, dy)
+        for sv in saved:
+            sv.pop("probs", None)
+        ost.stage_backward_weight(unit, saved, grads)
         units += 1
         el = time.perf_counter() - t0
         if el >= budget_s or units >= 8:
             break
-    flops = units * (3 * w.gemm_flops_per_pass() + w.attn_flops_fwd() + w.attn_flops_bwd())
+    flops = units * (3 * unit.gemm_flops_per_pass() + unit.attn_flops_fwd() + unit.attn_flops_bwd())
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{units} x (F+B+W of one stage, one microbatch, {w.n_layers} layers) at full size, fp64 numpy, "
-                      f"{el:.1f} s"}
+            "sample": f"{units} x (F+B+W of {unit.n_layers} layer(s) of one stage, one microbatch) at full size "
+                      f"(T={unit.tokens}, h={unit.hidden}), fp64 numpy, {el:.1f} s"}
+
+
+def draw_inputs(w, threads: int = 8):
+    import synthetic_inputs as si
+    ws = [si.stage_weights(w, s) for s in range(w.n_stages)]
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        xs = list(ex.map(lambda j: si.stage_input(w, j), range(w.n_micro)))
+        dys = list(ex.map(lambda j: si.last_stage_grad(w, j), range(w.n_micro)))
+    return ws, xs, dys
+
+
+def roofline_of(kern, workload: str) -> dict:
+    """The dominant kernel (largest total time) against the MFMA peak when its
+    algorithmic intensity is above the ridge point, against HBM otherwise."""
+    top = kern[0]
+    avg_ms = top["total_ms"] / top["launches"]
+    per_launch_flops = top["flops"] / top["launches"]
+    per_launch_bytes = top["bytes"] / top["launches"]
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    intensity = per_launch_flops / per_launch_bytes if per_launch_bytes > 0 else float("inf")
+    if intensity >= ridge:
+        achieved = per_launch_flops / (avg_ms / 1e3) / 1e12
+        r = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+             "frac": achieved / PEAK_BF16_TFLOPS}
+    else:
+        achieved = per_launch_bytes / (avg_ms / 1e3) / 1e9
+        r = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": achieved / PEAK_HBM_GBS}
+    r.update({"traffic": pmc_traffic(workload, top["name"]), "kernel": top["name"],
+              "avg_launch_us": avg_ms * 1e3, "flops_per_launch": per_launch_flops,
+              "bytes_per_launch": per_launch_bytes, "flop_per_byte": intensity, "ridge": ridge,
+              "tflops": per_launch_flops / (avg_ms / 1e3) / 1e12,
+              "measured_on": "one stream, hipEvent pair per launch on the launch's stream"})
+    return r
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gpt_mlp_h2048")
+    ap.add_argument("--steps", type=int, default=12)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="gpt_full_s4096")
     ap.add_argument("--order", default=None)
     ap.add_argument("--streams", type=int, default=2,
                     help="HIP streams the emulated stages are spread over (stages 2k, 2k+1 on stream k mod n; "
@@ -112,6 +162,11 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one plain device-to-device copy kernel of BYTES bytes (counter calibration)")
     a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py: this build measures one GPU's share of the pipeline only; --gpus {a.gpus} is not "
+              f"supported (the pipeline stages are emulated on one device, and no run here uses a second GPU).",
+              file=sys.stderr)
+        return 2
     if a.calibrate_copy:
         import torch
         n = a.calibrate_copy // 4
@@ -122,16 +177,12 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": 4 * n}))
         return 0
-    if a.gpus != 1:
-        print(f"bench.py: this build measures one GPU's share of the pipeline only; --gpus {a.gpus} is not "
-              f"supported (stages are emulated on one device).", file=sys.stderr)
-        return 2
 
-    import numpy as np
     import torch
 
     import split_backward_gemms_amd as zb
     import synthetic_inputs as si
+    from split_backward_gemms_amd import tracing
     from split_backward_gemms_amd.pipeline import (EmulatedPipeline, heuristic_ops, pass_times_us,
                                                    stash_per_microbatch, upload, zbv_ops)
 
@@ -144,32 +195,37 @@ def main() -> int:
     torch.cuda.set_device(0)
     log(f"workload {w.name}: P={w.n_stages} m={w.n_micro} layers={w.n_layers} h={w.hidden} T={w.tokens} {order}")
     t0 = time.perf_counter()
-    ws = [si.stage_weights(w, s) for s in range(w.n_stages)]
-    xs = [si.stage_input(w, j) for j in range(w.n_micro)]
-    dys = [si.last_stage_grad(w, j) for j in range(w.n_micro)]
+    ws, xs, dys = draw_inputs(w)
     log(f"inputs drawn in {time.perf_counter() - t0:.1f} s")
 
     P, m = w.n_stages, w.n_micro
     hand = w0.order if order in HEURISTIC else ("zbh1" if order == "zbv" else order)
     ops, sim = zb.zb_schedule_build(hand, P, m)
-    ops_fused, sim_fused = zb.zb_schedule_build("1f1b", P, m)
+    ops_fused, _ = zb.zb_schedule_build("1f1b", P, m)
+    X = [upload(x, w.dtype, dev) for x in xs]
+    DY = [upload(d, w.dtype, dev) for d in dys]
+    del xs, dys
+    flops = gpu_step_flops(w)
     torch.cuda.synchronize()
 
-    def timed(pipe, o, X, DY, y, dx, steps, warmup):
+    def timed(pipe, o, steps, warmup):
         for _ in range(warmup):
             pipe.run(o, X, DY, y, dx)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
+        t = time.perf_counter()
         for _ in range(steps):
             pipe.run(o, X, DY, y, dx)
         torch.cuda.synchronize()
-        return 1000.0 * (time.perf_counter() - t0) / steps
+        return 1000.0 * (time.perf_counter() - t) / max(1, steps)
 
-    X = [upload(x, w.dtype, dev) for x in xs]
-    DY = [upload(d, w.dtype, dev) for d in dys]
-    flops = gpu_step_flops(w)
+    def traced(pipe, o):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        tr, _ = pipe.run(o, X, DY, y, dx, trace=True)
+        torch.cuda.synchronize()
+        return tr, 1000.0 * (time.perf_counter() - t)
+
     heur = {}
-    probe_recompute = None
     if order in HEURISTIC or order == "zbv":
         # The automatic scheduler and ZB-V take the passes' measured times (one
         # stream, hipEvents) and the stages' own stash sizes.
@@ -184,7 +240,6 @@ def main() -> int:
         else:
             ops, hstats, choice, m_limit = heuristic_ops(probe.handles, P, m, times, HEURISTIC[order] * P)
         sim = hstats
-        probe_recompute = probe.recompute_act
         heur = {"pass_us": times, "m_limit_bytes": m_limit, "fill_balance": choice,
                 "sim_bubble_us": hstats["bubble"], "sim_makespan_us": hstats["makespan"]}
         log(f"{order}: pass times {times} us, M_limit {m_limit / 2**30:.2f} GiB per device, choice {choice}, "
@@ -193,92 +248,107 @@ def main() -> int:
         del probe, y, dx, tr
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-    fused = {}
+
+    out_extra = {}
     ms_per_step = tflops = float("nan")
     if a.mode == "full":
         # Headline: the emulated stages spread over a few HIP streams, so independent
-        # stages overlap the way pipeline stages on separate devices would.  Two
-        # streams (stages 2k, 2k+1 on stream k mod 2) measured fastest on every workload:
-        # one stream per stage runs more kernels at once than the chip gains from.
-        pipe = EmulatedPipeline(w, ws, ops=ops, device=dev, stage_streams=True, recompute_act=probe_recompute,
-                                n_streams=a.streams)
-        y, dx = pipe.io_buffers()
-        torch.cuda.synchronize()
-        log(f"device ready: workspace {pipe.workspace_bytes() / 2**30:.2f} GiB, "
-            f"{'A rebuilt for W' if pipe.recompute_act else 'A stashed'}")
-        ms_per_step = timed(pipe, ops, X, DY, y, dx, a.steps, a.warmup)
-        tflops = flops / (ms_per_step / 1000.0) / 1e12
-        log(f"{order}, {min(a.streams, P)} streams: {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s")
-    if a.mode == "full" and not a.no_fused:
-        pipe.plan(ops_fused)  # workspaces sized for the fused order
-        fms = timed(pipe, ops_fused, X, DY, y, dx, a.steps, a.warmup)
-        fused["ms_per_step_1f1b_unsplit"] = fms
-        fused["zb_vs_1f1b_speedup"] = fms / ms_per_step - 1.0
-        log(f"1f1b unsplit, {min(a.streams, P)} streams: {fms:.3f} ms/step")
-    recompute_act = None
-    if a.mode == "full":
-        recompute_act = pipe.recompute_act
-        pipe.close()
-        del pipe
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()  # hand the first pipeline's blocks back before the second allocates
-
-    # One shared stream: passes and kernels run in isolation, for the per-pass
-    # split overhead and the kernel roofline.
-    pipe = EmulatedPipeline(w, ws, ops=ops, device=dev, recompute_act=recompute_act)
+        # stages overlap the way pipeline stages on separate devices would.
+        pipe = EmulatedPipeline(w, ws, ops=ops, device=dev, stage_streams=True, n_streams=a.streams)
+    else:
+        pipe = EmulatedPipeline(w, ws, ops=ops, device=dev)
     del ws
     y, dx = pipe.io_buffers()
+    torch.cuda.synchronize()
+    log(f"device ready: workspace {pipe.workspace_bytes() / 2**30:.2f} GiB, "
+        f"{'A rebuilt for W' if pipe.recompute_act else 'A stashed'}")
     t_split = {}
     sim_measured = {}
+    join = None
     if a.mode == "full":
-        single_ms = timed(pipe, ops, X, DY, y, dx, max(2, a.steps // 2), 1)
-        tr, _ = pipe.run(ops, X, DY, y, dx, trace=True)
-        t_split = {k: sum(ms for (op, ms, _) in tr if op[1] == k) for k in "FBW"}
-        log(f"{order}, one stream: {single_ms:.3f} ms/step; passes {t_split}")
-        # Bubble rates the simulator gives across the devices at these measured
+        ms_per_step = timed(pipe, ops, a.steps, a.warmup)
+        tflops = flops / (ms_per_step / 1000.0) / 1e12
+        log(f"{order}, {min(a.streams, P)} streams: {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s")
+        short = ms_per_step < SHORT_STEP_MS
+        tr_multi, _ = traced(pipe, ops)
+        stream_of_stage = pipe.stream_index_of_stage()
+        if short and not a.no_fused:
+            pipe.plan(ops_fused)
+            fms = timed(pipe, ops_fused, max(2, a.steps // 2), 1)
+            out_extra["ms_per_step_1f1b_unsplit"] = fms
+            out_extra["zb_vs_1f1b_speedup"] = fms / ms_per_step - 1.0
+            log(f"1f1b unsplit, {min(a.streams, P)} streams: {fms:.3f} ms/step")
+
+        # One shared stream: passes run in isolation, for per-pass times, the
+        # split overhead and the plan's durations.
+        pipe.rebuild(ops, stage_streams=False)
+        reps = 2 if short else 1
+        if short:
+            timed(pipe, ops, 0, 1)
+        tr_one, wall_one = traced(pipe, ops)
+        t_split = {k: sum(ms for (op, ms, _) in tr_one if op[1] == k) for k in "FBW"}
+        log(f"{order}, one stream: {wall_one:.1f} ms/step; passes {t_split}")
+        join = tracing.join(ops, P, stream_of_stage, tr_multi, tracing.median_durations(tr_one))
+        log(f"plan vs observed ({join['streams']} streams): span {join['planned_span_ms']:.1f} planned, "
+            f"{join['observed_span_ms']:.1f} observed; dependency wait {join['dependency_wait_ms']}, "
+            f"resource wait {join['resource_wait_ms']}")
+        # Bubble rates the simulator gives across P devices at these measured
         # pass times (a ZB-V chunk counts as half a stage, in time and stash).
-        # An order with unsplit backwards (1F1B, GPipe) has no separate B and W
-        # times to feed it.
-    if a.mode == "full" and any(k in ("B", "W") for (_, k, _) in ops):
-        times = pass_times_us(tr)
-        cut = 2 if order == "zbv" else 1
-        st_times = tuple(cut * x for x in times)
-        ch_times = times if order == "zbv" else tuple(max(1, x // 2) for x in times)
-        m_b, m_w = (cut * v for v in stash_per_microbatch(pipe.handles))
-        for nm in ["1f1b", "zbh1"] + (["zbh2"] if m >= 2 * n_dev - 1 else []):
-            st = zb.zb_schedule_build(nm, n_dev, m, st_times)[1]
-            sim_measured[nm] = st["bubble"] / st["makespan"]
-        for nm, k in HEURISTIC.items():
-            st = zb.zb_schedule_heuristic(n_dev, m, st_times, m_b, m_w, k * n_dev * m_b + max(0, m_w - m_b))[1]
-            sim_measured[nm] = st["bubble"] / st["makespan"]
-        cb, cw = m_b // 2, m_w // 2
-        st = zb.zb_schedule_zbv(n_dev, m, ch_times, cb, cw, 2 * n_dev * cb + max(0, cw - cb))[1]
-        sim_measured["zbv"] = st["bubble"] / st["makespan"]
-        log(f"simulated bubble rates at measured pass times {times} us: "
-            + ", ".join(f"{k} {100 * v:.1f}%" for k, v in sim_measured.items()))
+        if any(k in ("B", "W") for (_, k, _) in ops):
+            times = pass_times_us(tr_one)
+            cut = 2 if order == "zbv" else 1
+            st_times = tuple(cut * x for x in times)
+            ch_times = times if order == "zbv" else tuple(max(1, x // 2) for x in times)
+            m_b, m_w = (cut * v for v in stash_per_microbatch(pipe.handles))
+            for nm in ["1f1b", "zbh1"] + (["zbh2"] if m >= 2 * n_dev - 1 else []):
+                st = zb.zb_schedule_build(nm, n_dev, m, st_times)[1]
+                sim_measured[nm] = st["bubble"] / st["makespan"]
+            for nm, k in HEURISTIC.items():
+                st = zb.zb_schedule_heuristic(n_dev, m, st_times, m_b, m_w, k * n_dev * m_b + max(0, m_w - m_b))[1]
+                sim_measured[nm] = st["bubble"] / st["makespan"]
+            cb, cw = m_b // 2, m_w // 2
+            st = zb.zb_schedule_zbv(n_dev, m, ch_times, cb, cw, 2 * n_dev * cb + max(0, cw - cb))[1]
+            sim_measured["zbv"] = st["bubble"] / st["makespan"]
+            log(f"simulated bubble rates at measured pass times {times} us: "
+                + ", ".join(f"{k} {100 * v:.1f}%" for k, v in sim_measured.items()))
+
+        if not a.no_fused and t_split.get("B", 0) > 0:
+            # Split overhead, like for like: the W pass issues one launch per linear,
+            # exactly as the fused backward does (same kernel, same launches).
+            pipe.rebuild(ops, stage_streams=False, w_per_linear=1)
+            if short:
+                timed(pipe, ops, 0, 1)
+            tr_pl, wall_pl = traced(pipe, ops)
+            t_pl = {k: sum(ms for (op, ms, _) in tr_pl if op[1] == k) for k in "FBW"}
+            pipe.rebuild(ops_fused, stage_streams=False, w_per_linear=0)
+            timed(pipe, ops_fused, 0, 1)
+            tr_fu, wall_fu = traced(pipe, ops_fused)
+            t_fu = {k: sum(ms for (op, ms, _) in tr_fu if op[1] == k) for k in "FU"}
+            out_extra.update({
+                "split_overhead_pass": (t_pl["B"] + t_pl["W"]) / t_fu["U"] - 1.0,
+                "split_overhead_pass_grouped_w": (t_split["B"] + t_split["W"]) / t_fu["U"] - 1.0,
+                "split_overhead_wall_one_stream": wall_pl / wall_fu - 1.0,
+                "split_overhead_wall_one_stream_grouped_w": wall_one / wall_fu - 1.0,
+                "ms_per_step_one_stream": wall_one,
+                "ms_per_step_one_stream_w_per_linear": wall_pl,
+                "ms_per_step_1f1b_unsplit_one_stream": wall_fu,
+                "pass_ms_w_per_linear": t_pl,
+                "pass_ms_1f1b": {"F": t_fu["F"], "U": t_fu["U"]},
+                "split_overhead_definition": "sum(t_B + t_W) of the split order / sum(t_U) of 1F1B's fused "
+                                             "backwards - 1, per-pass hipEvents on one stream; W issued with the "
+                                             "same kernel, one launch per linear, on both sides "
+                                             "(_grouped_w: the split W pass as one grouped launch)"})
+            log(f"split overhead (B+W vs U, same W launches): {100 * out_extra['split_overhead_pass']:.2f}%, "
+                f"grouped W {100 * out_extra['split_overhead_pass_grouped_w']:.2f}%; wall one stream "
+                f"{wall_pl:.1f} / {wall_one:.1f} (grouped) vs {wall_fu:.1f} ms")
+            pipe.rebuild(ops, stage_streams=False, w_per_linear=0)
     if a.mode != "full":
         pipe.run(ops, X, DY, y, dx)  # one untimed step before the kernel-timing phase
-    if a.mode == "full" and not a.no_fused:
-        pipe.plan(ops_fused)
-        fused_ms = timed(pipe, ops_fused, X, DY, y, dx, max(2, a.steps // 2), 1)
-        trf, _ = pipe.run(ops_fused, X, DY, y, dx, trace=True)
-        pipe.plan(ops)
-        t_f = {k: sum(ms for (op, ms, _) in trf if op[1] == k) for k in "FU"}
-        fused.update({"ms_per_step_one_stream": single_ms,
-                      "ms_per_step_1f1b_unsplit_one_stream": fused_ms,
-                      # an order with unsplit backwards has no B + W to compare
-                      "split_overhead_pass": ((t_split["B"] + t_split["W"]) / t_f["U"] - 1.0
-                                              if t_split["B"] + t_split["W"] > 0 else None),
-                      "split_overhead_wall_one_stream": single_ms / fused_ms - 1.0,
-                      "pass_ms_1f1b": {"F": t_f["F"], "U": t_f["U"]}})
-        so = fused["split_overhead_pass"]
-        log(f"1f1b unsplit, one stream: {fused_ms:.3f} ms/step; split overhead (B+W vs U) "
-            + (f"{100 * so:.2f}%" if so is not None else "n/a (unsplit order)"))
 
-    # kernel-level timing over profiled steps of the measured order (one stream)
+    # Kernel-level timing over one profiled step of the measured order (one stream).
     zb.zb_prof_reset()
     zb.zb_prof_enable(True)
-    prof_steps = 2
+    prof_steps = 1
     for _ in range(prof_steps):
         pipe.run(ops, X, DY, y, dx)
     torch.cuda.synchronize()
@@ -286,40 +356,18 @@ def main() -> int:
     kern = zb.zb_prof_read()
     zb.zb_prof_reset()
     kern.sort(key=lambda r: -r["total_ms"])
-    for r in kern[:10]:
+    for r in kern[:12]:
         log(f"  {r['name']:<28} {r['launches']:6d} launches {r['total_ms'] / prof_steps:8.3f} ms/step "
             f"{r['flops'] / r['total_ms'] / 1e9:8.1f} TFLOP/s")
     gemm_ms = sum(r["total_ms"] for r in kern if r["name"].startswith("gemm")) / prof_steps
     gemm_flops = sum(r["flops"] for r in kern if r["name"].startswith("gemm")) / prof_steps
-    top = kern[0]
-    avg_ms = top["total_ms"] / top["launches"]
-    per_launch_flops = top["flops"] / top["launches"]
-    per_launch_bytes = top["bytes"] / top["launches"]
-    # The dominant kernel's bound: MFMA when its algorithmic intensity is above
-    # the ridge point (peak FLOP/s over peak HBM bytes/s), HBM below it.
-    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    intensity = per_launch_flops / per_launch_bytes if per_launch_bytes > 0 else float("inf")
-    if intensity >= ridge:
-        achieved = per_launch_flops / (avg_ms / 1e3) / 1e12
-        roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": achieved / PEAK_BF16_TFLOPS}
-    else:
-        achieved = per_launch_bytes / (avg_ms / 1e3) / 1e9
-        roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": achieved / PEAK_HBM_GBS}
-    roofline.update({"traffic": pmc_traffic(w0.name, top["name"]), "kernel": top["name"],
-                     "avg_launch_us": avg_ms * 1e3, "flops_per_launch": per_launch_flops,
-                     "bytes_per_launch": per_launch_bytes, "flop_per_byte": intensity, "ridge": ridge,
-                     "tflops": per_launch_flops / (avg_ms / 1e3) / 1e12,
-                     "measured_on": "one stream, hipEvent pair per launch"})
+    roofline = roofline_of(kern, w0.name)
     kernels = [{"name": r["name"], "launches_per_step": r["launches"] / prof_steps,
                 "ms_per_step": r["total_ms"] / prof_steps,
                 "tflops": r["flops"] / r["total_ms"] / 1e9} for r in kern]
 
-    # Optimizer step with post-update validation (outside the step above): the
-    # staged gradient-state reduce and optimistic AdamW of every stage, then the
-    # validation, once where nothing rolls back and once where every stage but
-    # the last must roll back and step again.
+    # Optimizer step with post-update validation (outside the step above), where
+    # the moments fit beside the stash.
     optim = None
     n_params = sum(int(t.numel()) for ws_ in pipe.weights for t in ws_)
     if a.mode == "full" and not a.no_optim and 12 * n_params * 1.25 < torch.cuda.mem_get_info()[0]:
@@ -346,6 +394,7 @@ def main() -> int:
             f"({optim['step_gbs']:.0f} GB/s), validate {res['no_rollback']['validate_ms']:.3f} ms, "
             f"with rollback {res['rollback']['validate_ms']:.2f} ms ({res['rollback']['stages_rolled_back']} stages)")
 
+    recompute_act = pipe.recompute_act
     pipe.close()
     out = {
         "metric": "stage F+B+W TFLOP/s",
@@ -361,14 +410,14 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w0.name, "devices": n_dev, "stages_emulated": w.n_stages, "n_micro": w.n_micro,
-                   "layers_per_stage": w.n_layers, "hidden": w.hidden, "ffn": w.ffn, "seq": w.seq,
-                   "micro_batch": w.micro_batch, "order": order,
+                   "layers_per_stage": w.n_layers, "hidden": w.hidden, "ffn": w.ffn, "heads": w.n_heads,
+                   "seq": w.seq, "micro_batch": w.micro_batch, "order": order,
                    "executor": (f"{P} HIP streams, one per stage" if a.streams >= P else
                                 f"{a.streams} HIP streams, stages 2k, 2k+1 on stream k mod {a.streams}"),
-                   "recompute_act": recompute_act if recompute_act is not None else pipe.recompute_act,
-                   "flops_per_step": flops},
+                   "recompute_act": recompute_act, "flops_per_step": flops},
         "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS if a.mode == "full" else None,
         "gemm_only_tflops": gemm_flops / (gemm_ms / 1e3) / 1e12 if gemm_ms > 0 else None,
+        "gemm_only_pct_of_peak": 100.0 * gemm_flops / (gemm_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS if gemm_ms > 0 else None,
         "pass_ms": t_split,
         "sim_bubble_unit_times": {hand: zb.zb_schedule_build(hand, n_dev, m)[1]["bubble"],
                                   "1f1b": zb.zb_schedule_build("1f1b", n_dev, m)[1]["bubble"]},
@@ -376,7 +425,9 @@ def main() -> int:
         "roofline": roofline,
         "kernels": kernels,
     }
-    out.update(fused)
+    out.update(out_extra)
+    if join:
+        out["plan_vs_observed"] = join
     if optim:
         out["optimizer"] = optim
     if heur:

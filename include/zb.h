@@ -90,6 +90,10 @@ typedef struct {
                       *    before W: 8 T ffn bytes less per layer for every
                       *    microbatch between F and B, one elementwise pass
                       *    more per W (A then comes from the bf16 Z).      */
+  int w_per_linear; /* 0: a W pass issues the weight gradients of all its
+                     *    linears as one grouped launch (they are independent);
+                     * 1: one launch of the same kernel per linear, as the
+                     *    unsplit backward issues them.  Same bits either way. */
 } zb_stage_desc;
 
 /* One pass of a schedule.  kind: 'F', 'B', 'W', or 'U' = unsplit backward
@@ -197,12 +201,12 @@ zb_status zb_schedule_validate(int P, int m, const zb_op* ops, int n_ops, int* b
 zb_status zb_schedule_peak_memory(const zb_op* ops, int n_ops, int stage,
                                   int64_t m_b, int64_t m_w, int64_t* peak);
 
-/* Timed event of a schedule, for zb_events_inspect (the audit's checker). */
+/* Timed event of a schedule, for zb_events_inspect. */
 typedef struct {
   int32_t id;
   int32_t stage;
   int32_t micro;
-  char kind;            /* 'F', 'B', 'W' (others allowed, ignored by the live count) */
+  char kind;            /* 'F', 'B', 'W', 'U' (others allowed, ignored by the ledger) */
   char pad_[3];
   double start;
   double end;
@@ -211,19 +215,29 @@ typedef struct {
 } zb_event;
 
 typedef struct {
-  double span;               /* latest end                                   */
-  double busy;               /* sum of (end - start)                         */
-  double bubble_ratio;       /* 1 - busy / (stage_count * span)              */
-  int64_t unfinished_activations;  /* per microbatch: F count minus released by B */
+  double span;               /* latest end (the schedule's time starts at 0)   */
+  double busy;               /* sum of (end - start)                           */
+  double bubble_ratio;       /* 1 - busy / (stage_count * span)                */
+  int64_t unfinished_activations;  /* (stage, micro) activations whose F ran and
+                                    * whose stash no W (or U) has released      */
+  int64_t peak_live_activations;   /* most activations one stage held at once,
+                                    * each from its F to the W that frees its stash */
 } zb_event_report;
 
-/* Checks timed events (host).  Rejects in this order: stage_count < 2 ->
- * ZB_E_ARG; a repeated id -> ZB_E_DUPLICATE; then event by event: stage
- * outside [0, stage_count) -> ZB_E_INVALID_STAGE, start < 0 or end <= start
- * -> ZB_E_INTERVAL, a dependency id absent -> ZB_E_MISSING, a dependency
- * ending after the event starts -> ZB_E_DEPENDENCY; then two events of one
- * stage that overlap -> ZB_E_OVERLAP.  *bad_index (host, may be NULL) names
- * the offending event (-1 if none). */
+/* Checks a schedule given as timed events (host), as the audit "Zero-Bubble
+ * Pipeline Parallelism, Proven" asks in "Validate the schedule as data" and
+ * "Budget activation lifetime".  Phases, first failure wins:
+ *   n < 1, a null array or stage_count < 1 -> ZB_E_ARG;
+ *   an id used twice -> ZB_E_DUPLICATE (*bad_index = its second use);
+ *   stage outside [0, stage_count) -> ZB_E_INVALID_STAGE (first in list order);
+ *   start < 0 or end <= start -> ZB_E_INTERVAL (first in list order);
+ *   a dependency id naming no event -> ZB_E_MISSING (first in list order);
+ *   an event starting before one of its producers ends -> ZB_E_DEPENDENCY
+ *     (the violating event with the earliest start, ties to list order);
+ *   two events of one stage overlapping in time -> ZB_E_OVERLAP (over every
+ *     overlapping pair, the later-starting event, ties to the later in the
+ *     list; the earliest such start, ties to list order).
+ * *bad_index (host, may be NULL) names the offending event (-1 if none). */
 zb_status zb_events_inspect(const zb_event* events, int n, int stage_count,
                             zb_event_report* report, int* bad_index);
 
@@ -298,9 +312,23 @@ zb_status zb_backward_input(zb_stage* st, int mb, const void* dy, void* dx);
 zb_status zb_backward_weight(zb_stage* st, int mb);
 
 /* Unsplit backward (B and W of mb as one pass, each linear's input gradient
- * and weight gradient back to back): the fused baseline.  Same kernels and
- * the same bits as B followed by W. */
+ * and weight gradient back to back): the fused baseline.  Every weight
+ * gradient goes out as its own launch of the kernel the W pass uses (the W
+ * pass groups them unless w_per_linear is set), so a comparison with B + W
+ * measures the deferral and not a kernel difference; same bits as B then W. */
 zb_status zb_backward_unsplit(zb_stage* st, int mb, const void* dy, void* dx);
+
+/* Stage-boundary taps, for stage-by-stage checks ("Zero-Bubble Pipeline
+ * Parallelism, Proven", section "Split backward without changing the update":
+ * keep per-stage results so the first divergent one can be found).  y_tap and
+ * dx_tap are host arrays of n_micro device pointers ([T, h] each, either
+ * array may be NULL): after F(mb) the stage output is copied to y_tap[mb],
+ * after B(mb) (or U) the stage input gradient to dx_tap[mb], on the stage's
+ * stream before any hand-off event is recorded.  Passing NULL for both removes
+ * the taps.  The pointers are copied; the buffers stay caller-owned and must
+ * outlive the passes that write them.  Errors: ZB_E_ARG (a null entry in a
+ * non-null array). */
+zb_status zb_stage_set_taps(zb_stage* st, void* const* y_tap, void* const* dx_tap);
 
 /* ------------------------------------------------------------------------
  * Optimizer step with post-update validation (Zero Bubble Pipeline
@@ -391,6 +419,15 @@ zb_status zb_run_schedule(zb_stage* const* stages, int P, const zb_op* ops, int 
 /* Text of the calling thread's last error ("" if none); names the first
  * violating op index for schedule errors. */
 const char* zb_last_error(void);
+
+/* Debug mode: when on (or when the environment variable ZB_DEBUG_SYNC is set
+ * to a non-zero value at library load), every pass (zb_forward,
+ * zb_backward_input, zb_backward_weight, zb_backward_unsplit and each op of
+ * zb_run_schedule) synchronises its stream and checks for a device error
+ * afterwards, returning ZB_E_HIP that names the pass.  Off by default: it
+ * serialises the host with the device. */
+void zb_set_debug_sync(int on);
+int zb_get_debug_sync(void);
 
 /* Release the stage object (not the caller's buffers).  Enqueued work must have
  * finished. */

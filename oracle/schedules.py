@@ -348,47 +348,89 @@ class ScheduleError(Exception):
     pass
 
 
+def _interval_ok(t) -> bool:
+    return t["start"] >= 0 and t["end"] > t["start"]
+
+
 def inspect_events(tasks: Sequence[dict], stage_count) -> dict:
-    """Checks a timed schedule given as bounded events ([AUD] "Validate the
-    schedule as data").  Each task: id, stage, micro, kind, start, end,
-    optional depends_on.  Rejects, in this order: a stage count below 2,
-    repeated ids, then task by task an unknown stage, an empty or negative
-    interval, a dependency that is not in the list or ends after the task
-    starts; then two tasks of one stage that overlap.  Reports the span
-    (latest end), the idle fraction 1 - busy / (stages * span) and how many
-    forward activations no B has released (counted per microbatch)."""
-    if not isinstance(stage_count, int) or isinstance(stage_count, bool) or stage_count < 2:
+    """Checks a schedule given as timed events, following the prose of [AUD]
+    "Validate the schedule as data" (reject duplicate ids, unknown stages,
+    invalid intervals, missing dependencies, consumers that begin before their
+    producers end, and overlapping work on one stage; report span, busy time,
+    the idle ratio under a stated denominator and the activations still held)
+    and "Budget activation lifetime" (an activation is held from its F to the
+    W that consumes the stash its B leaves).
+
+    Each task: id, stage, micro, kind, start, end, optional depends_on.
+    Checks run in phases; within a phase the reported task is fixed as stated:
+      1. stage_count < 1                          -> invalid_stage_count
+      2. an id seen before                        -> duplicate_task (its second use)
+      3. stage outside [0, stage_count)           -> invalid_stage  (first in list order)
+      4. start < 0 or end <= start                -> invalid_interval (first in list order)
+      5. a dependency id that names no task       -> missing_dependency (first in list order)
+      6. a task starting before a producer ends   -> dependency_violation: the violating
+                                                     task with the earliest start, ties to
+                                                     the list order
+      7. two tasks of one stage overlapping       -> stage_overlap: of every overlapping
+                                                     pair the later-starting task (ties: later
+                                                     in the list); the smallest (start, index)
+    Report: span = latest end (time starts at 0), busy = sum of durations,
+    bubble_ratio = 1 - busy / (stage_count * span), unfinished_activations =
+    (stage, micro) activations whose F has run but whose stash no W (or
+    unsplit U) has released, peak_live_activations = the most held at once by
+    one stage.  Written as plain brute force over all tasks and pairs.
+    """
+    if not isinstance(stage_count, int) or isinstance(stage_count, bool) or stage_count < 1:
         raise ScheduleError("invalid_stage_count")
-    by_id = {}
-    for t in tasks:
-        by_id[t["id"]] = t
-    if len(by_id) != len(tasks):
-        raise ScheduleError("duplicate_task")
-    for t in tasks:
+    n = len(tasks)
+    for i in range(n):
+        for k in range(i):
+            if tasks[k]["id"] == tasks[i]["id"]:
+                raise ScheduleError("duplicate_task", i)
+    for i, t in enumerate(tasks):
         st = t["stage"]
-        if not isinstance(st, int) or isinstance(st, bool) or st < 0 or st >= stage_count:
-            raise ScheduleError("invalid_stage")
-        if not (t["start"] >= 0 and t["end"] > t["start"]):
-            raise ScheduleError("invalid_interval")
-        for dep_id in t.get("depends_on", []):
-            dep = by_id.get(dep_id)
-            if dep is None:
-                raise ScheduleError("missing_dependency")
-            if dep["end"] > t["start"]:
-                raise ScheduleError("dependency_violation")
-    for st in range(stage_count):
-        ts = sorted((t for t in tasks if t["stage"] == st), key=lambda t: t["start"])
-        for a, b in zip(ts, ts[1:]):
-            if a["end"] > b["start"]:
-                raise ScheduleError("stage_overlap")
+        if not isinstance(st, int) or isinstance(st, bool) or not 0 <= st < stage_count:
+            raise ScheduleError("invalid_stage", i)
+    for i, t in enumerate(tasks):
+        if not _interval_ok(t):
+            raise ScheduleError("invalid_interval", i)
+    ids = [t["id"] for t in tasks]
+    for i, t in enumerate(tasks):
+        for d in t.get("depends_on", []):
+            if d not in ids:
+                raise ScheduleError("missing_dependency", i)
+    violators = []
+    for i, t in enumerate(tasks):
+        producers = [tasks[ids.index(d)] for d in t.get("depends_on", [])]
+        if any(p["end"] > t["start"] for p in producers):
+            violators.append((t["start"], i))
+    if violators:
+        raise ScheduleError("dependency_violation", min(violators)[1])
+    overlaps = []
+    for i in range(n):
+        for k in range(n):
+            a, b = tasks[i], tasks[k]
+            if i == k or a["stage"] != b["stage"]:
+                continue
+            later = (b["start"], k) > (a["start"], i)
+            if later and a["start"] < b["end"] and b["start"] < a["end"]:
+                overlaps.append((b["start"], k))
+    if overlaps:
+        raise ScheduleError("stage_overlap", min(overlaps)[1])
     span = max(t["end"] for t in tasks)
     busy = sum(t["end"] - t["start"] for t in tasks)
-    live: Dict[int, int] = {}
-    for t in tasks:
+    # Activation ledger: walk the tasks by start time (ties in list order).
+    held = {}
+    peak = 0
+    for _, i in sorted((t["start"], i) for i, t in enumerate(tasks)):
+        t = tasks[i]
+        key = (t["stage"], t["micro"])
         if t["kind"] == "F":
-            live[t["micro"]] = live.get(t["micro"], 0) + 1
-        elif t["kind"] == "B":
-            live[t["micro"]] = max(0, live.get(t["micro"], 0) - 1)
+            held[key] = held.get(key, 0) + 1
+        elif t["kind"] in ("W", "U"):
+            held[key] = max(0, held.get(key, 0) - 1)
+        peak = max(peak, sum(v for (s, _), v in held.items() if s == t["stage"]))
     return {"span": span, "busy": busy,
             "bubble_ratio": 1 - Fraction(busy) / (stage_count * Fraction(span)),
-            "unfinished_activations": sum(live.values())}
+            "unfinished_activations": sum(held.values()),
+            "peak_live_activations": peak}

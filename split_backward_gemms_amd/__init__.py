@@ -47,7 +47,7 @@ class zb_adamw(C.Structure):
 class zb_stage_desc(C.Structure):
     _fields_ = [("kind", C.c_int), ("dtype", C.c_int), ("n_layers", C.c_int), ("hidden", C.c_int),
                 ("ffn", C.c_int), ("n_heads", C.c_int), ("seq", C.c_int), ("micro_batch", C.c_int),
-                ("n_micro", C.c_int), ("gelu", C.c_int), ("recompute_act", C.c_int)]
+                ("n_micro", C.c_int), ("gelu", C.c_int), ("recompute_act", C.c_int), ("w_per_linear", C.c_int)]
 
 
 class zb_op(C.Structure):
@@ -70,7 +70,7 @@ class zb_event(C.Structure):
 
 class zb_event_report(C.Structure):
     _fields_ = [("span", C.c_double), ("busy", C.c_double), ("bubble_ratio", C.c_double),
-                ("unfinished_activations", C.c_int64)]
+                ("unfinished_activations", C.c_int64), ("peak_live_activations", C.c_int64)]
 
 
 class zb_trace_rec(C.Structure):
@@ -122,6 +122,9 @@ def lib():
             "zb_backward_input": (I, [P, I, P, P]),
             "zb_backward_weight": (I, [P, I]),
             "zb_backward_unsplit": (I, [P, I, P, P]),
+            "zb_stage_set_taps": (I, [P, C.POINTER(P), C.POINTER(P)]),
+            "zb_set_debug_sync": (None, [I]),
+            "zb_get_debug_sync": (I, []),
             "zb_grad_flush": (I, [P, C.POINTER(I)]),
             "zb_stage_optim_bind": (I, [P, C.POINTER(zb_adamw), C.POINTER(P), C.POINTER(P), C.POINTER(P),
                                         C.POINTER(P)]),
@@ -155,7 +158,8 @@ def exported_symbols() -> List[str]:
             "zb_schedule_zbv", "zb_schedule_simulate_interleaved", "zb_schedule_validate", "zb_schedule_peak_memory",
             "zb_events_inspect", "zb_stage_create", "zb_stage_class_bytes", "zb_stage_workspace_bytes",
             "zb_stage_bind_workspace", "zb_stage_input_slot", "zb_stage_grad_slot", "zb_forward",
-            "zb_backward_input", "zb_backward_weight", "zb_backward_unsplit", "zb_grad_flush",
+            "zb_backward_input", "zb_backward_weight", "zb_backward_unsplit", "zb_stage_set_taps",
+            "zb_set_debug_sync", "zb_get_debug_sync", "zb_grad_flush",
             "zb_stage_optim_bind", "zb_stage_grad_state", "zb_stage_optim_step", "zb_stage_optim_validate",
             "zb_stage_optim_rollback",
             "zb_run_schedule", "zb_last_error", "zb_stage_destroy", "zb_prof_enable", "zb_prof_reset",
@@ -302,15 +306,17 @@ def zb_events_inspect(tasks: Sequence[dict], stage_count: int):
     if st != ZB_OK:
         return st, None, bad.value
     return st, {"span": rep.span, "busy": rep.busy, "bubble_ratio": rep.bubble_ratio,
-                "unfinished_activations": rep.unfinished_activations}, -1
+                "unfinished_activations": rep.unfinished_activations,
+                "peak_live_activations": rep.peak_live_activations}, -1
 
 
 # -------------------------------------------------------------- stage layer
 
 def make_desc(kind: int, dtype: int, n_layers: int, hidden: int, ffn: int, n_heads: int, seq: int,
-              micro_batch: int, n_micro: int, gelu: int = ZB_GELU_ERF, recompute_act: int = 0) -> zb_stage_desc:
+              micro_batch: int, n_micro: int, gelu: int = ZB_GELU_ERF, recompute_act: int = 0,
+              w_per_linear: int = 0) -> zb_stage_desc:
     return zb_stage_desc(kind, dtype, n_layers, hidden, ffn, n_heads, seq, micro_batch, n_micro, gelu,
-                         recompute_act)
+                         recompute_act, w_per_linear)
 
 
 def zb_stage_create(desc: zb_stage_desc, stage_index: int, weights: Sequence, dw: Sequence, stream=None) -> int:
@@ -368,6 +374,22 @@ def zb_backward_weight(stage: int, mb: int) -> None:
 
 def zb_backward_unsplit(stage: int, mb: int, dy, dx) -> None:
     _check(lib().zb_backward_unsplit(stage, mb, _ptr(dy), _ptr(dx)))
+
+
+def zb_stage_set_taps(stage: int, y_tap: Optional[Sequence], dx_tap: Optional[Sequence]) -> None:
+    """Device buffers ([T, h] per microbatch) that receive the stage output after
+    each F and the stage input gradient after each B; None removes a tap."""
+    def arr(xs):
+        return None if xs is None else (C.c_void_p * len(xs))(*[_ptr(x) for x in xs])
+    _check(lib().zb_stage_set_taps(stage, arr(y_tap), arr(dx_tap)))
+
+
+def zb_set_debug_sync(on: bool) -> None:
+    lib().zb_set_debug_sync(1 if on else 0)
+
+
+def zb_get_debug_sync() -> bool:
+    return bool(lib().zb_get_debug_sync())
 
 
 def zb_grad_flush(stage: int, check_finite: bool = False) -> Optional[int]:

@@ -190,6 +190,8 @@ int grid_for(int64_t n) {
 
 }  // namespace
 
+int grad_sumsq_blocks(int64_t n) { return grid_for(n); }
+
 zb_status launch_grad_sumsq(const float* g, int64_t n, double* part, int* blocks_out, hipStream_t s) {
   const int grid = grid_for(n);
   ProfScope ps("grad_sumsq", 0.0, 4.0 * (double)n, s);

@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <map>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -783,61 +784,109 @@ extern "C" zb_status zb_schedule_peak_memory(const zb_op* ops, int n_ops, int st
   return ZB_OK;
 }
 
+namespace {
+// One boundary of an event's interval for the per-stage sweep.
+struct SweepPoint {
+  double t;
+  int is_start;  // ends sort before starts at one instant: touching intervals do not overlap
+  int idx;
+};
+}  // namespace
+
 extern "C" zb_status zb_events_inspect(const zb_event* ev, int n, int stage_count, zb_event_report* rep,
                                        int* bad_index) {
   clear_error();
   if (bad_index) *bad_index = -1;
-  if (n < 1 || !ev || !rep) return set_error(ZB_E_ARG, "need at least one event");
-  if (stage_count < 2) return set_error(ZB_E_ARG, "invalid_stage_count");
-  std::unordered_map<int32_t, int> by_id;
-  for (int i = 0; i < n; ++i) by_id[ev[i].id] = i;
-  if ((int)by_id.size() != n) {
-    std::unordered_map<int32_t, int> seen;
-    for (int i = 0; i < n; ++i)
-      if (!seen.emplace(ev[i].id, i).second) {
-        if (bad_index) *bad_index = i;
-        break;
-      }
-    return set_error(ZB_E_DUPLICATE, "duplicate_task");
-  }
+  if (n < 1 || !ev || !rep) return set_error(ZB_E_ARG, "need at least one event and a report");
+  if (stage_count < 1) return set_error(ZB_E_ARG, "invalid_stage_count %d", stage_count);
+  auto fail = [&](zb_status st, int i, const char* why) {
+    if (bad_index) *bad_index = i;
+    return set_error(st, "event %d (id %d): %s", i, ev[i].id, why);
+  };
+  // Ids -> positions; the second use of an id is the duplicate.
+  std::unordered_map<int32_t, int> pos;
+  pos.reserve((size_t)n * 2);
+  for (int i = 0; i < n; ++i)
+    if (!pos.emplace(ev[i].id, i).second) return fail(ZB_E_DUPLICATE, i, "duplicate_task");
+  for (int i = 0; i < n; ++i)
+    if (ev[i].stage < 0 || ev[i].stage >= stage_count) return fail(ZB_E_INVALID_STAGE, i, "invalid_stage");
+  for (int i = 0; i < n; ++i)
+    if (!(ev[i].start >= 0.0 && ev[i].end > ev[i].start)) return fail(ZB_E_INTERVAL, i, "invalid_interval");
+  // Resolve the dependency edges once; a name with no event is a missing producer.
+  std::vector<int> prod_first(n + 1, 0), prod;
   for (int i = 0; i < n; ++i) {
-    const zb_event& e = ev[i];
-    auto fail = [&](zb_status st, const char* why) {
-      if (bad_index) *bad_index = i;
-      return set_error(st, "event %d (id %d): %s", i, e.id, why);
-    };
-    if (e.stage < 0 || e.stage >= stage_count) return fail(ZB_E_INVALID_STAGE, "invalid_stage");
-    if (!(e.start >= 0 && e.end > e.start)) return fail(ZB_E_INTERVAL, "invalid_interval");
-    for (int d = 0; d < e.n_deps; ++d) {
-      auto it = by_id.find(e.deps[d]);
-      if (it == by_id.end()) return fail(ZB_E_MISSING, "missing_dependency");
-      if (ev[it->second].end > e.start) return fail(ZB_E_DEPENDENCY, "dependency_violation");
+    if (ev[i].n_deps > 0 && !ev[i].deps) return fail(ZB_E_ARG, i, "null dependency array");
+    for (int d = 0; d < ev[i].n_deps; ++d) {
+      auto it = pos.find(ev[i].deps[d]);
+      if (it == pos.end()) return fail(ZB_E_MISSING, i, "missing_dependency");
+      prod.push_back(it->second);
     }
+    prod_first[i + 1] = (int)prod.size();
   }
-  for (int s = 0; s < stage_count; ++s) {
-    std::vector<int> idx;
-    for (int i = 0; i < n; ++i)
-      if (ev[i].stage == s) idx.push_back(i);
-    std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return ev[a].start < ev[b].start; });
-    for (size_t q = 1; q < idx.size(); ++q)
-      if (ev[idx[q - 1]].end > ev[idx[q]].start) {
-        if (bad_index) *bad_index = idx[q];
-        return set_error(ZB_E_OVERLAP, "stage_overlap on stage %d", s);
-      }
+  // A consumer that begins before a producer ends: report the earliest such start.
+  int early = -1;
+  for (int i = 0; i < n; ++i) {
+    double ready = 0.0;
+    for (int q = prod_first[i]; q < prod_first[i + 1]; ++q) ready = std::max(ready, ev[prod[q]].end);
+    if (ready > ev[i].start && (early < 0 || ev[i].start < ev[early].start)) early = i;
   }
-  double span = ev[0].end, busy = 0;
-  std::unordered_map<int32_t, int64_t> live;
+  if (early >= 0) return fail(ZB_E_DEPENDENCY, early, "dependency_violation");
+  // Exclusive work per stage: sweep every interval boundary in time order and
+  // count what is running on each stage; a start on a busy stage overlaps.
+  std::vector<SweepPoint> pts;
+  pts.reserve(2 * (size_t)n);
+  for (int i = 0; i < n; ++i) {
+    pts.push_back({ev[i].start, 1, i});
+    pts.push_back({ev[i].end, 0, i});
+  }
+  std::sort(pts.begin(), pts.end(), [](const SweepPoint& a, const SweepPoint& b) {
+    if (a.t != b.t) return a.t < b.t;
+    if (a.is_start != b.is_start) return a.is_start < b.is_start;
+    return a.idx < b.idx;
+  });
+  std::vector<int> running(stage_count, 0);
+  for (const SweepPoint& p : pts) {
+    int& r = running[ev[p.idx].stage];
+    if (!p.is_start) {
+      --r;
+      continue;
+    }
+    if (r > 0) return fail(ZB_E_OVERLAP, p.idx, "stage_overlap");
+    ++r;
+  }
+  // Totals and the activation ledger: an activation of (stage, micro) is held
+  // from its F until the W (or unsplit U) that frees the stash its B left.
+  double span = 0.0, busy = 0.0;
   for (int i = 0; i < n; ++i) {
     span = std::max(span, ev[i].end);
     busy += ev[i].end - ev[i].start;
-    if (ev[i].kind == 'F') live[ev[i].micro] += 1;
-    else if (ev[i].kind == 'B') live[ev[i].micro] = std::max<int64_t>(0, live[ev[i].micro] - 1);
+  }
+  std::vector<int> by_start(n);
+  for (int i = 0; i < n; ++i) by_start[i] = i;
+  std::stable_sort(by_start.begin(), by_start.end(), [&](int a, int b) { return ev[a].start < ev[b].start; });
+  std::map<std::pair<int32_t, int32_t>, int64_t> held;
+  std::vector<int64_t> held_by_stage(stage_count, 0);
+  int64_t peak = 0;
+  for (int i : by_start) {
+    const std::pair<int32_t, int32_t> key(ev[i].stage, ev[i].micro);
+    if (ev[i].kind == 'F') {
+      held[key] += 1;
+      held_by_stage[ev[i].stage] += 1;
+    } else if (ev[i].kind == 'W' || ev[i].kind == 'U') {
+      auto it = held.find(key);
+      if (it != held.end() && it->second > 0) {
+        it->second -= 1;
+        held_by_stage[ev[i].stage] -= 1;
+      }
+    }
+    peak = std::max(peak, held_by_stage[ev[i].stage]);
   }
   int64_t unfinished = 0;
-  for (auto& kv : live) unfinished += kv.second;
+  for (const auto& kv : held) unfinished += kv.second;
   rep->span = span;
   rep->busy = busy;
   rep->bubble_ratio = 1.0 - busy / (stage_count * span);
   rep->unfinished_activations = unfinished;
+  rep->peak_live_activations = peak;
   return ZB_OK;
 }

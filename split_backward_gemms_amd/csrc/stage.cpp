@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -88,6 +89,31 @@ ProfScope::~ProfScope() {
 using namespace zb;
 
 extern "C" const char* zb_last_error(void) { return g_err.c_str(); }
+
+// ============================================================ debug sync
+namespace zb {
+namespace {
+bool env_debug_sync() {
+  const char* v = getenv("ZB_DEBUG_SYNC");
+  return v && *v && strcmp(v, "0") != 0;
+}
+bool g_debug_sync = env_debug_sync();
+
+// In debug mode: wait for the stream and report any device error, naming the pass.
+zb_status debug_check(hipStream_t s, const char* what, int stage, int mb) {
+  if (!g_debug_sync) return ZB_OK;
+  const hipError_t e1 = hipStreamSynchronize(s);
+  const hipError_t e2 = hipGetLastError();
+  const hipError_t e = e1 != hipSuccess ? e1 : e2;
+  if (e != hipSuccess)
+    return set_error(ZB_E_HIP, "debug sync after %s of stage %d mb %d: %s", what, stage, mb, hipGetErrorString(e));
+  return ZB_OK;
+}
+}  // namespace
+}  // namespace zb
+
+extern "C" void zb_set_debug_sync(int on) { zb::g_debug_sync = on != 0; }
+extern "C" int zb_get_debug_sync(void) { return zb::g_debug_sync ? 1 : 0; }
 
 extern "C" const char* zb_version(void) { return "zb-stage gfx950 0.1"; }
 
@@ -238,6 +264,8 @@ struct zb_stage {
   bool opt_bound = false;
   zb_adamw opt{};
   std::vector<float*> opt_p, opt_m, opt_v;
+  // stage-boundary taps (zb_stage_set_taps): per microbatch, or empty
+  std::vector<void*> tap_y, tap_dx;
   // multi-stream schedules: stages on different streams
   bool multi = false;
   std::vector<hipEvent_t> f_done, b_done;  // per microbatch, created on first use
@@ -422,8 +450,27 @@ GemmDesc w_desc(const zb_stage* S, const void* X, int64_t ldx, const void* dY, i
   return g;
 }
 
+// The W pass's kernel for a list of weight gradients: bf16 goes through the
+// grouped W launch, all of them at once or (per_linear) one launch each.
+zb_status issue_w(zb_stage* S, const std::vector<GemmDesc>& gs, bool per_linear) {
+  if (S->d.dtype != ZB_DTYPE_BF16) {
+    for (const GemmDesc& g : gs) {
+      zb_status st = launch_gemm(g, S->stream);
+      if (st != ZB_OK) return st;
+    }
+    return ZB_OK;
+  }
+  if (!per_linear) return launch_gemm_w_group(gs.data(), (int)gs.size(), S->stream);
+  for (const GemmDesc& g : gs) {
+    zb_status st = launch_gemm_w_group(&g, 1, S->stream);
+    if (st != ZB_OK) return st;
+  }
+  return ZB_OK;
+}
+
+// One linear's weight gradient inside the unsplit backward: the W pass's kernel.
 zb_status gemm_w(zb_stage* S, const void* X, int64_t ldx, const void* dY, int64_t lddy, int lin, int beta) {
-  return launch_gemm(w_desc(S, X, ldx, dY, lddy, lin, beta), S->stream);
+  return issue_w(S, {w_desc(S, X, ldx, dY, lddy, lin, beta)}, true);
 }
 
 #define ZB_TRY(expr)                   \
@@ -600,9 +647,7 @@ zb_status run_weight(zb_stage* S, int mb, int beta) {
         break;
     }
   }
-  if (S->d.dtype == ZB_DTYPE_BF16) return launch_gemm_w_group(gs.data(), (int)gs.size(), S->stream);
-  for (const GemmDesc& g : gs) ZB_TRY(launch_gemm(g, S->stream));
-  return ZB_OK;
+  return issue_w(S, gs, S->d.w_per_linear != 0);
 }
 
 zb_status copy_in(zb_stage* S, void* dst, const void* src) {
@@ -610,6 +655,12 @@ zb_status copy_in(zb_stage* S, void* dst, const void* src) {
   const size_t bytes = (size_t)S->T * S->h * S->es;
   ZB_HIP_CHECK(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, S->stream));
   return ZB_OK;
+}
+
+// Stage-boundary tap: a copy of a [T, h] boundary tensor of mb, if tapped.
+zb_status tap(zb_stage* S, const std::vector<void*>& taps, int mb, const void* src) {
+  if (taps.empty() || !taps[mb]) return ZB_OK;
+  return copy_in(S, taps[mb], src);
 }
 
 zb_status check_mb(const zb_stage* S, int mb) {
@@ -660,8 +711,9 @@ zb_status do_forward(zb_stage* S, int mb, const void* x, void* y) {
   ZB_TRY(S->fb.order_after_release(sfb, S->stream));
   ZB_TRY(copy_in(S, S->fw.at(S->s_fw[mb]) + S->off[0].x, x));
   ZB_TRY(run_forward(S, mb, y));
+  ZB_TRY(tap(S, S->tap_y, mb, y));
   S->st[mb] = MB_F;
-  return ZB_OK;
+  return debug_check(S->stream, "F", S->index, mb);
 }
 
 zb_status do_backward(zb_stage* S, int mb, const void* dy, void* dx, bool unsplit) {
@@ -674,6 +726,7 @@ zb_status do_backward(zb_stage* S, int mb, const void* dy, void* dx, bool unspli
   const int beta = S->w_count > 0 ? 1 : 0;
   ZB_TRY(copy_in(S, S->bw.at(S->s_bw[mb]) + S->off[S->L - 1].dy, dy));
   ZB_TRY(run_backward(S, mb, dx, unsplit, beta));
+  ZB_TRY(tap(S, S->tap_dx, mb, dx));
   ZB_TRY(S->fb.release(S->s_fb[mb], S->stream, S->multi));
   S->s_fb[mb] = -1;
   if (unsplit) {
@@ -684,7 +737,7 @@ zb_status do_backward(zb_stage* S, int mb, const void* dy, void* dx, bool unspli
   } else {
     S->st[mb] = MB_B;
   }
-  return ZB_OK;
+  return debug_check(S->stream, unsplit ? "U" : "B", S->index, mb);
 }
 
 zb_status do_weight(zb_stage* S, int mb) {
@@ -696,7 +749,7 @@ zb_status do_weight(zb_stage* S, int mb) {
   S->st[mb] = MB_DONE;
   S->w_count += 1;
   S->grads_ready = false;
-  return ZB_OK;
+  return debug_check(S->stream, "W", S->index, mb);
 }
 
 }  // namespace
@@ -712,6 +765,7 @@ extern "C" zb_status zb_stage_create(const zb_stage_desc* d, int stage_index, co
   if (d->dtype != ZB_DTYPE_BF16 && d->dtype != ZB_DTYPE_FP32) return set_error(ZB_E_ARG, "dtype");
   if (d->gelu != ZB_GELU_ERF && d->gelu != ZB_GELU_TANH) return set_error(ZB_E_ARG, "gelu");
   if (d->recompute_act != 0 && d->recompute_act != 1) return set_error(ZB_E_ARG, "recompute_act must be 0 or 1");
+  if (d->w_per_linear != 0 && d->w_per_linear != 1) return set_error(ZB_E_ARG, "w_per_linear must be 0 or 1");
   if (d->n_layers < 1 || d->hidden < 1 || d->ffn < 1 || d->seq < 1 || d->micro_batch < 1 || d->n_micro < 1)
     return set_error(ZB_E_ARG, "sizes must be >= 1");
   if (stage_index < 0) return set_error(ZB_E_ARG, "stage_index must be >= 0");
@@ -846,6 +900,19 @@ extern "C" zb_status zb_stage_grad_slot(zb_stage* S, int mb, void** p) {
     return set_error(ZB_E_STATE, "stage %d mb %d already past its B", S->index, mb);
   ZB_TRY(claim_bw(S, mb, S->stream));
   *p = S->bw.at(S->s_bw[mb]) + S->off[S->L - 1].dy;
+  return ZB_OK;
+}
+
+extern "C" zb_status zb_stage_set_taps(zb_stage* S, void* const* y_tap, void* const* dx_tap) {
+  clear_error();
+  if (!S) return set_error(ZB_E_ARG, "null stage");
+  const int m = S->d.n_micro;
+  for (int j = 0; j < m; ++j)
+    if ((y_tap && !y_tap[j]) || (dx_tap && !dx_tap[j])) return set_error(ZB_E_ARG, "null tap for mb %d", j);
+  S->tap_y.clear();
+  S->tap_dx.clear();
+  if (y_tap) S->tap_y.assign(y_tap, y_tap + m);
+  if (dx_tap) S->tap_dx.assign(dx_tap, dx_tap + m);
   return ZB_OK;
 }
 
@@ -1053,13 +1120,20 @@ extern "C" zb_status zb_run_schedule(zb_stage* const* stages, int P, const zb_op
     zb_stage* S = stages[o.stage];
     hipStream_t st = S->stream;
     const int j = o.mb;
+    // The cross-stage hand-off first, so a traced pass's start is when its
+    // stream could begin it (its time then excludes the wait for a producer).
+    if (multi) {
+      hipEvent_t dep = nullptr;
+      if (o.kind == 'F' && o.stage > 0) dep = stages[o.stage - 1]->f_done[j];
+      if ((o.kind == 'B' || o.kind == 'U') && o.stage + 1 < P) dep = stages[o.stage + 1]->b_done[j];
+      if (dep && hipStreamWaitEvent(st, dep, 0) != hipSuccess) {
+        rc = set_error(ZB_E_HIP, "hipStreamWaitEvent failed");
+        break;
+      }
+    }
     if (trace) (void)hipEventRecord(ev[2 * i], st);
     switch (o.kind) {
       case 'F': {
-        if (multi && o.stage > 0 && hipStreamWaitEvent(st, stages[o.stage - 1]->f_done[j], 0) != hipSuccess) {
-          rc = set_error(ZB_E_HIP, "hipStreamWaitEvent failed");
-          break;
-        }
         void* y = y_last[j];
         if (o.stage + 1 < P) {
           zb_stage* N = stages[o.stage + 1];
@@ -1080,10 +1154,6 @@ extern "C" zb_status zb_run_schedule(zb_stage* const* stages, int P, const zb_op
       }
       case 'B':
       case 'U': {
-        if (multi && o.stage + 1 < P && hipStreamWaitEvent(st, stages[o.stage + 1]->b_done[j], 0) != hipSuccess) {
-          rc = set_error(ZB_E_HIP, "hipStreamWaitEvent failed");
-          break;
-        }
         void* dx = dx0[j];
         if (o.stage > 0) {
           zb_stage* U = stages[o.stage - 1];

@@ -108,6 +108,8 @@ constexpr int kSumsqBlocks = 1024;
 // part[2i], part[2i+1] = sum of squares, count of NaN/Inf over workgroup i's
 // share of g[0..n); *blocks_out = the number of pairs written.
 zb_status launch_grad_sumsq(const float* g, int64_t n, double* part, int* blocks_out, hipStream_t s);
+// Pairs launch_grad_sumsq writes for n values (its grid).
+int grad_sumsq_blocks(int64_t n);
 // out[0..1] = up[0..1] (may be null) + the sum of `count` pairs (flag as 0/1).
 zb_status launch_state_combine(const double* part, int count, const double* up, double* out, hipStream_t s);
 struct AdamwLaunch {

@@ -20,11 +20,11 @@ def torch_dtype(dtype: str):
     return torch.bfloat16 if dtype == "bf16" else torch.float32
 
 
-def desc_of(w, recompute_act: int = 0) -> "zb.zb_stage_desc":
+def desc_of(w, recompute_act: int = 0, w_per_linear: int = 0) -> "zb.zb_stage_desc":
     """Stage descriptor of a synthetic_inputs.Workload."""
     return zb.make_desc(KIND_OF[w.kind], zb.ZB_DTYPE_BF16 if w.dtype == "bf16" else zb.ZB_DTYPE_FP32,
                         w.n_layers, w.hidden, w.ffn, max(w.n_heads, 0), w.seq, w.micro_batch, w.n_micro,
-                        zb.ZB_GELU_TANH if w.gelu == "tanh" else zb.ZB_GELU_ERF, recompute_act)
+                        zb.ZB_GELU_TANH if w.gelu == "tanh" else zb.ZB_GELU_ERF, recompute_act, w_per_linear)
 
 
 def upload(a: np.ndarray, dtype: str, device) -> torch.Tensor:
@@ -89,7 +89,7 @@ class EmulatedPipeline:
     def __init__(self, w, weights: Sequence[Sequence[Dict[str, np.ndarray]]], ops: Optional[Sequence] = None,
                  device: str = "cuda", stream: Optional[torch.cuda.Stream] = None,
                  stage_streams: bool = False, recompute_act: Optional[int] = None,
-                 n_streams: Optional[int] = None):
+                 n_streams: Optional[int] = None, w_per_linear: int = 0):
         """stage_streams=True gives every emulated stage its own HIP stream (default
         priority), so independent stages' passes run concurrently; n_streams below P
         caps the number of streams, with neighbouring stages in pairs sharing one
@@ -97,20 +97,14 @@ class EmulatedPipeline:
         linearized order stay valid on a shared stream).  recompute_act
         0 / 1 fixes the stash layout (see zb_stage_desc); None stashes the MLP
         activation when that plan fits in free device memory and rebuilds it for W
-        otherwise."""
+        otherwise.  w_per_linear=1 makes every W pass issue one launch per
+        linear instead of one grouped launch (same kernel, same bits)."""
         self.w = w
+        self.w_per_linear = int(w_per_linear)
         self.device = torch.device(device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         self.P = w.n_stages
-        if stage_streams:
-            n = self.P if n_streams is None else max(1, min(self.P, n_streams))
-            pool = [torch.cuda.Stream(self.device) for _ in range(n)]
-            # Pairs keep the hand-off between stages 2k and 2k+1 on one stream:
-            # measured 0.7-0.9% faster than alternating stages at P = 4 (two
-            # streams) and no different at P = 8.
-            self.streams = pool if n == self.P else [pool[(s // 2) % n] for s in range(self.P)]
-        else:
-            self.streams = [self.stream] * self.P
+        self.streams = self._make_streams(stage_streams, n_streams)
         self.handles: List[int] = []
         self.weights: List[List[torch.Tensor]] = []
         self.grads: List[List[torch.Tensor]] = []
@@ -133,21 +127,76 @@ class EmulatedPipeline:
             self._create(int(recompute_act))
         self.plan(ops)
 
+    def rebuild(self, ops: Optional[Sequence], stage_streams: bool = False, n_streams: Optional[int] = None,
+                w_per_linear: Optional[int] = None) -> None:
+        """New stage objects over the same weights and gradient buffers: other
+        streams (one shared stream when stage_streams is False) or another W
+        launch mode, and workspaces planned for `ops`.  The stash layout stays."""
+        for st in self._distinct_streams():
+            st.synchronize()
+        self.close()
+        if w_per_linear is not None:
+            self.w_per_linear = int(w_per_linear)
+        self.streams = self._make_streams(stage_streams, n_streams)
+        self._create(self.recompute_act)
+        self.workspaces = []
+        self.plan(ops)
+
+    def _make_streams(self, stage_streams: bool, n_streams: Optional[int]):
+        if not stage_streams:
+            return [self.stream] * self.P
+        n = self.P if n_streams is None else max(1, min(self.P, n_streams))
+        pool = [torch.cuda.Stream(self.device) for _ in range(n)]
+        # Pairs keep the hand-off between stages 2k and 2k+1 on one stream:
+        # measured 0.7-0.9% faster than alternating stages at P = 4 (two
+        # streams) and no different at P = 8.
+        return pool if n == self.P else [pool[(s // 2) % n] for s in range(self.P)]
+
+    def stream_index_of_stage(self) -> List[int]:
+        """Index of the distinct stream each stage runs on."""
+        ids: Dict[int, int] = {}
+        return [ids.setdefault(id(st), len(ids)) for st in self.streams]
+
     def _create(self, recompute_act: int) -> None:
         self.recompute_act = recompute_act
-        desc = desc_of(self.w, recompute_act)
+        desc = desc_of(self.w, recompute_act, self.w_per_linear)
         self.handles = [zb.zb_stage_create(desc, s, self.weights[s], self.grads[s], self.streams[s].cuda_stream)
                         for s in range(self.P)]
 
+    def _distinct_streams(self):
+        return list({id(s): s for s in self.streams}.values())
+
     def plan(self, ops: Optional[Sequence]) -> None:
-        """(Re)size and bind every stage's workspace for the given order (None = all m live)."""
+        """(Re)size and bind every stage's workspace for the given order (None = all m live).
+
+        The old workspaces may still be read by work queued on the stage streams,
+        so those streams are drained before the old buffers go back to torch's
+        allocator; a new buffer comes from the caller's stream, and each stage
+        stream waits for that stream before the bind enqueues anything on it."""
+        cur = torch.cuda.current_stream(self.device)
+        if self.workspaces:
+            for st in self._distinct_streams():
+                st.synchronize()
         self.workspaces = []
-        for h in self.handles:
+        for s, h in enumerate(self.handles):
             nbytes = zb.zb_stage_workspace_bytes(h, ops)
             buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
             off = (-buf.data_ptr()) % 256
+            if self.streams[s] != cur:
+                self.streams[s].wait_stream(cur)
             zb.zb_stage_bind_workspace(h, buf.data_ptr() + off, nbytes)
             self.workspaces.append(buf)
+        for st in self._distinct_streams():
+            if st != cur:
+                cur.wait_stream(st)  # the binds' clearing work before anything the caller queues
+
+    def set_taps(self, y_taps: Optional[Sequence[Sequence[torch.Tensor]]],
+                 dx_taps: Optional[Sequence[Sequence[torch.Tensor]]]) -> None:
+        """Per-stage boundary taps: y_taps[s][j] receives stage s's output of
+        microbatch j after its F, dx_taps[s][j] its input gradient after its B."""
+        for s, h in enumerate(self.handles):
+            zb.zb_stage_set_taps(h, None if y_taps is None else y_taps[s],
+                                 None if dx_taps is None else dx_taps[s])
 
     def workspace_bytes(self) -> int:
         return sum(int(b.numel()) for b in self.workspaces)

@@ -156,7 +156,9 @@ def test_events_inspect_audit_golden():
     for case in g["rejections"]:
         st, _, _ = zb.zb_events_inspect(g["tasks"] + [case["extra"]], 2)
         assert st == want[case["error"]]
-    assert zb.zb_events_inspect(g["tasks"], 1)[0] == zb.ZB_E_ARG
+    assert zb.zb_events_inspect(g["tasks"], 0)[0] == zb.ZB_E_ARG
+    assert zb.zb_events_inspect(g["tasks"], 1)[0] == zb.ZB_E_INVALID_STAGE
+    assert rep["peak_live_activations"] == 2
     bad_dep = [dict(t) for t in g["tasks"]]
     bad_dep[3]["depends_on"] = ["nope"]
     assert zb.zb_events_inspect(bad_dep, 2)[0] == zb.ZB_E_MISSING
@@ -189,6 +191,88 @@ def test_events_inspect_matches_oracle_on_simulated_schedules():
         assert st == zb.ZB_OK
         assert got["span"] == want["span"] and got["busy"] == want["busy"]
         assert abs(got["bubble_ratio"] - float(want["bubble_ratio"])) < 1e-12
+        assert got["unfinished_activations"] == want["unfinished_activations"] == 0
+        assert got["peak_live_activations"] == want["peak_live_activations"]
+
+
+_INSPECT_STATUS = {"invalid_stage_count": zb.ZB_E_ARG, "duplicate_task": zb.ZB_E_DUPLICATE,
+                   "invalid_stage": zb.ZB_E_INVALID_STAGE, "invalid_interval": zb.ZB_E_INTERVAL,
+                   "missing_dependency": zb.ZB_E_MISSING, "dependency_violation": zb.ZB_E_DEPENDENCY,
+                   "stage_overlap": zb.ZB_E_OVERLAP}
+
+
+def _timed_tasks(name, P, m, t):
+    orders = sch.stage_orders(name, P, m)
+    r = sch.simulate(orders, t)
+    tasks = []
+    for s, o in enumerate(orders):
+        for k, j in o:
+            deps = []
+            if k == "F" and s > 0:
+                deps.append(f"{s-1}F{j}")
+            if k in "BU":
+                deps.append(f"{s}F{j}")
+                if s < P - 1:
+                    deps.append(f"{s+1}{'U' if k == 'U' else 'B'}{j}")
+            if k == "W":
+                deps.append(f"{s}B{j}")
+            tasks.append({"id": f"{s}{k}{j}", "stage": s, "micro": j, "kind": k,
+                          "start": r.start[(s, k, j)], "end": r.end[(s, k, j)], "depends_on": deps})
+    return tasks
+
+
+def test_events_inspect_matches_oracle_on_perturbed_schedules():
+    """Both inspectors give the same verdict, offending event and report on
+    simulated schedules with random faults planted: moved or shortened events,
+    repeated ids, wrong stages, dropped or renamed dependencies, removed W's."""
+    rng = random.Random(2027)
+    seen = set()
+    for trial in range(1500):
+        name = rng.choice(["1f1b", "zbh1", "zbh2", "gpipe"])
+        P = rng.randint(2, 4)
+        m = rng.randint(2 * P - 1, 2 * P + 2) if name == "zbh2" else rng.randint(1, 6)
+        t = dict(F=rng.randint(1, 3), B=rng.randint(1, 3), W=rng.randint(1, 2))
+        tasks = _timed_tasks(name, P, m, t)
+        for _ in range(rng.randint(0, 3)):
+            i = rng.randrange(len(tasks))
+            x = dict(tasks[i])
+            fault = rng.randrange(8)
+            if fault == 0:
+                x["start"] = max(0, x["start"] - rng.randint(1, 3))
+            elif fault == 1:
+                x["end"] = x["start"] - rng.choice([0, 1])
+            elif fault == 2:
+                x["id"] = tasks[rng.randrange(len(tasks))]["id"]
+            elif fault == 3:
+                x["stage"] = rng.choice([-1, P, P + 1])
+            elif fault == 4:
+                x["depends_on"] = list(x["depends_on"]) + ["nobody"]
+            elif fault == 5:
+                x["start"] += rng.randint(1, 4)
+                x["end"] += rng.randint(1, 4)
+            elif fault == 6 and x["kind"] == "W":
+                tasks.pop(i)
+                continue
+            else:
+                x["stage"] = rng.randrange(P)
+            tasks[i] = x
+        count = rng.choice([P, P, P, 0])
+        try:
+            want = sch.inspect_events(tasks, count)
+            w_st, w_bad = zb.ZB_OK, -1
+        except sch.ScheduleError as e:
+            want = None
+            w_st = _INSPECT_STATUS[e.args[0]]
+            w_bad = e.args[1] if len(e.args) > 1 else -1
+        st, got, bad = zb.zb_events_inspect(tasks, count)
+        assert (st, bad) == (w_st, w_bad), (trial, st, bad, w_st, w_bad)
+        seen.add(st)
+        if want is not None:
+            assert got["span"] == want["span"] and got["busy"] == want["busy"]
+            assert abs(got["bubble_ratio"] - float(want["bubble_ratio"])) < 1e-12
+            assert got["unfinished_activations"] == want["unfinished_activations"]
+            assert got["peak_live_activations"] == want["peak_live_activations"]
+    assert seen >= set(_INSPECT_STATUS.values()) | {zb.ZB_OK}
 
 
 # ------------------------------------------------ automatic (heuristic) scheduler

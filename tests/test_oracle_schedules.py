@@ -129,7 +129,11 @@ def test_audit_worked_schedule_golden():
             sch.inspect_events(g["tasks"] + [case["extra"]], g["stage_count"])
     assert sch.inspect_events(list(g["tasks"]), 2) == r
     with pytest.raises(sch.ScheduleError, match="invalid_stage_count"):
-        sch.inspect_events(g["tasks"], 1)
+        sch.inspect_events(g["tasks"], 0)
+    with pytest.raises(sch.ScheduleError, match="invalid_stage"):
+        sch.inspect_events(g["tasks"], 1)  # the tasks of stage 1 name an unknown stage
+    # every F is released by its W: stage 0 holds two activations at once (F0, F1 before W0)
+    assert r["peak_live_activations"] == 2
     bad = [dict(t) for t in g["tasks"]]
     bad[3]["depends_on"] = ["nope"]
     with pytest.raises(sch.ScheduleError, match="missing_dependency"):
@@ -162,3 +166,29 @@ def test_validator_cases():
     # unsplit plus split of one pass is a duplicate
     u = [(0, "F", 0), (1, "F", 0), (1, "U", 0), (1, "W", 0)]
     assert sch.validate_linear(P, m, u) == (sch.E_DUPLICATE, 3)
+
+
+def test_inspector_ledger_counts_w_stash():
+    """An activation stays held from F through B until its W: dropping the W of
+    one microbatch leaves one unfinished activation; a B alone releases nothing."""
+    g = json.load(open(os.path.join(GOLDEN, "aud_worked_schedule.json")))
+    no_w = [t for t in g["tasks"] if t["id"] != "s1w1"]
+    assert sch.inspect_events(no_w, 2)["unfinished_activations"] == 1
+    only_f = [t for t in g["tasks"] if t["kind"] == "F"]
+    assert sch.inspect_events(only_f, 2)["unfinished_activations"] == 4
+
+
+def test_inspector_reports_earliest_violation():
+    """Two consumers start too early; the one with the earlier start is named.
+    Two overlaps on one stage; the later-starting member of the earliest pair."""
+    base = [{"id": "p", "stage": 0, "micro": 0, "kind": "F", "start": 0, "end": 4}]
+    late = {"id": "c1", "stage": 1, "micro": 0, "kind": "F", "start": 3, "end": 5, "depends_on": ["p"]}
+    early = {"id": "c2", "stage": 2, "micro": 0, "kind": "F", "start": 1, "end": 2, "depends_on": ["p"]}
+    with pytest.raises(sch.ScheduleError) as e:
+        sch.inspect_events(base + [late, early], 3)
+    assert e.value.args == ("dependency_violation", 2)
+    ov = [{"id": i, "stage": 0, "micro": 0, "kind": "W", "start": s, "end": s + 2} for i, s in
+          (("a", 5), ("b", 0), ("c", 6), ("d", 1))]
+    with pytest.raises(sch.ScheduleError) as e:
+        sch.inspect_events(ov, 1)
+    assert e.value.args == ("stage_overlap", 3)  # d (start 1) overlaps b (start 0)
