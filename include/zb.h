@@ -364,6 +364,21 @@ zb_status zb_stage_optim_bind(zb_stage* st, const zb_adamw* hp, float* const* ma
  * fixed reduction order. */
 zb_status zb_stage_grad_state(zb_stage* st, const double* upstream, double* partial_out);
 
+/* zb_stage_grad_state for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid it):
+ * same result bits, but the per-workgroup partial states live in the
+ * library's own device array of 65536 (sum of squares, non-finite count)
+ * pairs (1 MiB, one copy per GPU, held until the process ends) instead of the
+ * stage's workspace, so neither this call nor the stage needs a bound
+ * workspace for it, and nothing is allocated.  Needs the stage's device to be
+ * current.  Every call on one GPU shares that array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be ordered by the caller.
+ * The array needs no clearing: every partial is written before it is read.
+ * Errors: ZB_E_ARG (null), ZB_E_UNSUPPORTED (the stage's gradients need more
+ * than 65536 partial states: about 64 linears of 1 M elements or more),
+ * ZB_E_STATE (no flushed step gradients), ZB_E_HIP. */
+zb_status zb_stage_grad_state_noalloc(zb_stage* st, const double* upstream, double* partial_out);
+
 /* Optimistic step number `step` (>= 1) with the state `used` (device, 2
  * doubles; normally this stage's partial).  Same preconditions. */
 zb_status zb_stage_optim_step(zb_stage* st, int step, const double* used);

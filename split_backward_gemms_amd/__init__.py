@@ -129,6 +129,7 @@ def lib():
             "zb_stage_optim_bind": (I, [P, C.POINTER(zb_adamw), C.POINTER(P), C.POINTER(P), C.POINTER(P),
                                         C.POINTER(P)]),
             "zb_stage_grad_state": (I, [P, P, P]),
+            "zb_stage_grad_state_noalloc": (I, [P, P, P]),
             "zb_stage_optim_step": (I, [P, I, P]),
             "zb_stage_optim_validate": (I, [P, I, P, P, P]),
             "zb_stage_optim_rollback": (I, [P, I, P]),
@@ -160,7 +161,8 @@ def exported_symbols() -> List[str]:
             "zb_stage_bind_workspace", "zb_stage_input_slot", "zb_stage_grad_slot", "zb_forward",
             "zb_backward_input", "zb_backward_weight", "zb_backward_unsplit", "zb_stage_set_taps",
             "zb_set_debug_sync", "zb_get_debug_sync", "zb_grad_flush",
-            "zb_stage_optim_bind", "zb_stage_grad_state", "zb_stage_optim_step", "zb_stage_optim_validate",
+            "zb_stage_optim_bind", "zb_stage_grad_state", "zb_stage_grad_state_noalloc", "zb_stage_optim_step",
+            "zb_stage_optim_validate",
             "zb_stage_optim_rollback",
             "zb_run_schedule", "zb_last_error", "zb_stage_destroy", "zb_prof_enable", "zb_prof_reset",
             "zb_prof_read", "zb_version", "zb_linear_forward", "zb_linear_backward_input",
@@ -411,6 +413,12 @@ def zb_stage_optim_bind(stage: int, hp: "zb_adamw", master: Sequence, exp_avg: S
 
 def zb_stage_grad_state(stage: int, upstream, partial_out) -> None:
     _check(lib().zb_stage_grad_state(stage, _ptr(upstream), _ptr(partial_out)))
+
+
+def zb_stage_grad_state_noalloc(stage: int, upstream, partial_out) -> None:
+    """As zb_stage_grad_state, with the partial states in the library's own
+    device array (allocates nothing; calls on one GPU must not overlap)."""
+    _check(lib().zb_stage_grad_state_noalloc(stage, _ptr(upstream), _ptr(partial_out)))
 
 
 def zb_stage_optim_step(stage: int, step: int, used) -> None:

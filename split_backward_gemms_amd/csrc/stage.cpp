@@ -1040,6 +1040,61 @@ extern "C" zb_status zb_stage_grad_state(zb_stage* S, const double* upstream, do
   return launch_state_combine(part, count, upstream, partial_out, S->stream);
 }
 
+// ------------------------------------ gradient state without allocating
+
+namespace {
+// Per-workgroup partial gradient states of zb_stage_grad_state_noalloc: the
+// library's own device array instead of the stage workspace, so the call
+// allocates nothing.  Every GPU the library runs on holds its own copy, at its
+// own address, until the process ends.  In host code `scratch` only names the
+// symbol: its device address comes from hipGetSymbolAddress, once per device.
+constexpr int kNoAllocPairs = 65536;  // (sum of squares, non-finite count) pairs: 1 MiB
+static __device__ __align__(256) double scratch[2 * kNoAllocPairs];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+double* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's copy of `scratch`, looked up on first use.
+zb_status noalloc_scratch(double** out) {
+  int dev = -1;
+  ZB_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return set_error(ZB_E_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    ZB_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return set_error(ZB_E_HIP, "hipGetSymbolAddress gave a null address");
+    g_scratch_ptr[dev] = static_cast<double*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return ZB_OK;
+}
+}  // namespace
+
+extern "C" zb_status zb_stage_grad_state_noalloc(zb_stage* S, const double* upstream, double* partial_out) {
+  clear_error();
+  if (!S) return set_error(ZB_E_ARG, "null stage");
+  if (!partial_out) return set_error(ZB_E_ARG, "null partial_out");
+  int64_t pairs = 0;
+  for (size_t i = 0; i < S->w.size(); ++i) pairs += grad_sumsq_blocks(S->wK[i] * S->wN[i]);
+  if (pairs > kNoAllocPairs)
+    return set_error(ZB_E_UNSUPPORTED, "stage %d: %lld partial states exceed the %d of the library's scratch",
+                     S->index, (long long)pairs, kNoAllocPairs);
+  if (!S->grads_ready)
+    return set_error(ZB_E_STATE, "stage %d: no flushed step gradients (flush first; a W of the next step "
+                     "overwrites them)", S->index);
+  double* part = nullptr;
+  ZB_TRY(noalloc_scratch(&part));
+  int count = 0;
+  for (size_t i = 0; i < S->w.size(); ++i) {
+    int blocks = 0;
+    ZB_TRY(launch_grad_sumsq(S->dw[i], S->wK[i] * S->wN[i], part + 2 * count, &blocks, S->stream));
+    count += blocks;
+  }
+  return launch_state_combine(part, count, upstream, partial_out, S->stream);
+}
+
 extern "C" zb_status zb_stage_optim_step(zb_stage* S, int step, const double* used) {
   clear_error();
   return optim_launch(S, 0, step, used, nullptr, nullptr);
