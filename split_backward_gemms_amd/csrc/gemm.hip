@@ -9,9 +9,13 @@
 // tutorial "Pipeline Schedules: GPipe, 1F1B and Zero Bubble" writes them in
 // "Zero bubble: split the backward pass".)
 //
-// bf16 path: 256 threads = 4 waves of 64 in a 2x2 grid; each wave owns a
-// (BM/2)x(BN/2) block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, fp32
-// accumulators).  K advances 64 at a time (32 in the grouped W launch) through
+// bf16 path: 8 waves of 64 in a 2x4 grid, two per SIMD, for tiles of at least
+// 128x128 (4 waves in a 2x2 grid for 128x64); each wave owns a (BM/2)x(BN/4)
+// (or (BM/2)x(BN/2)) block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16,
+// fp32 accumulators).  With two waves on a SIMD one wave's LDS reads, waits
+// and barrier overlap the other's MFMAs: measured 5-20% faster than one wave
+// per SIMD on every 256x256 F and B product of the seq-4096 workload and
+// 3-9% on the 256x128 and 128x128 tiles of the seq-1024 one, bit-identical.  K advances 64 at a time (32 in the grouped W launch) through
 // a ring of 2 to 4 LDS stages that global->LDS copies (buffer_load ... lds, 16
 // bytes per lane, hardware range checks in place of bounds branches) keep
 // filled ahead of the MFMAs; every wait for them is an explicit vmcnt wait
@@ -58,7 +62,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BKT = 64;   // K per LDS tile
-constexpr int NT = 256;   // threads per workgroup
+constexpr int kWavesWide = 8;    // waves per workgroup for tiles of at least 128x128
+constexpr int kWavesNarrow = 4;  // for 128x64
 constexpr int XCDS = 8;   // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
 
 struct Params {
@@ -184,11 +189,11 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 //   otherwise: LDS [BK][ROWS] bf16; chunk c (8 m values) of k-row k sits at
 //              position c ^ 4 (k % 4) of its 2 ROWS-byte row (c ^ 4 (k % 2) when
 //              ROWS = 64).
-// The four waves of the workgroup each move a quarter of the tile.
-template <int ROWS, bool KCONTIG, int BK = BKT>
+// The WV waves of the workgroup each move an equal share of the tile.
+template <int ROWS, bool KCONTIG, int BK, int WV>
 struct DmaLoader {
   static_assert(BK == BKT || !KCONTIG, "k-contiguous operands use 64-deep tiles");
-  static constexpr int NI = ROWS * BK / 2048;  // instructions per wave per tile
+  static constexpr int NI = ROWS * BK / (512 * WV);  // instructions per wave per tile
   u32x4 rsrc;
   uint32_t voff[NI];                    // lane's byte offset at k0 = 0 (kOOB outside the matrix)
   int kofs[KCONTIG ? NI : 1];           // KCONTIG: lane's first k within the tile
@@ -263,7 +268,7 @@ struct Ring {
   static constexpr int S3 = NS > 3 ? STAGE : 16;
 };
 
-template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC = 1, int BK = BKT>
+template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC, int BK, int WV>
 __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, char* s0, char* s1, char* s2,
                                           char* s3);
 
@@ -275,8 +280,8 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
   __shared__ __attribute__((aligned(1024))) char s2[Ring<BM, BN, OCC, BK>::S2];     \
   __shared__ __attribute__((aligned(1024))) char s3[Ring<BM, BN, OCC, BK>::S3]
 
-template <int BM, int BN, bool AK, bool BKC, int EPI>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN, bool AK, bool BKC, int EPI, int WV>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64 * WV, 64 * WV), amdgpu_waves_per_eu(WV / 4, WV / 4)))
 gemm_bf16_mfma(Params p) {
   ZB_GEMM_LDS(BM, BN, 1, BKT);
   const int total = p.nbm * p.nbn * p.splits;
@@ -284,12 +289,13 @@ gemm_bf16_mfma(Params p) {
     if (b0 != (int)blockIdx.x) __syncthreads();
     int b = b0;
     if (p.xcd_remap) b = xcd_remap(b, total);  // a tile's splits share an XCD
-    gemm_tile<BM, BN, AK, BKC, EPI>(p, b / p.splits, b % p.splits, s0, s1, s2, s3);
+    gemm_tile<BM, BN, AK, BKC, EPI, 1, BKT, WV>(p, b / p.splits, b % p.splits, s0, s1, s2, s3);
   }
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC, int BK>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(OCC, OCC)))
+template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC, int BK, int WV>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64 * WV, 64 * WV),
+                               amdgpu_waves_per_eu(OCC * WV / 4, OCC * WV / 4)))
 gemm_bf16_mfma_group(GroupParams gp) {
   ZB_GEMM_LDS(BM, BN, OCC, BK);
   const int total = gp.tile_start[gp.n];
@@ -303,7 +309,7 @@ gemm_bf16_mfma_group(GroupParams gp) {
     if (total % XCDS == 0) b = (b % XCDS) * (total / XCDS) + b / XCDS;  // one XCD works a GEMM's neighbours
     int g = 0;
     while (g + 1 < gp.n && b >= gp.tile_start[g + 1]) ++g;
-    gemm_tile<BM, BN, AK, BKC, EPI, OCC, BK>(gp.p[g], b - gp.tile_start[g], 0, s0, s1, s2, s3);
+    gemm_tile<BM, BN, AK, BKC, EPI, OCC, BK, WV>(gp.p[g], b - gp.tile_start[g], 0, s0, s1, s2, s3);
   }
 }
 
@@ -321,10 +327,10 @@ __device__ __forceinline__ bf16x8 frag_t(const char* tile, uint32_t off) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC, int BK>
+template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC, int BK, int WV>
 __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, char* s0, char* s1, char* s2,
                                           char* s3) {
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int WTM = BM / 2, WTN = BN / (WV / 2);  // waves in a 2 x (WV / 2) grid
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int NS = Ring<BM, BN, OCC, BK>::NS;
   constexpr int AT = BM * BK * 2;  // bytes of the A tile in a ring stage (the B tile follows)
@@ -355,9 +361,9 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
   __amdgpu_buffer_rsrc_t crsrc = make_rsrc(p.C, (uint32_t)(((int64_t)(p.M - 1) * p.ldc + p.N) *
                                                            (EPI == EPI_ACC ? 4 : 2)));
 
-  DmaLoader<BM, AK, BK> la(static_cast<const uint16_t*>(p.A), p.lda, m0, p.M, p.K, wave, lane);
-  DmaLoader<BN, BKC, BK> lb(static_cast<const uint16_t*>(p.B), p.ldb, n0, p.N, p.K, wave, lane);
-  constexpr int NI = DmaLoader<BM, AK, BK>::NI + DmaLoader<BN, BKC, BK>::NI;  // copies per wave per tile
+  DmaLoader<BM, AK, BK, WV> la(static_cast<const uint16_t*>(p.A), p.lda, m0, p.M, p.K, wave, lane);
+  DmaLoader<BN, BKC, BK, WV> lb(static_cast<const uint16_t*>(p.B), p.ldb, n0, p.N, p.K, wave, lane);
+  constexpr int NI = DmaLoader<BM, AK, BK, WV>::NI + DmaLoader<BN, BKC, BK, WV>::NI;  // copies per wave per tile
   // This workgroup's k tiles: [kt0, kt0 + nk) of the product's ceil(K / BK).
   const int nk_all = (p.K + BK - 1) / BK;
   const int kt0 = split * p.kts;
@@ -825,7 +831,8 @@ void launch_mfma(Params p, hipStream_t s) {
   // with the stages on separate streams a 2% shorter step (gpt_full_h4096).
   const int total = p.nbm * p.nbn * p.splits;
   const int grid = std::min(total, cu_count() / XCDS * XCDS);
-  hipLaunchKernelGGL((gemm_bf16_mfma<BM, BN, AK, BKC, EPI>), dim3(grid), dim3(NT), 0, s, p);
+  constexpr int WV = (BM >= 128 && BN >= 128) ? kWavesWide : kWavesNarrow;
+  hipLaunchKernelGGL((gemm_bf16_mfma<BM, BN, AK, BKC, EPI, WV>), dim3(grid), dim3(64 * WV), 0, s, p);
 }
 
 template <int BM, int BN, int OCC = 1, int BK = BKT>
@@ -844,7 +851,8 @@ void launch_w_group(GroupParams gp, hipStream_t s) {
   // One workgroup per CU (OCC per CU), each looping over its tiles: measured
   // 3-4% faster than one workgroup per tile for the grouped W launch.
   const int grid = std::min(total, cu_count() / XCDS * XCDS * OCC);
-  hipLaunchKernelGGL((gemm_bf16_mfma_group<BM, BN, false, false, EPI_ACC, OCC, BK>), dim3(grid), dim3(NT), 0, s, gp);
+  hipLaunchKernelGGL((gemm_bf16_mfma_group<BM, BN, false, false, EPI_ACC, OCC, BK, kWavesWide>), dim3(grid),
+                     dim3(64 * kWavesWide), 0, s, gp);
 }
 
 template <bool AK, bool BKC, int EPI>
@@ -911,11 +919,12 @@ zb_status launch_gemm_w_group(const GemmDesc* gs, int n, hipStream_t s) {
       bytes += 2.0 * ((double)g.M * g.K + (double)g.K * g.N) + (g.beta ? 8.0 : 4.0) * g.M * g.N;
     }
     if (gp.n == 0) continue;
-    // 256x256 tiles, one workgroup per CU, 32-deep k tiles in a four-stage
-    // ring (three in flight).  Measured in one process against 64-deep tiles
-    // in a two-stage ring: 3.6% faster at T = 1024 and 2048, 7.8% at 4096;
-    // 128x128 and 256x128 tiles two to a CU, and 128x256 tiles one or two to a
-    // CU, were slower at T >= 2048 and no faster at T = 1024.
+    // 256x256 tiles, one workgroup of eight waves per CU, 32-deep k tiles in
+    // a four-stage ring (three in flight).  Measured in one process against
+    // 64-deep tiles in a two-stage ring: 3.6% faster at T = 1024 and 2048, 7.8%
+    // at 4096; 128x128 and 256x128 tiles two to a CU, and 128x256 tiles one or
+    // two to a CU, were slower at T >= 2048 and no faster at T = 1024.  Eight
+    // waves instead of four: 3.5-5% shorter launches at T = 1024 and 4096.
     ProfScope ps("gemm_w_group_256x256", flops, bytes, s);
     launch_w_group<256, 256, 1, 32>(gp, s);
     ZB_HIP_CHECK(hipGetLastError());
