@@ -143,6 +143,40 @@ def roofline_of(kern, workload: str) -> dict:
     return r
 
 
+def counter_run(w0, a) -> int:
+    """One full-size stage of the workload, two microbatches, two steps, one stream."""
+    import torch
+
+    import split_backward_gemms_amd as zb
+    import synthetic_inputs as si
+    from split_backward_gemms_amd.pipeline import EmulatedPipeline, upload
+
+    w = w0.replace(n_stages=1, n_micro=2)
+    torch.cuda.set_device(0)
+    ws = [si.stage_weights(w, 0)]
+    X = [upload(si.stage_input(w, j), w.dtype, "cuda:0") for j in range(2)]
+    DY = [upload(si.last_stage_grad(w, j), w.dtype, "cuda:0") for j in range(2)]
+    ops = [(0, "F", 0), (0, "F", 1), (0, "B", 0), (0, "B", 1), (0, "W", 0), (0, "W", 1)]
+    pipe = EmulatedPipeline(w, ws, ops=ops, device="cuda:0", recompute_act=a.recompute_act)
+    y, dx = pipe.io_buffers()
+    log(f"counter run {w.name}: one stage, 2 microbatches, recompute_act={pipe.recompute_act}")
+    zb.zb_prof_reset()
+    for step in range(2):
+        zb.zb_prof_enable(step == 1)
+        pipe.run(ops, X, DY, y, dx)
+        torch.cuda.synchronize()
+    zb.zb_prof_enable(False)
+    kern = sorted(zb.zb_prof_read(), key=lambda r: -r["total_ms"])
+    zb.zb_prof_reset()
+    pipe.close()
+    print(json.dumps({"mode": "counters", "workload": w0.name, "recompute_act": pipe.recompute_act,
+                      "kernels": [{"name": r["name"], "launches": r["launches"],
+                                   "avg_us": 1e3 * r["total_ms"] / r["launches"],
+                                   "flops_per_launch": r["flops"] / r["launches"],
+                                   "bytes_per_launch": r["bytes"] / r["launches"]} for r in kern]}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,8 +191,12 @@ def main() -> int:
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-optim", action="store_true",
                     help="skip timing the optimizer step with post-update validation")
-    ap.add_argument("--mode", choices=["full", "kernels"], default="full",
-                    help="kernels: only the one-stream kernel-timing phase (the phase a kernel profile covers)")
+    ap.add_argument("--mode", choices=["full", "kernels", "counters"], default="full",
+                    help="kernels: only the one-stream kernel-timing phase (the phase a kernel profile covers); "
+                         "counters: one full-size stage of the workload with two microbatches (F, F, B, B, W, W), "
+                         "two steps: the same kernels at the same shapes for counter passes, in a few GiB")
+    ap.add_argument("--recompute-act", type=int, choices=[0, 1], default=None,
+                    help="stash layout (zb_stage_desc.recompute_act); default: stash A when it fits")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one plain device-to-device copy kernel of BYTES bytes (counter calibration)")
     a = ap.parse_args()
@@ -187,6 +225,8 @@ def main() -> int:
                                                    stash_per_microbatch, upload, zbv_ops)
 
     w0 = si.WORKLOADS[a.workload]
+    if a.mode == "counters":
+        return counter_run(w0, a)
     order = a.order or w0.order
     # ZB-V runs the same model cut into 2P chunk stages of half the layers.
     w = si.v_chunks(w0) if order == "zbv" else w0
