@@ -59,7 +59,6 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int HD = 128;           // head dim
 constexpr int NT = 256;           // 4 waves
 constexpr int BLK = 64 * 256;     // one 64 x 128 bf16 block in LDS
-constexpr int NI_BLK = 4;         // copies per wave per block (16 KiB / 4 waves / 1 KiB)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnParams {
@@ -109,23 +108,26 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 
 
 // Copies of one block: rows row0 .. row0+63 (those at or past `valid` read as
 // zero), columns col0 .. col0+127 of a row-major bf16 matrix with leading
-// dimension ld.  Wave w issues copies 4w .. 4w+3; copy q covers LDS bytes
-// 1024 q .. +1023, i.e. rows 4q .. 4q+3, with lane l at LDS chunk l of them.
+// dimension ld.  The NW waves of the workgroup each issue 16 / NW copies;
+// copy q of wave w covers LDS bytes 1024 (w 16 / NW + q) .. +1023, i.e. four
+// rows, with lane l at LDS chunk l of them.
+template <int NW>
 struct BlockDma {
+  static constexpr int NI = 16 / NW;  // copies per wave per block (16 KiB / NW waves / 1 KiB)
   dev::u32x4 rsrc;
-  uint32_t boff[NI_BLK];  // lane's byte offset at row0 = 0
-  uint32_t rowstep;       // bytes per row
-  int row0;               // the lane's row within the block for copy 0 (copy q adds 4 q)
-  uint32_t lds0;          // this wave's first KiB within the block
+  uint32_t boff[NI];  // lane's byte offset at row0 = 0
+  uint32_t rowstep;   // bytes per row
+  int row0;           // the lane's row within the block for copy 0 (copy q adds 4 q)
+  uint32_t lds0;      // this wave's first KiB within the block
 
   __device__ __forceinline__ BlockDma(const uint16_t* base, uint32_t extent, int64_t ld, int col0, int wave,
                                       int lane) {
     rsrc = make_rsrc4(base, extent);
     rowstep = (uint32_t)(ld * 2);
-    lds0 = (uint32_t)(wave * NI_BLK * 1024);
-    row0 = wave * NI_BLK * 4 + (lane >> 4);
+    lds0 = (uint32_t)(wave * NI * 1024);
+    row0 = wave * NI * 4 + (lane >> 4);
 #pragma unroll
-    for (int q = 0; q < NI_BLK; ++q) {
+    for (int q = 0; q < NI; ++q) {
       const int r = row0 + 4 * q;
       const int c = (lane & 15) ^ swz(r);
       boff[q] = (uint32_t)(((int64_t)r * ld + col0 + 8 * c) * 2);
@@ -134,7 +136,7 @@ struct BlockDma {
   __device__ __forceinline__ void load(uint32_t dst, int64_t first_row, int valid) const {
     const uint32_t step = (uint32_t)(first_row * rowstep);
 #pragma unroll
-    for (int q = 0; q < NI_BLK; ++q)
+    for (int q = 0; q < NI; ++q)
       dma16(rsrc, dst + lds0 + q * 1024, row0 + 4 * q < valid ? boff[q] + step : kOOB);
   }
 };
@@ -209,8 +211,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
     const uint32_t off = qv ? (uint32_t)(((base_row + q) * ld3 + hd * HD + 16 * kk + 8 * h) * 2) : kOOB;
     qf[kk] = __builtin_bit_cast(bf16x8, bload16(rq, off));
   }
-  const BlockDma dk(p.qkv, ext3, ld3, p.h + hd * HD, w, lane);
-  const BlockDma dv(p.qkv, ext3, ld3, 2 * p.h + hd * HD, w, lane);
+  const BlockDma<4> dk(p.qkv, ext3, ld3, p.h + hd * HD, w, lane);
+  const BlockDma<4> dv(p.qkv, ext3, ld3, 2 * p.h + hd * HD, w, lane);
   const RowFrag rf(lane);
   const TrFrag tf(lane);
 
@@ -228,7 +230,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
   };
   fetch(sK0, sV0, 0);
   if (nkb > 1) fetch(sK1, sV1, 1);
-  if (nkb > 1) wait_vm_barrier<2 * NI_BLK>();
+  if (nkb > 1) wait_vm_barrier<2 * BlockDma<4>::NI>();
   else wait_vm_barrier<0>();
 
   // Block kb from (sk, sv); at the end every wave has its copies of block
@@ -351,8 +353,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
   dsum += __shfl_xor(dsum, 32);
   const float lse = qv ? p.lse2[(int64_t)hd * p.T + base_row + q] : 0.0f;
   if (qv && h == 0) p.dsum[(int64_t)hd * p.T + base_row + q] = dsum;
-  const BlockDma dk(p.qkv, ext3, ld3, p.h + hd * HD, w, lane);
-  const BlockDma dv(p.qkv, ext3, ld3, 2 * p.h + hd * HD, w, lane);
+  const BlockDma<4> dk(p.qkv, ext3, ld3, p.h + hd * HD, w, lane);
+  const BlockDma<4> dv(p.qkv, ext3, ld3, 2 * p.h + hd * HD, w, lane);
   const RowFrag rf(lane);
   const TrFrag tf(lane);
 
@@ -369,7 +371,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
   };
   fetch(sK0, sV0, 0);
   if (nkb > 1) fetch(sK1, sV1, 1);
-  if (nkb > 1) wait_vm_barrier<2 * NI_BLK>();
+  if (nkb > 1) wait_vm_barrier<2 * BlockDma<4>::NI>();
   else wait_vm_barrier<0>();
 
   auto body = [&](char* sk, char* sv, int kb) {
@@ -427,56 +429,63 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
 }
 
 // =============================================================== dK, dV
-// Workgroup: 128 key rows (32 per wave) of one (sequence, head); (Q, dO)
-// blocks of 64 queries, from the first query that can see the keys to the end.
-// LSE2 and D of a block ride along: lanes 0-15 of one extra copy fetch 64
-// LSE2 values, lanes 16-31 the 64 D values (the rest read as zero).
-__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) attn_bwd_dkdv(AttnParams p) {
+// Workgroup: 128 key rows of one (sequence, head), four 32-key blocks;
+// (Q, dO) blocks of 64 queries, from the first query that can see the keys to
+// the end.  LSE2 and D of a block ride along: lanes 0-15 of one extra copy
+// fetch 64 LSE2 values, lanes 16-31 the 64 D values (the rest read as zero).
+// Grid (heads x sequences, key blocks), heaviest first: key block 0 sees every
+// query block, and workgroups are handed out with x varying fastest.
+// Each key block is worked by a pair of waves on one SIMD: wave k (k < 4) computes S = Q K^T,
+// P and dV += P^T dO for key block k, wave k + 4 computes dP = dO V^T,
+// dS = P (dP - D) and dK += dS^T Q for the same keys, reading P from LDS
+// (fp32, in the register order both waves share).  Each wave holds half the
+// registers of one wave doing all four products, so two fit on a SIMD and
+// one's waits and LDS reads overlap the other's MFMAs: 16% shorter than one
+// wave per key block doing all four products (one wave per SIMD), with the
+// same products and summation order per key, so the same bits.
+constexpr int NTP = 512;  // 8 waves
+__global__ void __attribute__((amdgpu_flat_work_group_size(NTP, NTP), amdgpu_waves_per_eu(2, 2))) attn_bwd_dkdv_pair(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) char sQ0[BLK];
   __shared__ __attribute__((aligned(1024))) char sG0[BLK];
   __shared__ __attribute__((aligned(1024))) char sQ1[BLK];
   __shared__ __attribute__((aligned(1024))) char sG1[BLK];
   __shared__ __attribute__((aligned(1024))) char sLD0[1024];
   __shared__ __attribute__((aligned(1024))) char sLD1[1024];
-  // Grid (heads x sequences, key blocks), heaviest first: key block 0 sees
-  // every query block, and workgroups are handed out with x varying fastest.
+  __shared__ __attribute__((aligned(1024))) float sP[4 * 2 * 16 * 64];  // [key block][half][register][lane]
   const int kb = (int)blockIdx.y;
   const int hd = blockIdx.x % p.heads, sq = blockIdx.x / p.heads;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, lc = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kbw = w & 3;          // key block of the wave
+  const bool role_p = w < 4;      // S, P, dV (else dP, dS, dK)
   const int64_t ld3 = 3LL * p.h, base_row = (int64_t)sq * p.seq;
   const uint32_t ext3 = (uint32_t)((int64_t)p.T * ld3 * 2);
   const uint32_t exth = (uint32_t)((int64_t)p.T * p.h * 2);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qkv, ext3);
   const __amdgpu_buffer_rsrc_t rdq = make_rsrc(p.dqkv, ext3);
   const float c = p.scale * kLog2e;
-  const int kv = kb * 128 + 32 * w + lc;  // this lane's key row
+  const int kv = kb * 128 + 32 * kbw + lc;  // this lane's key row
   const bool kvv = kv < p.seq;
-  bf16x8 kf[8], vf[8];
+  bf16x8 xf[8];  // K rows (role P) or V rows (role dS)
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     const int dd = hd * HD + 16 * kk + 8 * h;
-    const uint32_t offk = kvv ? (uint32_t)(((base_row + kv) * ld3 + p.h + dd) * 2) : kOOB;
-    const uint32_t offv = kvv ? (uint32_t)(((base_row + kv) * ld3 + 2 * p.h + dd) * 2) : kOOB;
-    kf[kk] = __builtin_bit_cast(bf16x8, bload16(rq, offk));
-    vf[kk] = __builtin_bit_cast(bf16x8, bload16(rq, offv));
+    const uint32_t off = kvv ? (uint32_t)(((base_row + kv) * ld3 + (role_p ? p.h : 2 * p.h) + dd) * 2) : kOOB;
+    xf[kk] = __builtin_bit_cast(bf16x8, bload16(rq, off));
   }
-  const BlockDma dmq(p.qkv, ext3, ld3, hd * HD, w, lane);
-  const BlockDma dmg(p.dout, exth, p.h, hd * HD, w, lane);
-  // LSE2 / D copy: the [heads, T] fp32 rows of this head, 16 bytes per lane.
+  const BlockDma<8> dmq(p.qkv, ext3, ld3, hd * HD, w, lane);
+  const BlockDma<8> dmg(p.dout, exth, p.h, hd * HD, w, lane);
   const dev::u32x4 rl = make_rsrc4(p.lse2 + (int64_t)hd * p.T + base_row, (uint32_t)(p.seq * 4));
   const dev::u32x4 rd = make_rsrc4(p.dsum + (int64_t)hd * p.T + base_row, (uint32_t)(p.seq * 4));
   const RowFrag rf(lane);
   const TrFrag tf(lane);
+  float* const myP = sP + kbw * 2 * 16 * 64 + lane;
 
-  f32x16 dk[4], dv[4];
+  f32x16 acc[4];  // dV^T (role P) or dK^T (role dS) of the wave's keys
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    dk[d] = zero16();
-    dv[d] = zero16();
-  }
-  const int kv_wave_min = kb * 128 + 32 * w, kv_wave_max = kv_wave_min + 31;
-  const int qb0 = kb * 2;                // first 64-query block that can see these keys
+  for (int d = 0; d < 4; ++d) acc[d] = zero16();
+  const int kv_wave_min = kb * 128 + 32 * kbw, kv_wave_max = kv_wave_min + 31;
+  const int qb0 = kb * 2;
   const int nqb = (p.seq + 63) / 64 - qb0;
 
   auto fetch = [&](char* sq_, char* sg, char* sld, int j) {
@@ -497,46 +506,73 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
 
   auto body = [&](char* sq_, char* sg, const char* sld, int j) {
     const int q0 = (qb0 + j) * 64;
-    if (q0 + 63 >= kv_wave_min) {  // some query of the block sees some key of the wave
-      const float* sL = reinterpret_cast<const float*>(sld);
-      const float* sD = reinterpret_cast<const float*>(sld + 256);
-      const bool masked = q0 < kv_wave_max || q0 + 64 > p.seq;
+    const bool active = q0 + 63 >= kv_wave_min;  // some query of the block sees some key of the pair
+    const float* sL = reinterpret_cast<const float*>(sld);
+    const float* sD = reinterpret_cast<const float*>(sld + 256);
+    f32x16 x[2];  // S -> P (role P) or dP (role dS), per 32-query half
+    if (active) {
+      const char* rows = role_p ? sq_ : sg;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {  // two 32-query halves
-        f32x16 s = zero16(), dp = zero16();
+      for (int b = 0; b < 2; ++b) {
+        x[b] = zero16();
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          s = mfma(rf.get(sq_, b, kk), kf[kk], s);   // S[q][kv]
-          dp = mfma(rf.get(sg, b, kk), vf[kk], dp);  // dP[q][kv]
-        }
+        for (int kk = 0; kk < 8; ++kk) x[b] = mfma(rf.get(rows, b, kk), xf[kk], x[b]);
+      }
+      if (role_p) {
+        const bool masked = q0 < kv_wave_max || q0 + 64 > p.seq;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int ql = 32 * b + 8 * g + 4 * h;  // local query row of register 4g
-          const f32x4 lv = *reinterpret_cast<const f32x4*>(sL + ql);
-          const f32x4 dv4 = *reinterpret_cast<const f32x4*>(sD + ql);
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int qq = q0 + ql + t;
-            const int r = 4 * g + t;
-            float pr = exp2_hw(fmaf(s[r], c, -lv[t]));
-            if (masked && (kv > qq || qq >= p.seq)) pr = 0.0f;
-            s[r] = pr;                      // P
-            dp[r] = pr * (dp[r] - dv4[t]);  // dS
+          for (int g = 0; g < 4; ++g) {
+            const int ql = 32 * b + 8 * g + 4 * h;
+            const f32x4 lv = *reinterpret_cast<const f32x4*>(sL + ql);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int qq = q0 + ql + t;
+              const int r = 4 * g + t;
+              float pr = exp2_hw(fmaf(x[b][r], c, -lv[t]));
+              if (masked && (kv > qq || qq >= p.seq)) pr = 0.0f;
+              x[b][r] = pr;
+              myP[(b * 16 + r) * 64] = pr;
+            }
           }
-        }
+      }
+    }
+    __syncthreads();  // P of the block is in LDS
+    if (active) {
+      if (role_p) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          float pv[8], sv[8];
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            pv[e] = s[8 * st + e];
-            sv[e] = dp[8 * st + e];
+          for (int st = 0; st < 2; ++st) {
+            float pv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pv[e] = x[b][8 * st + e];
+            const bf16x8 pf = to_frag(pv);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) acc[d] = mfma(tf.get(sg, d, 2 * b + st), pf, acc[d]);  // dV^T[d][kv]
           }
-          const bf16x8 pf = to_frag(pv), sf = to_frag(sv);
+      } else {
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            dv[d] = mfma(tf.get(sg, d, 2 * b + st), pf, dv[d]);   // dV^T[d][kv]
-            dk[d] = mfma(tf.get(sq_, d, 2 * b + st), sf, dk[d]);  // dK^T[d][kv]
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int ql = 32 * b + 8 * g + 4 * h;
+            const f32x4 dv4 = *reinterpret_cast<const f32x4*>(sD + ql);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int r = 4 * g + t;
+              x[b][r] = myP[(b * 16 + r) * 64] * (x[b][r] - dv4[t]);  // dS
+            }
+          }
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            float sv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sv[e] = x[b][8 * st + e];
+            const bf16x8 sf = to_frag(sv);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) acc[d] = mfma(tf.get(sq_, d, 2 * b + st), sf, acc[d]);  // dK^T[d][kv]
           }
         }
       }
@@ -551,20 +587,17 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
   }
   if (j < nqb) body(sQ0, sG0, sLD0, j);
 
+  const float sc = role_p ? 1.0f : p.scale;
+  const int col = role_p ? 2 * p.h : p.h;
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int dd = hd * HD + 32 * d + 8 * g + 4 * h;
-      const int64_t row = base_row + kv;
-      const uint32_t offk = kvv ? (uint32_t)((row * ld3 + p.h + dd) * 2) : kOOB;
-      const uint32_t offv = kvv ? (uint32_t)((row * ld3 + 2 * p.h + dd) * 2) : kOOB;
-      const float sc = p.scale;
-      const u32x2 kv2 = {pack_bf16x2(dk[d][4 * g] * sc, dk[d][4 * g + 1] * sc),
-                         pack_bf16x2(dk[d][4 * g + 2] * sc, dk[d][4 * g + 3] * sc)};
-      const u32x2 vv2 = {pack_bf16x2(dv[d][4 * g], dv[d][4 * g + 1]), pack_bf16x2(dv[d][4 * g + 2], dv[d][4 * g + 3])};
-      bstore8(rdq, offk, kv2);
-      bstore8(rdq, offv, vv2);
+      const uint32_t off = kvv ? (uint32_t)(((base_row + kv) * ld3 + col + dd) * 2) : kOOB;
+      const u32x2 v2 = {pack_bf16x2(acc[d][4 * g] * sc, acc[d][4 * g + 1] * sc),
+                        pack_bf16x2(acc[d][4 * g + 2] * sc, acc[d][4 * g + 3] * sc)};
+      bstore8(rdq, off, v2);
     }
 }
 
@@ -610,7 +643,7 @@ zb_status launch_attention_bwd(const AttnArgs& a, hipStream_t s) {
   }
   {
     ProfScope ps("attn_bwd_dkdv", alg * 4.0 / 7.0, 2.0 * p.T * 6.0 * p.h, s);
-    hipLaunchKernelGGL(attn_bwd_dkdv, grid, dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(attn_bwd_dkdv_pair, grid, dim3(NTP), 0, s, p);
     ZB_HIP_CHECK(hipGetLastError());
   }
   return ZB_OK;
