@@ -170,7 +170,13 @@ zb_status zb_schedule_heuristic(int P, int m, const int64_t* times, int64_t t_co
  * between chunks on different devices; m_b, m_w the stash of one chunk and
  * microbatch; m_limit the budget per device (P M_B of a whole stage = 2P *
  * m_b).  The order is list-scheduled within the budget (a forward of a
- * device's earlier chunk keeps room for one later-chunk forward).  Emits the
+ * device's earlier chunk keeps room for one later-chunk forward).  When
+ * T_F = T_B = T_W a second candidate is searched: an order at unit slots with
+ * no idle slot inside any device's span, at most m_limit / max(m_b, m_w) live
+ * chunk stashes per device (the section reports zero bubble within P M_B);
+ * the search gives up after a fixed number of steps (it finds one for
+ * m >= 2P - 1 up to P = 9 at least).  The candidate with the smaller makespan
+ * at times and t_comm is emitted, ties to the searched one.  Emits the
  * 6*P*m chunk passes (zb_op.stage = chunk index 0..2P-1, split B and W, each
  * chunk's W ascending) into linear_out (host, cap >= 6*P*m) by start time,
  * ties to the lower chunk: a one-device order for 2P chained stages.  stats

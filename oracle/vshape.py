@@ -29,6 +29,12 @@ again in the design notes):
   B; a pass over M_limit is not a candidate, and a stage over the budget with
   a W pending runs that W.  M_limit for ZB-V is P M_B of a whole stage = 2P
   chunk M_B.
+* At equal pass times the section's result is zero bubble within P M_B.  The
+  list-scheduled order does not reach it, so a second candidate is searched
+  (search_order): passes are unit slots, device d works in every slot from d
+  to d + 6m - 1, and a depth-first search fills the slots device by device.
+  Of the two candidates the one with the smaller simulated makespan at the
+  given times is kept (ties: the searched one).
 """
 from __future__ import annotations
 
@@ -43,14 +49,33 @@ def device_of(c: int, P: int) -> int:
     return c if c < P else 2 * P - 1 - c
 
 
+SEARCH_BUDGET = 1_000_000   # search steps before the searched candidate is given up
+
+
 def build(P: int, m: int, t: Dict[str, int], m_b: int, m_w: int, m_limit: int,
           t_comm: int = 0) -> List[List[VOp]]:
-    """Per-device pass orders of the V schedule."""
+    """Per-device pass orders of the V schedule: the list-scheduled order, or at
+    equal pass times the searched zero-bubble order when it is not slower."""
     if P < 1 or m < 1:
         raise ValueError("P and m must be >= 1")
     reserve = max(0, m_w - m_b)
     if m_b < 0 or m_w < 0 or m_limit < 2 * m_b + reserve or m_limit < m_w:
         raise ValueError("M_limit below one microbatch through both chunks")
+    listed = list_orders(P, m, t, m_b, m_w, m_limit, t_comm)
+    if not t["F"] == t["B"] == t["W"]:
+        return listed
+    found = search_order(P, m, m_b, m_w, m_limit)
+    if found is None:
+        return listed
+    if simulate(P, found, t, t_comm).makespan <= simulate(P, listed, t, t_comm).makespan:
+        return found
+    return listed
+
+
+def list_orders(P: int, m: int, t: Dict[str, int], m_b: int, m_w: int, m_limit: int,
+                t_comm: int = 0) -> List[List[VOp]]:
+    """The list-scheduled candidate (rules in the module docstring)."""
+    reserve = max(0, m_w - m_b)
     C = 2 * P
     nf = [0] * C
     nb = [0] * C
@@ -140,6 +165,180 @@ def build(P: int, m: int, t: Dict[str, int], m_b: int, m_w: int, m_limit: int,
         free[d] = st + t[kind]
         placed += 1
     return orders
+
+
+def latest_starts(P: int, m: int) -> Dict[Tuple[str, int, int], int]:
+    """Latest slot of every chunk pass when device d works in slots d .. d+6m-1.
+
+    A pass must leave room for everything that depends on it: each successor
+    starts at least one slot later (F(c+1,j) and B(c,j) after F(c,j); B(c-1,j)
+    and W(c,j) after B(c,j); the same pass of microbatch j+1 after j), and no
+    pass ends after its device's last slot."""
+    C = 2 * P
+    L: Dict[Tuple[str, int, int], int] = {}
+    for j in range(m - 1, -1, -1):
+        for c in range(C):
+            cap = device_of(c, P) + 6 * m - 1
+            if j + 1 < m:
+                cap = min(cap, L[("W", c, j + 1)] - 1)
+            L[("W", c, j)] = cap
+        for c in range(C):
+            cap = min(device_of(c, P) + 6 * m - 1, L[("W", c, j)] - 1)
+            if c > 0:
+                cap = min(cap, L[("B", c - 1, j)] - 1)
+            if j + 1 < m:
+                cap = min(cap, L[("B", c, j + 1)] - 1)
+            L[("B", c, j)] = cap
+        for c in range(C - 1, -1, -1):
+            cap = min(device_of(c, P) + 6 * m - 1, L[("B", c, j)] - 1)
+            if c + 1 < C:
+                cap = min(cap, L[("F", c + 1, j)] - 1)
+            if j + 1 < m:
+                cap = min(cap, L[("F", c, j + 1)] - 1)
+            L[("F", c, j)] = cap
+    return L
+
+
+def search_order(P: int, m: int, m_b: int, m_w: int, m_limit: int,
+                 budget: int = SEARCH_BUDGET) -> Optional[List[List[VOp]]]:
+    """A V order with no idle slot inside any device's span at unit pass times,
+    within m_limit per device, or None (none found within the budget).
+
+    Slots are filled in time order, device 0 to P-1 within a slot; a device
+    picks among the passes whose producers finished before the slot began.
+    Choices are tried by urgency: the pass's latest start (latest_starts; for
+    microbatches more than P+1 before the last, the value of microbatch m-P-1
+    less six slots per microbatch, so that early microbatches are as urgent as
+    in a short pipeline), then W before F before B, then the earlier chunk.
+    After each slot the branch is cut when a pending pass is past its latest
+    start, or when some device cannot have work in every coming slot even if
+    all other devices ran every chain as early as it allows."""
+    C = 2 * P
+    lst = latest_starts(P, m)
+    h = P + 1
+
+    def urgency(k: str, c: int, j: int) -> int:
+        if m > h and j < m - h:
+            return lst[(k, c, m - h)] - 6 * (m - h - j)
+        return lst[(k, c, j)]
+
+    cnt = {"F": [0] * C, "B": [0] * C, "W": [0] * C}
+    done = [0] * P
+    orders: List[List[VOp]] = [[] for _ in range(P)]
+    rank = {"W": 0, "F": 1, "B": 2}
+
+    # Stashes live per device (forward started, W not yet): at most `room`, so
+    # that the ledger level, at most max(M_B, M_W) per live stash, stays
+    # within m_limit whatever the ratio of M_B to M_W.
+    room = m_limit // max(m_b, m_w) if max(m_b, m_w) > 0 else 2 * m
+
+    def choices(d: int, snap) -> List[Tuple[str, int]]:
+        sF, sB, sW = snap
+        live = sum(sF[c] - sW[c] for c in (d, C - 1 - d))
+        out = []
+        for c in (d, C - 1 - d):
+            if sF[c] < m and live < room and (c == 0 or sF[c - 1] > sF[c]):
+                out.append(("F", c))
+            if sB[c] < sF[c] and (c == C - 1 or sB[c + 1] > sB[c]):
+                out.append(("B", c))
+            if sW[c] < sB[c]:
+                out.append(("W", c))
+        out.sort(key=lambda kc: (urgency(kc[0], kc[1], cnt[kc[0]][kc[1]]), rank[kc[0]]))
+        return out
+
+    def hopeless(t: int) -> bool:
+        for k in "FBW":
+            for c in range(C):
+                j = cnt[k][c]
+                if j < m and lst[(k, c, j)] < t:
+                    return True
+        est: Dict[Tuple[str, int, int], int] = {}
+        for j in range(m):
+            for c in range(C):
+                if cnt["F"][c] <= j:
+                    e = t
+                    if c > 0 and ("F", c - 1, j) in est:
+                        e = max(e, est[("F", c - 1, j)] + 1)
+                    if j > 0 and ("F", c, j - 1) in est:
+                        e = max(e, est[("F", c, j - 1)] + 1)
+                    est[("F", c, j)] = e
+            for c in range(C - 1, -1, -1):
+                if cnt["B"][c] <= j:
+                    e = t
+                    if ("F", c, j) in est:
+                        e = max(e, est[("F", c, j)] + 1)
+                    if c < C - 1 and ("B", c + 1, j) in est:
+                        e = max(e, est[("B", c + 1, j)] + 1)
+                    if j > 0 and ("B", c, j - 1) in est:
+                        e = max(e, est[("B", c, j - 1)] + 1)
+                    est[("B", c, j)] = e
+                if cnt["W"][c] <= j:
+                    e = t
+                    if ("B", c, j) in est:
+                        e = max(e, est[("B", c, j)] + 1)
+                    if j > 0 and ("W", c, j - 1) in est:
+                        e = max(e, est[("W", c, j - 1)] + 1)
+                    est[("W", c, j)] = e
+        for d in range(P):
+            if done[d] == 6 * m:
+                continue
+            mine = sorted(e for (k, c, j), e in est.items() if device_of(c, P) == d)
+            first = max(t, d)
+            if any(e > first + i for i, e in enumerate(mine)):
+                return True
+        return False
+
+    # Depth-first search with an explicit stack.  A level is (slot t, device d);
+    # d == P closes the slot.  Each level holds its choices and the index of the
+    # one applied; None stands for a device that is finished or not started.
+    snaps = {}
+    stack = []
+    steps = 0
+
+    def enter(t: int, d: int) -> Optional[list]:
+        nonlocal steps
+        steps += 1
+        if steps > budget:
+            raise TimeoutError
+        if d == P:
+            if all(x == 6 * m for x in done):
+                return ["done"]
+            if hopeless(t + 1):
+                return []
+            snaps[t + 1] = (tuple(cnt["F"]), tuple(cnt["B"]), tuple(cnt["W"]))
+            return [None]
+        if done[d] == 6 * m or t < d:
+            return [None]
+        return choices(d, snaps[t])
+
+    snaps[0] = (tuple(cnt["F"]), tuple(cnt["B"]), tuple(cnt["W"]))
+    try:
+        stack.append([0, 0, enter(0, 0), -1])
+        while stack:
+            top = stack[-1]
+            t, d, opts, i = top
+            if opts and opts[0] == "done":
+                return orders
+            if i >= 0 and opts[i] is not None:
+                k, c = opts[i]
+                cnt[k][c] -= 1
+                done[d] -= 1
+                orders[d].pop()
+            i += 1
+            top[3] = i
+            if i >= len(opts):
+                stack.pop()
+                continue
+            if opts[i] is not None:
+                k, c = opts[i]
+                orders[d].append((k, c, cnt[k][c]))
+                cnt[k][c] += 1
+                done[d] += 1
+            nt, nd = (t + 1, 0) if d == P else (t, d + 1)
+            stack.append([nt, nd, enter(nt, nd), -1])
+    except TimeoutError:
+        return None
+    return None
 
 
 @dataclass

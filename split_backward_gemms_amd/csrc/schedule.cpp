@@ -538,6 +538,10 @@ extern "C" zb_status zb_schedule_heuristic(int P, int m, const int64_t* times, i
 //    forward of the earlier chunk keeps room for a later-chunk forward and a
 //    B's growth, a forward of the later chunk room for its B's growth;
 //  - hand-offs between chunks on different devices cost t_comm.
+// At equal pass times the section reports zero bubble within P M_B, which
+// that list order does not reach.  A second candidate comes from a search
+// over unit slots (zbv_search below); the candidate with the smaller makespan
+// simulated at the given times and t_comm wins, ties to the searched one.
 namespace {
 
 zb_status zbv_build(int P, int m, const int64_t* t, int64_t t_comm, int64_t m_b, int64_t m_w, int64_t m_limit,
@@ -634,6 +638,270 @@ zb_status zbv_build(int P, int m, const int64_t* t, int64_t t_comm, int64_t m_b,
   return ZB_OK;
 }
 
+constexpr int64_t kZbvSearchBudget = 1000000;  // search steps before the searched candidate is given up
+
+// Latest slot of every chunk pass when device d works in slots d .. d+6m-1:
+// each successor (F(c+1,j) and B(c,j) after F(c,j); B(c-1,j) and W(c,j) after
+// B(c,j); the same pass of microbatch j+1 after j) starts at least one slot
+// later, and no pass ends after its device's last slot.  Index
+// (kind*C + c)*m + j, kind 0 = F, 1 = B, 2 = W.
+std::vector<int> zbv_latest_starts(int P, int m) {
+  const int C = 2 * P;
+  auto dev = [P](int c) { return c < P ? c : 2 * P - 1 - c; };
+  std::vector<int> L((size_t)3 * C * m);
+  auto at = [&](int k, int c, int j) -> int& { return L[((size_t)k * C + c) * m + j]; };
+  for (int j = m - 1; j >= 0; --j) {
+    for (int c = 0; c < C; ++c) {
+      int cap = dev(c) + 6 * m - 1;
+      if (j + 1 < m) cap = std::min(cap, at(2, c, j + 1) - 1);
+      at(2, c, j) = cap;
+    }
+    for (int c = 0; c < C; ++c) {
+      int cap = std::min(dev(c) + 6 * m - 1, at(2, c, j) - 1);
+      if (c > 0) cap = std::min(cap, at(1, c - 1, j) - 1);
+      if (j + 1 < m) cap = std::min(cap, at(1, c, j + 1) - 1);
+      at(1, c, j) = cap;
+    }
+    for (int c = C - 1; c >= 0; --c) {
+      int cap = std::min(dev(c) + 6 * m - 1, at(1, c, j) - 1);
+      if (c + 1 < C) cap = std::min(cap, at(0, c + 1, j) - 1);
+      if (j + 1 < m) cap = std::min(cap, at(0, c, j + 1) - 1);
+      at(0, c, j) = cap;
+    }
+  }
+  return L;
+}
+
+struct VPass { char kind; int chunk, mb; };
+
+// A V order with no idle slot inside any device's span at unit pass times,
+// within m_limit per device.  Slots are filled in time order, devices 0..P-1
+// within a slot; a device picks among the passes whose producers finished
+// before the slot began.  Choices go by urgency: the pass's latest start (for
+// microbatches more than P+1 before the last, that of microbatch m-P-1 less six
+// slots per microbatch, so early microbatches are as urgent as in a short
+// pipeline), then W before F before B, then the earlier chunk.  After each slot
+// a branch is cut when a pending pass is past its latest start, or when some
+// device cannot have work in every coming slot even if every chain ran as early
+// as it allows.  Returns false when none is found within the budget.
+bool zbv_search(int P, int m, int64_t m_b, int64_t m_w, int64_t m_limit,
+                std::vector<std::vector<VPass>>& orders) {
+  const int C = 2 * P, h = P + 1;
+  auto dev = [P](int c) { return c < P ? c : 2 * P - 1 - c; };
+  const std::vector<int> lst = zbv_latest_starts(P, m);
+  auto L = [&](int k, int c, int j) { return lst[((size_t)k * C + c) * m + j]; };
+  auto urgency = [&](int k, int c, int j) {
+    if (m > h && j < m - h) return L(k, c, m - h) - 6 * (m - h - j);
+    return L(k, c, j);
+  };
+  std::vector<int> cnt((size_t)3 * C, 0), done(P, 0);
+  auto N = [&](int k, int c) -> int& { return cnt[(size_t)k * C + c]; };
+  orders.assign(P, {});
+  static const int rank[3] = {1, 2, 0};  // F, B, W -> W first, then F, then B
+  static const char kname[3] = {'F', 'B', 'W'};
+
+  struct Choice { int k, c; };  // k = -1: nothing this slot
+  struct Level { int t, d; bool finished; std::vector<Choice> opts; int i; };
+  std::vector<std::vector<int>> snaps;  // counts at the start of each slot
+  std::vector<int> est((size_t)3 * C * m), mine;
+
+  auto hopeless = [&](int t) {
+    for (int k = 0; k < 3; ++k)
+      for (int c = 0; c < C; ++c) {
+        const int j = N(k, c);
+        if (j < m && L(k, c, j) < t) return true;
+      }
+    auto E = [&](int k, int c, int j) -> int& { return est[((size_t)k * C + c) * m + j]; };
+    std::fill(est.begin(), est.end(), -1);
+    for (int j = 0; j < m; ++j) {
+      for (int c = 0; c < C; ++c) {
+        if (N(0, c) > j) continue;
+        int e = t;
+        if (c > 0 && E(0, c - 1, j) >= 0) e = std::max(e, E(0, c - 1, j) + 1);
+        if (j > 0 && E(0, c, j - 1) >= 0) e = std::max(e, E(0, c, j - 1) + 1);
+        E(0, c, j) = e;
+      }
+      for (int c = C - 1; c >= 0; --c) {
+        if (N(1, c) <= j) {
+          int e = t;
+          if (E(0, c, j) >= 0) e = std::max(e, E(0, c, j) + 1);
+          if (c < C - 1 && E(1, c + 1, j) >= 0) e = std::max(e, E(1, c + 1, j) + 1);
+          if (j > 0 && E(1, c, j - 1) >= 0) e = std::max(e, E(1, c, j - 1) + 1);
+          E(1, c, j) = e;
+        }
+        if (N(2, c) <= j) {
+          int e = t;
+          if (E(1, c, j) >= 0) e = std::max(e, E(1, c, j) + 1);
+          if (j > 0 && E(2, c, j - 1) >= 0) e = std::max(e, E(2, c, j - 1) + 1);
+          E(2, c, j) = e;
+        }
+      }
+    }
+    for (int d = 0; d < P; ++d) {
+      if (done[d] == 6 * m) continue;
+      mine.clear();
+      for (int c : {d, C - 1 - d})
+        for (int k = 0; k < 3; ++k)
+          for (int j = N(k, c); j < m; ++j) mine.push_back(E(k, c, j));
+      std::sort(mine.begin(), mine.end());
+      const int first = std::max(t, d);
+      for (size_t i = 0; i < mine.size(); ++i)
+        if (mine[i] > first + (int)i) return true;
+    }
+    return false;
+  };
+
+  // Stashes live per device (forward started, W not yet): at most `room`, so
+  // that the ledger level, at most max(M_B, M_W) per live stash, stays within
+  // m_limit whatever the ratio of M_B to M_W.
+  const int64_t big = std::max(m_b, m_w);
+  const int64_t room = big > 0 ? m_limit / big : 2LL * m;
+  auto choices = [&](int d, const std::vector<int>& s, std::vector<Choice>& out) {
+    out.clear();
+    auto S = [&](int k, int c) { return s[(size_t)k * C + c]; };
+    int64_t live = 0;
+    for (int c : {d, C - 1 - d}) live += S(0, c) - S(2, c);
+    for (int c : {d, C - 1 - d}) {
+      if (S(0, c) < m && live < room && (c == 0 || S(0, c - 1) > S(0, c))) out.push_back({0, c});
+      if (S(1, c) < S(0, c) && (c == C - 1 || S(1, c + 1) > S(1, c))) out.push_back({1, c});
+      if (S(2, c) < S(1, c)) out.push_back({2, c});
+    }
+    std::stable_sort(out.begin(), out.end(), [&](const Choice& a, const Choice& b) {
+      const int ua = urgency(a.k, a.c, N(a.k, a.c)), ub = urgency(b.k, b.c, N(b.k, b.c));
+      if (ua != ub) return ua < ub;
+      return rank[a.k] < rank[b.k];
+    });
+  };
+
+  int64_t steps = 0;
+  auto enter = [&](int t, int d, Level& lv) -> bool {  // false: budget spent
+    if (++steps > kZbvSearchBudget) return false;
+    lv.t = t;
+    lv.d = d;
+    lv.finished = false;
+    lv.i = -1;
+    lv.opts.clear();
+    if (d == P) {
+      bool all = true;
+      for (int x : done) all = all && x == 6 * m;
+      if (all) {
+        lv.finished = true;
+        return true;
+      }
+      if (hopeless(t + 1)) return true;
+      if ((int)snaps.size() < t + 2) snaps.resize(t + 2);
+      snaps[t + 1] = cnt;
+      lv.opts.push_back({-1, -1});
+      return true;
+    }
+    if (done[d] == 6 * m || t < d) {
+      lv.opts.push_back({-1, -1});
+      return true;
+    }
+    choices(d, snaps[t], lv.opts);
+    return true;
+  };
+
+  snaps.assign(1, cnt);
+  std::vector<Level> stack(1);
+  if (!enter(0, 0, stack[0])) return false;
+  size_t depth = 1;
+  while (depth) {
+    Level& lv = stack[depth - 1];
+    if (lv.finished) return true;
+    if (lv.i >= 0 && lv.opts[lv.i].k >= 0) {
+      const Choice& ch = lv.opts[lv.i];
+      --N(ch.k, ch.c);
+      --done[lv.d];
+      orders[lv.d].pop_back();
+    }
+    ++lv.i;
+    if (lv.i >= (int)lv.opts.size()) {
+      --depth;
+      continue;
+    }
+    const Choice ch = lv.opts[lv.i];
+    if (ch.k >= 0) {
+      orders[lv.d].push_back({kname[ch.k], ch.c, N(ch.k, ch.c)});
+      ++N(ch.k, ch.c);
+      ++done[lv.d];
+    }
+    const int nt = lv.d == P ? lv.t + 1 : lv.t, nd = lv.d == P ? 0 : lv.d + 1;
+    if (stack.size() <= depth) stack.resize(depth + 1);
+    if (!enter(nt, nd, stack[depth])) return false;
+    ++depth;
+  }
+  return false;
+}
+
+// As-soon-as-possible start of every pass of fixed per-device V orders; false
+// when the orders deadlock.  ops/start are filled device by device.
+bool zbv_simulate(int P, int m, const std::vector<std::vector<VPass>>& orders, const int64_t* t,
+                  int64_t t_comm, std::vector<zb_op>& ops, std::vector<int64_t>& start) {
+  const int C = 2 * P;
+  auto dev = [P](int c) { return c < P ? c : 2 * P - 1 - c; };
+  auto hop = [&](int a, int b) { return dev(a) == dev(b) ? int64_t(0) : t_comm; };
+  std::vector<int64_t> end_f((size_t)C * m, -1), end_b((size_t)C * m, -1), freet(P, 0);
+  std::vector<size_t> pos(P, 0);
+  ops.clear();
+  start.clear();
+  size_t remaining = 0;
+  for (const auto& o : orders) remaining += o.size();
+  while (remaining) {
+    bool progressed = false;
+    for (int d = 0; d < P; ++d) {
+      while (pos[d] < orders[d].size()) {
+        const VPass& p = orders[d][pos[d]];
+        const int c = p.chunk, j = p.mb;
+        int64_t r = freet[d];
+        bool ok = true;
+        auto need = [&](int64_t e, int64_t extra) {
+          if (e < 0) ok = false;
+          else r = std::max(r, e + extra);
+        };
+        if (p.kind == 'F') {
+          if (c > 0) need(end_f[(size_t)(c - 1) * m + j], hop(c - 1, c));
+        } else if (p.kind == 'B') {
+          need(end_f[(size_t)c * m + j], 0);
+          if (c < C - 1) need(end_b[(size_t)(c + 1) * m + j], hop(c + 1, c));
+        } else {
+          need(end_b[(size_t)c * m + j], 0);
+        }
+        if (!ok) break;
+        const int64_t e = r + (p.kind == 'F' ? t[0] : (p.kind == 'B' ? t[1] : t[2]));
+        if (p.kind == 'F') end_f[(size_t)c * m + j] = e;
+        if (p.kind == 'B') end_b[(size_t)c * m + j] = e;
+        freet[d] = e;
+        zb_op o;
+        o.stage = c;
+        o.mb = j;
+        o.kind = p.kind;
+        ops.push_back(o);
+        start.push_back(r);
+        ++pos[d];
+        --remaining;
+        progressed = true;
+      }
+    }
+    if (!progressed) return false;
+  }
+  return true;
+}
+
+// Eq. 3 makespan of passes with start times: the largest per-device span.
+int64_t zbv_makespan(int P, const std::vector<zb_op>& ops, const std::vector<int64_t>& start, const int64_t* t) {
+  std::vector<int64_t> first(P, -1), last(P, 0);
+  for (size_t i = 0; i < ops.size(); ++i) {
+    const int c = ops[i].stage, d = c < P ? c : 2 * P - 1 - c;
+    const int64_t e = start[i] + (ops[i].kind == 'F' ? t[0] : (ops[i].kind == 'B' ? t[1] : t[2]));
+    if (first[d] < 0 || start[i] < first[d]) first[d] = start[i];
+    last[d] = std::max(last[d], e);
+  }
+  int64_t mk = 0;
+  for (int d = 0; d < P; ++d) mk = std::max(mk, last[d] - first[d]);
+  return mk;
+}
+
 }  // namespace
 
 extern "C" zb_status zb_schedule_zbv(int P, int m, const int64_t* times, int64_t t_comm, int64_t m_b, int64_t m_w,
@@ -654,6 +922,16 @@ extern "C" zb_status zb_schedule_zbv(int P, int m, const int64_t* times, int64_t
   std::vector<int64_t> start;
   zb_status st = zbv_build(P, m, times, t_comm, m_b, m_w, m_limit, ops, start);
   if (st != ZB_OK) return st;
+  if (times[0] == times[1] && times[1] == times[2]) {
+    std::vector<std::vector<VPass>> found;
+    std::vector<zb_op> s_ops;
+    std::vector<int64_t> s_start;
+    if (zbv_search(P, m, m_b, m_w, m_limit, found) && zbv_simulate(P, m, found, times, t_comm, s_ops, s_start) &&
+        zbv_makespan(P, s_ops, s_start, times) <= zbv_makespan(P, ops, start, times)) {
+      ops.swap(s_ops);
+      start.swap(s_start);
+    }
+  }
   // Linearize over the 2P chunk stages by start time, ties to the lower chunk.
   std::vector<int> idx(ops.size());
   for (size_t i = 0; i < idx.size(); ++i) idx[i] = (int)i;

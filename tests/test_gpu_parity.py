@@ -19,7 +19,7 @@ import split_backward_gemms_amd as zb
 import synthetic_inputs as si
 from oracle import stage as ost
 from oracle import schedules as sch
-from split_backward_gemms_amd.pipeline import EmulatedPipeline, heuristic_ops, upload, zbv_ops
+from split_backward_gemms_amd.pipeline import EmulatedPipeline, heuristic_ops, stash_per_microbatch, upload, zbv_ops
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -411,8 +411,14 @@ def test_zbv_order_matches_oracle_and_1f1b_bits(name):
     ws, xs, dys = _inputs(w)
     pipe = EmulatedPipeline(w, ws, ops=None, recompute_act=0)
     _, y0, dx0, dw0, _ = _run(w, ws, xs, dys, "1f1b", pipe)
-    for times in ((1, 1, 1), (2, 3, 1), (9, 9, 5)):
-        ops, stats, m_limit = zbv_ops(pipe.handles, w.n_micro, times)
+    orders = [(times, zbv_ops(pipe.handles, w.n_micro, times)[0]) for times in ((1, 1, 1), (2, 3, 1), (9, 9, 5))]
+    # the searched zero-bubble order (equal times, P whole-stage stashes of the larger kind per device)
+    m_b, m_w = stash_per_microbatch(pipe.handles)
+    n_dev = w.n_stages // 2
+    ops, st = zb.zb_schedule_zbv(n_dev, w.n_micro, (1, 1, 1), m_b, m_w, 2 * n_dev * max(m_b, m_w))
+    assert st["bubble"] == 0
+    orders.append(("searched", ops))
+    for times, ops in orders:
         assert zb.zb_schedule_validate(w.n_stages, w.n_micro, ops) == (zb.ZB_OK, -1)
         _, y, dx, dw, _ = _run(w, ws, xs, dys, ops, pipe)
         for j in range(w.n_micro):

@@ -329,6 +329,44 @@ def test_zbv_matches_oracle():
         assert zb.zb_schedule_validate(2 * P, m, ops) == (zb.ZB_OK, -1)
 
 
+def test_zbv_equal_times_matches_oracle():
+    """At equal pass times both sides search for a zero-bubble order and keep
+    the better of it and the list order: same orders, same statistics."""
+    from oracle import vshape as vs
+    rng = random.Random(17)
+    for _ in range(60):
+        P = rng.randint(1, 5)
+        m = rng.randint(1, 4 * P)
+        tt = rng.randint(1, 4)
+        t = {"F": tt, "B": tt, "W": tt}
+        m_b, m_w = rng.randint(1, 4), rng.randint(1, 4)
+        lo = 2 * m_b + max(0, m_w - m_b)
+        m_limit = max(m_w, rng.choice([lo, 2 * P * max(m_b, m_w), rng.randint(lo, 3 * P * max(m_b, m_w))]))
+        comm = rng.choice([0, 0, 0, 1])
+        orders = vs.build(P, m, t, m_b, m_w, m_limit, comm)
+        sim = vs.simulate(P, orders, t, comm)
+        ops, st = zb.zb_schedule_zbv(P, m, (tt, tt, tt), m_b, m_w, m_limit, comm)
+        assert ops == vs.linearize(orders, sim)
+        assert (st["makespan"], st["ideal"], st["bubble"]) == (sim.makespan, sim.ideal, sim.bubble)
+
+
+@pytest.mark.parametrize("P,m", [(2, 4), (4, 8), (4, 32), (6, 18), (7, 21), (8, 16), (8, 24), (8, 32), (8, 64)])
+def test_zbv_zero_bubble_at_equal_times(P, m):
+    """The native V order at T_F = T_B = T_W: no bubble on any device, each
+    device peaking at P M_B of a whole stage (checked with the oracle's
+    simulator and ledger)."""
+    from oracle import vshape as vs
+    ops, st = zb.zb_schedule_zbv(P, m, (1, 1, 1), 1, 1, 2 * P)
+    assert st["bubble"] == 0
+    assert zb.zb_schedule_validate(2 * P, m, ops) == (zb.ZB_OK, -1)
+    orders = [[] for _ in range(P)]
+    for c, k, j in ops:
+        orders[vs.device_of(c, P)].append((k, c, j))
+    sim = vs.simulate(P, orders, {"F": 1, "B": 1, "W": 1})
+    assert sim.bubble == 0 and all(x == sim.ideal for x in sim.device_cost)
+    assert [vs.peak_memory(o, 1, 1) for o in orders] == [2 * P] * P
+
+
 def test_zbv_rejects_small_budget():
     with pytest.raises(zb.ZbError):
         zb.zb_schedule_zbv(4, 8, (1, 1, 1), 2, 3, 4)

@@ -1,8 +1,9 @@
 """Pins of the ZB-V oracle (oracle/vshape.py): the V placement, validity of its
 orders, balanced per-device memory, its bubble against the handcrafted orders,
-and — independently of the list-scheduled order — that a zero-bubble V order
-within P M_B exists at equal pass times, as "Zero Bubble Pipeline Parallelism"
-section 6 states (exhaustive search on the smallest pipeline).
+and the result of "Zero Bubble Pipeline Parallelism" section 6 at equal pass
+times: zero bubble with P M_B per device.  An exhaustive search on the smallest
+pipeline (written here, independent of the oracle's own search) shows such an
+order exists; the built orders reach it for P = 2 .. 8.
 """
 import json
 import os
@@ -59,7 +60,7 @@ def test_budget_below_one_microbatch_is_rejected():
         V.build(4, 8, UNIT, 2, 3, 4)   # needs 2 M_B + (M_W - M_B) = 5
 
 
-@pytest.mark.parametrize("P", [2, 4, 8])
+@pytest.mark.parametrize("P", [2, 4])
 def test_memory_is_balanced_at_p_mb(P):
     """Every device peaks at the same level, P M_B of a whole stage (2P chunk
     stashes), where ZB-H2's first stage holds (2P-1) whole-stage M_B."""
@@ -90,10 +91,57 @@ def test_profiled_times_beat_zbh1_and_1f1b():
 
 
 @pytest.mark.parametrize("P,m", [(2, 4), (4, 8), (8, 24)])
-def test_equal_times_bubble_below_zbh1(P, m):
-    sim = V.simulate(P, V.build(P, m, UNIT, 1, 1, 2 * P), UNIT)
+def test_equal_times_list_candidate_below_zbh1(P, m):
+    sim = V.simulate(P, V.list_orders(P, m, UNIT, 1, 1, 2 * P), UNIT)
     h1 = S.simulate(S.stage_orders("zbh1", P, m), {"F": 2, "B": 2, "W": 2})
     assert 0 <= sim.bubble < h1.bubble
+
+
+def _zero_bubble_at_p_mb(P, m, t, m_b, m_w):
+    limit = 2 * P * m_b
+    orders = V.build(P, m, t, m_b, m_w, limit)
+    sim = _check(P, m, orders, t, m_b, m_w, limit)
+    assert sim.bubble == 0 and sim.makespan == sim.ideal
+    assert all(c == sim.ideal for c in sim.device_cost)
+    assert [V.peak_memory(o, m_b, m_w) for o in orders] == [limit] * P
+
+
+@pytest.mark.parametrize("P,m", [(2, 4), (2, 8), (3, 6), (4, 8), (4, 12), (5, 10), (6, 12)])
+@pytest.mark.parametrize("m_b,m_w", [(1, 1), (3, 2)])
+def test_equal_times_zero_bubble_within_p_mb(P, m, m_b, m_w):
+    """Section 6's result: at T_F = T_B = T_W the V order has no bubble (every
+    device busy from its first pass to its last) and every device peaks at
+    exactly P M_B of a whole stage, 2P chunk stashes; the same holds when a W
+    stash is smaller than a B stash (the pages' M_W < M_B)."""
+    for t in (UNIT, {"F": 5, "B": 5, "W": 5}):
+        _zero_bubble_at_p_mb(P, m, t, m_b, m_w)
+
+
+def test_equal_times_zero_bubble_eight_devices():
+    _zero_bubble_at_p_mb(8, 16, UNIT, 1, 1)
+
+
+@pytest.mark.parametrize("P,m", [(4, 32), (8, 24)])
+def test_search_scales_with_microbatches(P, m):
+    orders = V.search_order(P, m, 1, 1, 2 * P)
+    assert orders is not None
+    sim = _check(P, m, orders, UNIT, 1, 1, 2 * P)
+    assert sim.bubble == 0
+
+
+def test_search_gives_up_below_the_warm_up():
+    """With fewer than 2P - 1 microbatches a device cannot fill its warm-up with
+    forwards; the search reports no order and build keeps the list order."""
+    assert V.search_order(4, 6, 1, 1, 8) is None
+    assert V.search_order(4, 7, 1, 1, 8) is not None
+    orders = V.build(4, 6, UNIT, 1, 1, 8)
+    assert orders == V.list_orders(4, 6, UNIT, 1, 1, 8)
+    assert V.simulate(4, orders, UNIT).bubble > 0
+
+
+def test_unequal_times_keep_the_list_order():
+    t = {"F": 3, "B": 4, "W": 2}
+    assert V.build(4, 8, t, 1, 1, 8) == V.list_orders(4, 8, t, 1, 1, 8)
 
 
 def _zero_bubble_v_exists(P, m, cap):
@@ -170,7 +218,11 @@ def _zero_bubble_v_exists(P, m, cap):
 def test_zero_bubble_v_order_exists_within_p_mb():
     """The pages' claim at equal pass times, checked by exhaustive search on the
     smallest V (P = 2, m = 4): an order with no idle time inside any device's
-    span exists within 2P chunk stashes (P M_B).  The list-scheduled order of
-    oracle/vshape.py is one chunk pass above it there."""
+    span exists within 2P chunk stashes (P M_B), and none within one stash
+    less.  The built order reaches it; the list-scheduled candidate alone is
+    one chunk pass above it."""
     assert _zero_bubble_v_exists(2, 4, 4)
-    assert V.simulate(2, V.build(2, 4, UNIT, 1, 1, 4), UNIT).bubble == 1
+    assert not _zero_bubble_v_exists(2, 4, 3)
+    assert V.search_order(2, 4, 1, 1, 3) is None
+    assert V.simulate(2, V.build(2, 4, UNIT, 1, 1, 4), UNIT).bubble == 0
+    assert V.simulate(2, V.list_orders(2, 4, UNIT, 1, 1, 4), UNIT).bubble == 1
