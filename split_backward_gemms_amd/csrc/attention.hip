@@ -238,13 +238,11 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
   auto body = [&](char* sk, char* sv, int kb) {
     const int k0 = kb * 64;
     if (k0 <= q_wave_max) {
-      f32x16 s[2];
+      f32x16 s[2] = {zero16(), zero16()};
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        s[b] = zero16();
+      for (int kk = 0; kk < 8; ++kk)  // two independent chains, interleaved
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) s[b] = mfma(rf.get(sk, b, kk), qf[kk], s[b]);
-      }
+        for (int b = 0; b < 2; ++b) s[b] = mfma(rf.get(sk, b, kk), qf[kk], s[b]);
       if (k0 + 63 > q_wave_min || k0 + 64 > p.seq) {  // diagonal or last block: mask
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -435,23 +433,21 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
 // fetch 64 LSE2 values, lanes 16-31 the 64 D values (the rest read as zero).
 // Grid (heads x sequences, key blocks), heaviest first: key block 0 sees every
 // query block, and workgroups are handed out with x varying fastest.
-// Each key block is worked by a pair of waves on one SIMD: wave k (k < 4) computes S = Q K^T,
-// P and dV += P^T dO for key block k, wave k + 4 computes dP = dO V^T,
-// dS = P (dP - D) and dK += dS^T Q for the same keys, reading P from LDS
-// (fp32, in the register order both waves share).  Each wave holds half the
-// registers of one wave doing all four products, so two fit on a SIMD and
-// one's waits and LDS reads overlap the other's MFMAs: 16% shorter than one
-// wave per key block doing all four products (one wave per SIMD), with the
-// same products and summation order per key, so the same bits.
-constexpr int NTP = 512;  // 8 waves
-__global__ void __attribute__((amdgpu_flat_work_group_size(NTP, NTP), amdgpu_waves_per_eu(2, 2))) attn_bwd_dkdv_pair(AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) char sQ0[BLK];
-  __shared__ __attribute__((aligned(1024))) char sG0[BLK];
-  __shared__ __attribute__((aligned(1024))) char sQ1[BLK];
-  __shared__ __attribute__((aligned(1024))) char sG1[BLK];
-  __shared__ __attribute__((aligned(1024))) char sLD0[1024];
-  __shared__ __attribute__((aligned(1024))) char sLD1[1024];
-  __shared__ __attribute__((aligned(1024))) float sP[4 * 2 * 16 * 64];  // [key block][half][register][lane]
+//
+// Each key block is worked by a pair of waves on one SIMD, one query block
+// apart.  In step j wave k (k < 4) takes query block j: S = Q K^T, P, and
+// dV += P^T dO; it leaves P's four bf16 operand fragments in LDS.  Wave k + 4
+// takes query block j - 1: dP = dO V^T, dS = P (dP - D) with P read back from
+// those fragments, and dK += dS^T Q.  The two waves' instruction streams are
+// independent within a step, so one's exponentials and element-wise work run
+// under the other's MFMAs, and one barrier per step (which also retires the
+// ring's oldest block) is all the pair needs.  (Q, dO, LSE2/D) blocks go
+// through a three-block ring: j - 1 and j in use, j + 1 in flight.
+constexpr int NTP = 512;                  // 8 waves
+constexpr int RSLOT = 2 * BLK + 1024;     // Q block, dO block, LSE2 and D
+__global__ void __attribute__((amdgpu_flat_work_group_size(NTP, NTP), amdgpu_waves_per_eu(2, 2))) attn_bwd_dkdv_skew(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) char sRing[3 * RSLOT];
+  __shared__ __attribute__((aligned(1024))) char sPf[2 * 4 * 4 * 1024];  // [step parity][key block][fragment][lane] 16 B
   const int kb = (int)blockIdx.y;
   const int hd = blockIdx.x % p.heads, sq = blockIdx.x / p.heads;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, lc = lane & 31;
@@ -479,7 +475,6 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NTP, NTP), amdgpu_wav
   const dev::u32x4 rd = make_rsrc4(p.dsum + (int64_t)hd * p.T + base_row, (uint32_t)(p.seq * 4));
   const RowFrag rf(lane);
   const TrFrag tf(lane);
-  float* const myP = sP + kbw * 2 * 16 * 64 + lane;
 
   f32x16 acc[4];  // dV^T (role P) or dK^T (role dS) of the wave's keys
 #pragma unroll
@@ -488,104 +483,109 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NTP, NTP), amdgpu_wav
   const int qb0 = kb * 2;
   const int nqb = (p.seq + 63) / 64 - qb0;
 
-  auto fetch = [&](char* sq_, char* sg, char* sld, int j) {
+  auto slot = [&](int j) -> char* { return sRing + (j % 3) * RSLOT; };
+  auto pfrag = [&](int j, int f) -> char* { return sPf + (((j & 1) * 4 + kbw) * 4 + f) * 1024 + lane * 16; };
+  auto fetch = [&](int j) {
+    char* s = slot(j);
     const int q0 = (qb0 + j) * 64;
-    dmq.load(__builtin_amdgcn_readfirstlane(lds_addr(sq_)), base_row + q0, p.seq - q0);
-    dmg.load(__builtin_amdgcn_readfirstlane(lds_addr(sg)), base_row + q0, p.seq - q0);
+    dmq.load(__builtin_amdgcn_readfirstlane(lds_addr(s)), base_row + q0, p.seq - q0);
+    dmg.load(__builtin_amdgcn_readfirstlane(lds_addr(s + BLK)), base_row + q0, p.seq - q0);
     if (w == 0) {
-      const bool is_l = lane < 16;
       const int e = 4 * (lane & 15);
       const uint32_t off = lane < 32 && q0 + e < p.seq ? (uint32_t)((q0 + e) * 4) : kOOB;
-      if (is_l) dma16(rl, __builtin_amdgcn_readfirstlane(lds_addr(sld)), off);
-      else dma16(rd, __builtin_amdgcn_readfirstlane(lds_addr(sld)), off);
+      if (lane < 16) dma16(rl, __builtin_amdgcn_readfirstlane(lds_addr(s + 2 * BLK)), off);
+      else dma16(rd, __builtin_amdgcn_readfirstlane(lds_addr(s + 2 * BLK)), off);
     }
   };
-  fetch(sQ0, sG0, sLD0, 0);
-  if (nqb > 1) fetch(sQ1, sG1, sLD1, 1);
-  wait_vm_barrier<0>();
+  // some query of block j sees some key of the wave's block
+  auto active = [&](int j) { return (qb0 + j) * 64 + 63 >= kv_wave_min; };
 
-  auto body = [&](char* sq_, char* sg, const char* sld, int j) {
+  // Role P, query block j: S, P (masked), P's fragments to LDS, dV.
+  auto p_step = [&](int j) {
+    const char* s = slot(j);
     const int q0 = (qb0 + j) * 64;
-    const bool active = q0 + 63 >= kv_wave_min;  // some query of the block sees some key of the pair
-    const float* sL = reinterpret_cast<const float*>(sld);
-    const float* sD = reinterpret_cast<const float*>(sld + 256);
-    f32x16 x[2];  // S -> P (role P) or dP (role dS), per 32-query half
-    if (active) {
-      const char* rows = role_p ? sq_ : sg;
+    const float* sL = reinterpret_cast<const float*>(s + 2 * BLK);
+    f32x16 x[2] = {zero16(), zero16()};
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        x[b] = zero16();
+    for (int kk = 0; kk < 8; ++kk)  // the two halves are independent chains: interleave them
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) x[b] = mfma(rf.get(rows, b, kk), xf[kk], x[b]);
-      }
-      if (role_p) {
-        const bool masked = q0 < kv_wave_max || q0 + 64 > p.seq;
+      for (int b = 0; b < 2; ++b) x[b] = mfma(rf.get(s, b, kk), xf[kk], x[b]);  // S[q][kv]
+    const bool masked = q0 < kv_wave_max || q0 + 64 > p.seq;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int ql = 32 * b + 8 * g + 4 * h;
-            const f32x4 lv = *reinterpret_cast<const f32x4*>(sL + ql);
+      for (int g = 0; g < 4; ++g) {
+        const int ql = 32 * b + 8 * g + 4 * h;
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(sL + ql);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int qq = q0 + ql + t;
-              const int r = 4 * g + t;
-              float pr = exp2_hw(fmaf(x[b][r], c, -lv[t]));
-              if (masked && (kv > qq || qq >= p.seq)) pr = 0.0f;
-              x[b][r] = pr;
-              myP[(b * 16 + r) * 64] = pr;
-            }
-          }
-      }
-    }
-    __syncthreads();  // P of the block is in LDS
-    if (active) {
-      if (role_p) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            float pv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pv[e] = x[b][8 * st + e];
-            const bf16x8 pf = to_frag(pv);
-#pragma unroll
-            for (int d = 0; d < 4; ++d) acc[d] = mfma(tf.get(sg, d, 2 * b + st), pf, acc[d]);  // dV^T[d][kv]
-          }
-      } else {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int ql = 32 * b + 8 * g + 4 * h;
-            const f32x4 dv4 = *reinterpret_cast<const f32x4*>(sD + ql);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int r = 4 * g + t;
-              x[b][r] = myP[(b * 16 + r) * 64] * (x[b][r] - dv4[t]);  // dS
-            }
-          }
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            float sv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sv[e] = x[b][8 * st + e];
-            const bf16x8 sf = to_frag(sv);
-#pragma unroll
-            for (int d = 0; d < 4; ++d) acc[d] = mfma(tf.get(sq_, d, 2 * b + st), sf, acc[d]);  // dK^T[d][kv]
-          }
+        for (int t = 0; t < 4; ++t) {
+          const int qq = q0 + ql + t;
+          float pr = exp2_hw(fmaf(x[b][4 * g + t], c, -lv[t]));
+          if (masked && (kv > qq || qq >= p.seq)) pr = 0.0f;
+          x[b][4 * g + t] = pr;
         }
       }
-    }
-    wait_vm_barrier<0>();
-    if (j + 2 < nqb) fetch(sq_, sg, const_cast<char*>(sld), j + 2);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = x[b][8 * st + e];
+        const bf16x8 pf = to_frag(pv);
+        *reinterpret_cast<bf16x8*>(pfrag(j, 2 * b + st)) = pf;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) acc[d] = mfma(tf.get(s + BLK, d, 2 * b + st), pf, acc[d]);  // dV^T[d][kv]
+      }
   };
-  int j = 0;
-  for (; j + 1 < nqb; j += 2) {
-    body(sQ0, sG0, sLD0, j);
-    body(sQ1, sG1, sLD1, j + 1);
+
+  // Role dS, query block j: dP, dS from P's fragments, dK.
+  auto ds_step = [&](int j) {
+    const char* s = slot(j);
+    const float* sD = reinterpret_cast<const float*>(s + 2 * BLK + 256);
+    f32x16 x[2] = {zero16(), zero16()};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) x[b] = mfma(rf.get(s + BLK, b, kk), xf[kk], x[b]);  // dP[q][kv]
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const u32x4 pw = *reinterpret_cast<const u32x4*>(pfrag(j, 2 * b + st));
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(sD + 32 * b + 16 * st + 4 * h);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(sD + 32 * b + 16 * st + 8 + 4 * h);
+        float sv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pr = (e & 1) ? bf_hi(pw[e >> 1]) : bf_lo(pw[e >> 1]);
+          const float dv = e < 4 ? d0[e] : d1[e - 4];
+          sv[e] = pr * (x[b][8 * st + e] - dv);  // dS
+        }
+        const bf16x8 sf = to_frag(sv);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) acc[d] = mfma(tf.get(s, d, 2 * b + st), sf, acc[d]);  // dK^T[d][kv]
+      }
+  };
+
+  fetch(0);
+  if (nqb > 1) fetch(1);
+  wait_vm_barrier<0>();
+  // The roles run separate loops (wave-uniform branch) so that each keeps only
+  // its own values live; both meet the same barrier once per step.
+  if (role_p) {
+    for (int j = 0; j <= nqb; ++j) {
+      if (j < nqb && active(j)) p_step(j);
+      wait_vm_barrier<0>();  // block j+1 landed; P of block j visible; block j-1's slot free
+      if (j + 2 < nqb) fetch(j + 2);
+    }
+  } else {
+    for (int j = 0; j <= nqb; ++j) {
+      if (j >= 1 && active(j - 1)) ds_step(j - 1);
+      wait_vm_barrier<0>();
+      if (j + 2 < nqb) fetch(j + 2);
+    }
   }
-  if (j < nqb) body(sQ0, sG0, sLD0, j);
 
   const float sc = role_p ? 1.0f : p.scale;
   const int col = role_p ? 2 * p.h : p.h;
@@ -643,7 +643,7 @@ zb_status launch_attention_bwd(const AttnArgs& a, hipStream_t s) {
   }
   {
     ProfScope ps("attn_bwd_dkdv", alg * 4.0 / 7.0, 2.0 * p.T * 6.0 * p.h, s);
-    hipLaunchKernelGGL(attn_bwd_dkdv_pair, grid, dim3(NTP), 0, s, p);
+    hipLaunchKernelGGL(attn_bwd_dkdv_skew, grid, dim3(NTP), 0, s, p);
     ZB_HIP_CHECK(hipGetLastError());
   }
   return ZB_OK;

@@ -687,7 +687,6 @@ struct VPass { char kind; int chunk, mb; };
 bool zbv_search(int P, int m, int64_t m_b, int64_t m_w, int64_t m_limit,
                 std::vector<std::vector<VPass>>& orders) {
   const int C = 2 * P, h = P + 1;
-  auto dev = [P](int c) { return c < P ? c : 2 * P - 1 - c; };
   const std::vector<int> lst = zbv_latest_starts(P, m);
   auto L = [&](int k, int c, int j) { return lst[((size_t)k * C + c) * m + j]; };
   auto urgency = [&](int k, int c, int j) {
