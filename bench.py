@@ -55,23 +55,37 @@ def gpu_step_flops(w) -> float:
     return float(per_mb_stage) * w.n_micro * w.n_stages
 
 
-def pmc_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (FETCH_SIZE / WRITE_SIZE, calibrated against a plain copy), or None
-    when there is none or a kernel source changed since it was taken."""
+KERNEL_SOURCES = {
+    # the files that define each kernel family's device code
+    "gemm": ["split_backward_gemms_amd/csrc/gemm.hip", "split_backward_gemms_amd/csrc/device_common.h"],
+    "attn": ["split_backward_gemms_amd/csrc/attention.hip", "split_backward_gemms_amd/csrc/device_common.h"],
+    "other": ["split_backward_gemms_amd/csrc/elementwise.hip", "split_backward_gemms_amd/csrc/device_common.h"],
+}
+
+
+def sources_of(kernel: str):
+    return KERNEL_SOURCES["gemm" if kernel.startswith("gemm") else "attn" if kernel.startswith("attn") else "other"]
+
+
+def sources_sha16(srcs) -> str:
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"pmc_traffic_{workload}.json")
-    if not os.path.exists(path):
-        return None
-    d = json.load(open(path))
-    srcs = d["source"] if isinstance(d["source"], list) else [d["source"]]
     h = hashlib.sha256()
     for src in srcs:
         h.update(open(os.path.join(ROOT, src), "rb").read())
-    if h.hexdigest()[:16] != d["source_sha256_16"]:
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE / WRITE_SIZE, calibrated against a plain copy), or None
+    when there is none or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_traffic_{workload}.json")
+    if not os.path.exists(path):
         return None
-    k = d["kernels"].get(kernel)
-    return None if k is None else k["hbm_bytes_per_launch"]
+    k = json.load(open(path))["kernels"].get(kernel)
+    if k is None or k.get("source_sha256_16") != sources_sha16(k.get("source", [])):
+        return None
+    return k["hbm_bytes_per_launch"]
 
 
 def cpu_baseline(w, budget_s: float = 12.0) -> dict:

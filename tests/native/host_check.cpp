@@ -75,6 +75,9 @@ static void schedule_layer(std::mt19937& rng) {
           std::vector<zb_op> v(6 * (size_t)P * m);
           CHECK(zb_schedule_zbv(P, m, unit, 0, 10, 12, 2 * (int64_t)P * 10 + 2, v.data(), (int)v.size(), &n, &hs) ==
                 ZB_OK);
+          // equal stashes and 2P of them per device: the zero-bubble search runs and succeeds when m >= 2P - 1
+          CHECK(zb_schedule_zbv(P, m, unit, 0, 1, 1, 2 * (int64_t)P, v.data(), (int)v.size(), &n, &hs) == ZB_OK);
+          CHECK(m < 2 * P - 1 || P > 8 || hs.bubble == 0);
         }
         if (m % P == 0) {
           zb_sim_stats is;
