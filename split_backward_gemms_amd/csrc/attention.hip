@@ -384,12 +384,17 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
           s = mfma(rf.get(sk, b, kk), qf[kk], s);     // S^T[kv][q]
           dp = mfma(rf.get(sv, b, kk), dof[kk], dp);  // dP^T[kv][q]
         }
+        if (masked) {  // diagonal or last block (uniform branch: most blocks skip the index math)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kv = k0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-          float pr = exp2_hw(fmaf(s[r], c, -lse));
-          if (masked && (kv > q || kv >= p.seq)) pr = 0.0f;
-          s[r] = pr * (dp[r] - dsum);  // dS^T
+          for (int r = 0; r < 16; ++r) {
+            const int kv = k0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
+            float pr = exp2_hw(fmaf(s[r], c, -lse));
+            if (kv > q || kv >= p.seq) pr = 0.0f;
+            s[r] = pr * (dp[r] - dsum);  // dS^T
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = exp2_hw(fmaf(s[r], c, -lse)) * (dp[r] - dsum);
         }
         // dQ^T[d][q] += sum_kv K^T[d][kv] dS^T[kv][q]
 #pragma unroll
@@ -517,12 +522,17 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NTP, NTP), amdgpu_wav
       for (int g = 0; g < 4; ++g) {
         const int ql = 32 * b + 8 * g + 4 * h;
         const f32x4 lv = *reinterpret_cast<const f32x4*>(sL + ql);
+        if (masked) {  // uniform branch: only diagonal and last blocks pay for the index math
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int qq = q0 + ql + t;
-          float pr = exp2_hw(fmaf(x[b][4 * g + t], c, -lv[t]));
-          if (masked && (kv > qq || qq >= p.seq)) pr = 0.0f;
-          x[b][4 * g + t] = pr;
+          for (int t = 0; t < 4; ++t) {
+            const int qq = q0 + ql + t;
+            float pr = exp2_hw(fmaf(x[b][4 * g + t], c, -lv[t]));
+            if (kv > qq || qq >= p.seq) pr = 0.0f;
+            x[b][4 * g + t] = pr;
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) x[b][4 * g + t] = exp2_hw(fmaf(x[b][4 * g + t], c, -lv[t]));
         }
       }
 #pragma unroll
