@@ -106,6 +106,14 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // ---- LDS blocks ------------------------------------------------------------
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
+// A buffer descriptor the copies can take from scalar registers: the value is
+// the same in every lane, but after inlining into divergent-looking control
+// flow the compiler may hold it in vector registers.
+__device__ __forceinline__ dev::u32x4 uniform4(const dev::u32x4& v) {
+  return {(uint32_t)__builtin_amdgcn_readfirstlane((int)v[0]), (uint32_t)__builtin_amdgcn_readfirstlane((int)v[1]),
+          (uint32_t)__builtin_amdgcn_readfirstlane((int)v[2]), (uint32_t)__builtin_amdgcn_readfirstlane((int)v[3])};
+}
+
 // Copies of one block: rows row0 .. row0+63 (those at or past `valid` read as
 // zero), columns col0 .. col0+127 of a row-major bf16 matrix with leading
 // dimension ld.  The NW waves of the workgroup each issue 16 / NW copies;
@@ -135,9 +143,10 @@ struct BlockDma {
   }
   __device__ __forceinline__ void load(uint32_t dst, int64_t first_row, int valid) const {
     const uint32_t step = (uint32_t)(first_row * rowstep);
+    const dev::u32x4 r = uniform4(rsrc);
 #pragma unroll
     for (int q = 0; q < NI; ++q)
-      dma16(rsrc, dst + lds0 + q * 1024, row0 + 4 * q < valid ? boff[q] + step : kOOB);
+      dma16(r, dst + lds0 + q * 1024, row0 + 4 * q < valid ? boff[q] + step : kOOB);
   }
 };
 
@@ -449,9 +458,12 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
 // ring's oldest block) is all the pair needs.  (Q, dO, LSE2/D) blocks go
 // through a three-block ring: j - 1 and j in use, j + 1 in flight.
 constexpr int NTP = 512;                  // 8 waves
-constexpr int RSLOT = 2 * BLK + 1024;     // Q block, dO block, LSE2 and D
 __global__ void __attribute__((amdgpu_flat_work_group_size(NTP, NTP), amdgpu_waves_per_eu(2, 2))) attn_bwd_dkdv_skew(AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) char sRing[3 * RSLOT];
+  // Three-block rings of Q, dO and (LSE2, D); the step loop is unrolled six
+  // ways so that every ring slot and P buffer is a compile-time offset.
+  __shared__ __attribute__((aligned(1024))) char sQr[3 * BLK];
+  __shared__ __attribute__((aligned(1024))) char sGr[3 * BLK];
+  __shared__ __attribute__((aligned(1024))) char sLDr[3 * 1024];
   __shared__ __attribute__((aligned(1024))) char sPf[2 * 4 * 4 * 1024];  // [step parity][key block][fragment][lane] 16 B
   const int kb = (int)blockIdx.y;
   const int hd = blockIdx.x % p.heads, sq = blockIdx.x / p.heads;
@@ -488,28 +500,31 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NTP, NTP), amdgpu_wav
   const int qb0 = kb * 2;
   const int nqb = (p.seq + 63) / 64 - qb0;
 
-  auto slot = [&](int j) -> char* { return sRing + (j % 3) * RSLOT; };
-  auto pfrag = [&](int j, int f) -> char* { return sPf + (((j & 1) * 4 + kbw) * 4 + f) * 1024 + lane * 16; };
-  auto fetch = [&](int j) {
-    char* s = slot(j);
+  auto pfrag = [&](auto pb, int f) -> char* {
+    return sPf + (((decltype(pb)::value) * 4 + kbw) * 4 + f) * 1024 + lane * 16;
+  };
+  auto fetch = [&](auto sl, int j) {
+    constexpr int S = decltype(sl)::value;
     const int q0 = (qb0 + j) * 64;
-    dmq.load(__builtin_amdgcn_readfirstlane(lds_addr(s)), base_row + q0, p.seq - q0);
-    dmg.load(__builtin_amdgcn_readfirstlane(lds_addr(s + BLK)), base_row + q0, p.seq - q0);
+    dmq.load(__builtin_amdgcn_readfirstlane(lds_addr(sQr + S * BLK)), base_row + q0, p.seq - q0);
+    dmg.load(__builtin_amdgcn_readfirstlane(lds_addr(sGr + S * BLK)), base_row + q0, p.seq - q0);
     if (w == 0) {
       const int e = 4 * (lane & 15);
       const uint32_t off = lane < 32 && q0 + e < p.seq ? (uint32_t)((q0 + e) * 4) : kOOB;
-      if (lane < 16) dma16(rl, __builtin_amdgcn_readfirstlane(lds_addr(s + 2 * BLK)), off);
-      else dma16(rd, __builtin_amdgcn_readfirstlane(lds_addr(s + 2 * BLK)), off);
+      if (lane < 16) dma16(uniform4(rl), __builtin_amdgcn_readfirstlane(lds_addr(sLDr + S * 1024)), off);
+      else dma16(uniform4(rd), __builtin_amdgcn_readfirstlane(lds_addr(sLDr + S * 1024)), off);
     }
   };
   // some query of block j sees some key of the wave's block
   auto active = [&](int j) { return (qb0 + j) * 64 + 63 >= kv_wave_min; };
 
   // Role P, query block j: S, P (masked), P's fragments to LDS, dV.
-  auto p_step = [&](int j) {
-    const char* s = slot(j);
+  auto p_step = [&](auto sl, auto pb, int j) {
+    constexpr int S = decltype(sl)::value;
+    const char* s = sQr + S * BLK;
+    const char* sg = sGr + S * BLK;
     const int q0 = (qb0 + j) * 64;
-    const float* sL = reinterpret_cast<const float*>(s + 2 * BLK);
+    const float* sL = reinterpret_cast<const float*>(sLDr + S * 1024);
     f32x16 x[2] = {zero16(), zero16()};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)  // the two halves are independent chains: interleave them
@@ -543,26 +558,28 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NTP, NTP), amdgpu_wav
 #pragma unroll
         for (int e = 0; e < 8; ++e) pv[e] = x[b][8 * st + e];
         const bf16x8 pf = to_frag(pv);
-        *reinterpret_cast<bf16x8*>(pfrag(j, 2 * b + st)) = pf;
+        *reinterpret_cast<bf16x8*>(pfrag(pb, 2 * b + st)) = pf;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) acc[d] = mfma(tf.get(s + BLK, d, 2 * b + st), pf, acc[d]);  // dV^T[d][kv]
+        for (int d = 0; d < 4; ++d) acc[d] = mfma(tf.get(sg, d, 2 * b + st), pf, acc[d]);  // dV^T[d][kv]
       }
   };
 
   // Role dS, query block j: dP, dS from P's fragments, dK.
-  auto ds_step = [&](int j) {
-    const char* s = slot(j);
-    const float* sD = reinterpret_cast<const float*>(s + 2 * BLK + 256);
+  auto ds_step = [&](auto sl, auto pb) {
+    constexpr int S = decltype(sl)::value;
+    const char* s = sQr + S * BLK;
+    const char* sg = sGr + S * BLK;
+    const float* sD = reinterpret_cast<const float*>(sLDr + S * 1024 + 256);
     f32x16 x[2] = {zero16(), zero16()};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) x[b] = mfma(rf.get(s + BLK, b, kk), xf[kk], x[b]);  // dP[q][kv]
+      for (int b = 0; b < 2; ++b) x[b] = mfma(rf.get(sg, b, kk), xf[kk], x[b]);  // dP[q][kv]
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const u32x4 pw = *reinterpret_cast<const u32x4*>(pfrag(j, 2 * b + st));
+        const u32x4 pw = *reinterpret_cast<const u32x4*>(pfrag(pb, 2 * b + st));
         const f32x4 d0 = *reinterpret_cast<const f32x4*>(sD + 32 * b + 16 * st + 4 * h);
         const f32x4 d1 = *reinterpret_cast<const f32x4*>(sD + 32 * b + 16 * st + 8 + 4 * h);
         float sv[8];
@@ -578,24 +595,43 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NTP, NTP), amdgpu_wav
       }
   };
 
-  fetch(0);
-  if (nqb > 1) fetch(1);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  fetch(I0{}, 0);
+  if (nqb > 1) fetch(I1{}, 1);
   wait_vm_barrier<0>();
+  // Step j (j % 6 == R): role P takes block j (slot j % 3, P buffer j % 2), role
+  // dS block j - 1; then block j+1 has landed, P of block j is visible and
+  // block j-1's slot, (j + 2) % 3, takes block j + 2.
+  auto step = [&](auto r, int j) {
+    constexpr int R = decltype(r)::value;
+    using SP = std::integral_constant<int, R % 3>;
+    using PP = std::integral_constant<int, R % 2>;
+    using SD = std::integral_constant<int, (R + 2) % 3>;
+    using PD = std::integral_constant<int, (R + 1) % 2>;
+    if (role_p) {
+      if (j < nqb && active(j)) p_step(SP{}, PP{}, j);
+    } else {
+      if (j >= 1 && active(j - 1)) ds_step(SD{}, PD{});
+    }
+    wait_vm_barrier<0>();
+    if (j + 2 < nqb) fetch(SD{}, j + 2);
+  };
   // The roles run separate loops (wave-uniform branch) so that each keeps only
-  // its own values live; both meet the same barrier once per step.
-  if (role_p) {
-    for (int j = 0; j <= nqb; ++j) {
-      if (j < nqb && active(j)) p_step(j);
-      wait_vm_barrier<0>();  // block j+1 landed; P of block j visible; block j-1's slot free
-      if (j + 2 < nqb) fetch(j + 2);
+  // its own values live; both meet the same barriers, one per step.
+  auto run = [&]() __attribute__((always_inline)) {
+    for (int j = 0; j <= nqb; j += 6) {
+      step(I0{}, j);
+      if (j + 1 <= nqb) step(I1{}, j + 1);
+      if (j + 2 <= nqb) step(I2{}, j + 2);
+      if (j + 3 <= nqb) step(std::integral_constant<int, 3>{}, j + 3);
+      if (j + 4 <= nqb) step(std::integral_constant<int, 4>{}, j + 4);
+      if (j + 5 <= nqb) step(std::integral_constant<int, 5>{}, j + 5);
     }
-  } else {
-    for (int j = 0; j <= nqb; ++j) {
-      if (j >= 1 && active(j - 1)) ds_step(j - 1);
-      wait_vm_barrier<0>();
-      if (j + 2 < nqb) fetch(j + 2);
-    }
-  }
+  };
+  if (role_p) run();
+  else run();
 
   const float sc = role_p ? 1.0f : p.scale;
   const int col = role_p ? 2 * p.h : p.h;
