@@ -438,6 +438,31 @@ def test_zbv_order_matches_oracle_and_1f1b_bits(name):
     assert max(errs) <= TOL
 
 
+def test_zbv_searched_order_four_devices_matches_1f1b_bits():
+    """The searched zero-bubble V order on four devices (8 chunk stages, m = 8) runs through the
+    executor and gives the same bits as 1F1B over the chunk stages."""
+    base = si.reduced(si.WORKLOADS["gpt_full_h4096"], hidden=256, heads=2, seq=96, n_micro=8, n_stages=4,
+                      n_layers=2)
+    w = si.v_chunks(base)
+    assert w.n_stages == 8
+    print(f"zb-v searched: {w.n_stages} chunk stages x {w.n_layers} layers, m = {w.n_micro}", flush=True)
+    ws, xs, dys = _inputs(w)
+    pipe = EmulatedPipeline(w, ws, ops=None, recompute_act=0)
+    _, y0, dx0, dw0, _ = _run(w, ws, xs, dys, "1f1b", pipe)
+    m_b, m_w = stash_per_microbatch(pipe.handles)
+    ops, st = zb.zb_schedule_zbv(4, w.n_micro, (1, 1, 1), m_b, m_w, 8 * max(m_b, m_w))
+    assert st["bubble"] == 0
+    assert zb.zb_schedule_validate(w.n_stages, w.n_micro, ops) == (zb.ZB_OK, -1)
+    _, y, dx, dw, _ = _run(w, ws, xs, dys, ops, pipe)
+    pipe.close()
+    for j in range(w.n_micro):
+        assert np.array_equal(y[j], y0[j]) and np.array_equal(dx[j], dx0[j]), j
+    for s_ in range(w.n_stages):
+        for l in range(w.n_layers):
+            for nm in dw[s_][l]:
+                assert np.array_equal(dw[s_][l][nm].view(np.uint32), dw0[s_][l][nm].view(np.uint32)), (s_, l, nm)
+
+
 def test_single_stage_api_order_errors():
     w = REDUCED["tiny_bf16"]
     ws, xs, dys = _inputs(w)
