@@ -60,6 +60,9 @@ constexpr int HD = 128;           // head dim
 constexpr int NT = 256;           // 4 waves
 constexpr int BLK = 64 * 256;     // one 64 x 128 bf16 block in LDS
 constexpr float kLog2e = 1.4426950408889634f;
+// Forward: exponentials may reach 2^8 before the running maximum is moved
+// (the fp32 sums and the bf16 operands of P V keep their relative precision).
+constexpr float kRescaleSlack = 8.0f;
 
 struct AttnParams {
   const uint16_t* qkv;  // [T, 3h]
@@ -267,10 +270,16 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
 #pragma unroll
         for (int r = 0; r < 16; ++r) mb = fmaxf(mb, s[b][r]);
       mb = fmaxf(mb, __shfl_xor(mb, 32));
-      const float mn = fmaxf(m, mb * c);  // block 0 always has key 0 <= q, so mn is finite
-      const float alpha = exp2_hw(m - mn);
-      m = mn;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+      // The running maximum m (base 2) moves only when a row's block maximum
+      // exceeds it by more than kRescaleSlack; until then the exponentials of
+      // later blocks stay below 2^kRescaleSlack and the sums need no rescale.
+      // Block 0 always has key 0 <= q, so the first maximum is finite.
+      const float mc = mb * c;
+      const bool grow = mc > m + kRescaleSlack;  // always true on the first block (m = -inf)
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float mn = grow ? mc : m;
+        const float alpha = exp2_hw(m - mn);
+        m = mn;
         l *= alpha;
 #pragma unroll
         for (int d = 0; d < 4; ++d)
@@ -281,7 +290,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = exp2_hw(fmaf(s[b][r], c, -mn));
+          const float e = exp2_hw(fmaf(s[b][r], c, -m));
           s[b][r] = e;
           l += e;
         }
