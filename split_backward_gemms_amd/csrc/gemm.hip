@@ -270,7 +270,8 @@ struct Ring {
 
 template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC, int BK, int WV>
 __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, char* s0, char* s1, char* s2,
-                                          char* s3);
+                                          char* s3, bool pre, bool has_next, const Params& np, int ntile,
+                                          int nsplit);
 
 // The ring stages are separate LDS objects (so the code that addresses each
 // one is fixed at compile time).
@@ -285,11 +286,18 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(64 * WV, 64 * WV), am
 gemm_bf16_mfma(Params p) {
   ZB_GEMM_LDS(BM, BN, 1, BKT);
   const int total = p.nbm * p.nbn * p.splits;
-  for (int b0 = blockIdx.x; b0 < total; b0 += gridDim.x) {  // persistent when the grid is smaller
-    if (b0 != (int)blockIdx.x) __syncthreads();
-    int b = b0;
-    if (p.xcd_remap) b = xcd_remap(b, total);  // a tile's splits share an XCD
-    gemm_tile<BM, BN, AK, BKC, EPI, 1, BKT, WV>(p, b / p.splits, b % p.splits, s0, s1, s2, s3);
+  // Persistent when the grid is smaller: a tile's epilogue runs after the
+  // first copies of the workgroup's next tile are issued.
+  for (int b0 = blockIdx.x; b0 < total; b0 += gridDim.x) {
+    const int nb0 = b0 + gridDim.x;
+    int b = b0, nb = nb0 < total ? nb0 : b0;
+    if (p.xcd_remap) {  // a tile's splits share an XCD
+      b = xcd_remap(b, total);
+      nb = xcd_remap(nb, total);
+    }
+    gemm_tile<BM, BN, AK, BKC, EPI, 1, BKT, WV>(p, b / p.splits, b % p.splits, s0, s1, s2, s3,
+                                                 b0 != (int)blockIdx.x, nb0 < total, p, nb / p.splits,
+                                                 nb % p.splits);
   }
 }
 
@@ -300,16 +308,23 @@ gemm_bf16_mfma_group(GroupParams gp) {
   ZB_GEMM_LDS(BM, BN, OCC, BK);
   const int total = gp.tile_start[gp.n];
   // Persistent when the grid is smaller than the tile count: workgroup w takes
-  // tiles w, w + grid, ...; the barrier keeps the next tile's copies out of the
-  // ring until every wave is past the last one.  The grid is a multiple of the
-  // XCD count, so a workgroup's tiles stay on its XCD.
-  for (int b0 = blockIdx.x; b0 < total; b0 += gridDim.x) {
-    if (b0 != (int)blockIdx.x) __syncthreads();
+  // tiles w, w + grid, ..., and a tile's epilogue runs after the next tile's
+  // first copies are issued.  The grid is a multiple of the XCD count, so a
+  // workgroup's tiles stay on its XCD.
+  auto locate = [&](int b0, int& g) {
     int b = b0;
     if (total % XCDS == 0) b = (b % XCDS) * (total / XCDS) + b / XCDS;  // one XCD works a GEMM's neighbours
-    int g = 0;
+    g = 0;
     while (g + 1 < gp.n && b >= gp.tile_start[g + 1]) ++g;
-    gemm_tile<BM, BN, AK, BKC, EPI, OCC, BK, WV>(gp.p[g], b - gp.tile_start[g], 0, s0, s1, s2, s3);
+    return b - gp.tile_start[g];
+  };
+  for (int b0 = blockIdx.x; b0 < total; b0 += gridDim.x) {
+    const int nb0 = b0 + gridDim.x;
+    int g, ng;
+    const int tile = locate(b0, g);
+    const int ntile = locate(nb0 < total ? nb0 : b0, ng);
+    gemm_tile<BM, BN, AK, BKC, EPI, OCC, BK, WV>(gp.p[g], tile, 0, s0, s1, s2, s3, b0 != (int)blockIdx.x,
+                                                  nb0 < total, gp.p[ng], ntile, 0);
   }
 }
 
@@ -327,9 +342,45 @@ __device__ __forceinline__ bf16x8 frag_t(const char* tile, uint32_t off) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Copies of the first min(NS, nk) k tiles of one output tile (split `split`
+// of tile `tile`) into ring stages 0, 1, ..., A then B for each stage: the
+// same copies, in the same order, as the k loop's own start.
+template <int BM, int BN, bool AK, bool BKC, int OCC, int BK, int WV>
+__device__ __forceinline__ void tile_prologue(const Params& p, int tile, int split, char* s0, char* s1, char* s2,
+                                              char* s3) {
+  constexpr int NS = Ring<BM, BN, OCC, BK>::NS;
+  constexpr int AT = BM * BK * 2;
+  char* const bufs[4] = {s0, s1, s2, s3};
+  int tm, tn;
+  tile_raster(p, tm, tn, tile);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  DmaLoader<BM, AK, BK, WV> la(static_cast<const uint16_t*>(p.A), p.lda, tm * BM, p.M, p.K, wave, lane);
+  DmaLoader<BN, BKC, BK, WV> lb(static_cast<const uint16_t*>(p.B), p.ldb, tn * BN, p.N, p.K, wave, lane);
+  const int nk_all = (p.K + BK - 1) / BK;
+  const int kt0 = split * p.kts;
+  const int nk = min(nk_all - kt0, p.kts);
+  const bool k_ragged = (p.K % BK) != 0;
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    if (st < nk) {
+      const uint32_t b = __builtin_amdgcn_readfirstlane(lds_addr(bufs[st]));
+      const int k0 = (kt0 + st) * BK;
+      if (k_ragged && kt0 + st == nk_all - 1) {
+        la.template load<true>(b, k0, p.K);
+        lb.template load<true>(b + AT, k0, p.K);
+      } else {
+        la.template load<false>(b, k0, p.K);
+        lb.template load<false>(b + AT, k0, p.K);
+      }
+    }
+  }
+}
+
 template <int BM, int BN, bool AK, bool BKC, int EPI, int OCC, int BK, int WV>
 __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, char* s0, char* s1, char* s2,
-                                          char* s3) {
+                                          char* s3, bool pre, bool has_next, const Params& np, int ntile,
+                                          int nsplit) {
   constexpr int WTM = BM / 2, WTN = BN / (WV / 2);  // waves in a 2 x (WV / 2) grid
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int NS = Ring<BM, BN, OCC, BK>::NS;
@@ -364,6 +415,11 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
   DmaLoader<BM, AK, BK, WV> la(static_cast<const uint16_t*>(p.A), p.lda, m0, p.M, p.K, wave, lane);
   DmaLoader<BN, BKC, BK, WV> lb(static_cast<const uint16_t*>(p.B), p.ldb, n0, p.N, p.K, wave, lane);
   constexpr int NI = DmaLoader<BM, AK, BK, WV>::NI + DmaLoader<BN, BKC, BK, WV>::NI;  // copies per wave per tile
+  // 16-byte stores one wave's epilogue issues on every path.  With `pre` the
+  // previous tile's epilogue (same kind) ran after this tile's first copies
+  // were issued; loads and stores complete in issue order, so those copies are
+  // done once no more than this many newer operations are outstanding.
+  constexpr int EPN = (EPI == EPI_ACC || EPI == EPI_PART || EPI == EPI_GELU) ? TM * TN * 4 : TM * TN * 2;
   // This workgroup's k tiles: [kt0, kt0 + nk) of the product's ceil(K / BK).
   const int nk_all = (p.K + BK - 1) / BK;
   const int kt0 = split * p.kts;
@@ -449,13 +505,19 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
 
   // Ring: tiles t+1 .. t+NS-1 are in flight while tile t feeds the MFMAs;
   // tile t+NS goes into tile t's stage once every wave has read it.
-  if (0 < nk) dma(std::integral_constant<int, 0>{}, 0);  // K == 0: no copies (none would be waited for)
-  if (NS > 1 && 1 < nk) dma(std::integral_constant<int, 1>{}, 1);
-  if (NS > 2 && 2 < nk) dma(std::integral_constant<int, (NS > 2 ? 2 : 0)>{}, 2);
-  if (NS > 3 && 3 < nk) dma(std::integral_constant<int, (NS > 3 ? 3 : 0)>{}, 3);
+  if (!pre) {  // else issued before the previous tile's epilogue
+    if (0 < nk) dma(std::integral_constant<int, 0>{}, 0);  // K == 0: no copies (none would be waited for)
+    if (NS > 1 && 1 < nk) dma(std::integral_constant<int, 1>{}, 1);
+    if (NS > 2 && 2 < nk) dma(std::integral_constant<int, (NS > 2 ? 2 : 0)>{}, 2);
+    if (NS > 3 && 3 < nk) dma(std::integral_constant<int, (NS > 3 ? 3 : 0)>{}, 3);
+  }
   if (nk > 0) {  // K == 0: empty sum
-    if (nk >= NS) wait_vm_barrier<(NS - 1) * NI>();
-    else wait_vm_barrier<0>();
+    if (nk >= NS) {
+      if (pre) wait_vm_barrier<(NS - 1) * NI + EPN>();
+      else wait_vm_barrier<(NS - 1) * NI>();
+    } else {
+      wait_vm_barrier<0>();
+    }
     read_frags(bufs[0], 0, 0);
   }
 
@@ -476,8 +538,13 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
       mfmas(kk & 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (t + NS - 1 < nk) wait_vm_barrier<(NS - 2) * NI>();
-    else wait_vm_barrier<0>();
+    if (t + NS - 1 < nk) {
+      // Tiles t + 1 .. NS - 1 came from the start before the previous epilogue.
+      if (pre && t < NS - 1) wait_vm_barrier<(NS - 2) * NI + EPN>();
+      else wait_vm_barrier<(NS - 2) * NI>();
+    } else {
+      wait_vm_barrier<0>();
+    }
     const bool refill = t + NS < nk;
     read_a(bufs[NXT], 0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -515,6 +582,13 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
     if (t + 2 < nk) body(B2{}, t + 2);
   }
 
+  // Every wave is past its last read of the ring (and no copy is in flight):
+  // the next tile's first copies go out before this tile's epilogue.
+  if (has_next) {
+    wait_vm_barrier<0>();
+    tile_prologue<BM, BN, AK, BKC, OCC, BK, WV>(np, ntile, nsplit, s0, s1, s2, s3);
+  }
+
   // Epilogue: lane (i, j, g) owns C[em + 32 i][en + 32 j + 8 g + 0..3].
   if constexpr (EPI == EPI_PART) {
     // This split's fp32 partial sum, to its own M x N slice.
@@ -534,13 +608,12 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), prsrc, (int)off, 0, 0);
         }
   } else if constexpr (EPI == EPI_ACC) {
-    // dW (+)= this GEMM's sum over k, in fp32.  The old values of one row of
-    // 32x32 blocks (TN * 4 16-byte loads per lane) are all requested before the
-    // first add, so the loads overlap instead of each waiting out its latency.
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      uint32_t off[TN][4];
-      f32x4 c[TN][4];
+    // dW (+)= this GEMM's sum over k, in fp32.  Rows of 32x32 blocks go
+    // through a two-deep pipeline: the old values of row i + 1 (TN * 4
+    // 16-byte loads per lane) are requested before row i is added and
+    // stored, so one row's loads are in flight while the previous one is
+    // written.
+    auto offsets = [&](int i, uint32_t (&off)[TN][4]) {
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -548,13 +621,15 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
           const int m = em + i * 32, n = en + j * 32 + 8 * g;
           off[j][g] = (m < p.M && n < p.N) ? (uint32_t)(((int64_t)m * p.ldc + n) * 4) : kOOB;
         }
-      if (p.beta) {
+    };
+    auto load_row = [&](const uint32_t (&off)[TN][4], f32x4 (&c)[TN][4]) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-            c[j][g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(crsrc, (int)off[j][g], 0, 0));
-      }
+        for (int g = 0; g < 4; ++g)
+          c[j][g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(crsrc, (int)off[j][g], 0, 0));
+    };
+    auto store_row = [&](int i, const uint32_t (&off)[TN][4], const f32x4 (*c)[4]) {
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -562,12 +637,35 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
           f32x4 v;
 #pragma unroll
           for (int t2 = 0; t2 < 4; ++t2) v[t2] = acc[i][j][4 * g + t2];
-          if (p.beta) {
+          if (c) {
 #pragma unroll
             for (int t2 = 0; t2 < 4; ++t2) v[t2] = c[j][g][t2] + v[t2];
           }
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), crsrc, (int)off[j][g], 0, 0);
         }
+    };
+    if (p.beta) {
+      uint32_t off[2][TN][4];
+      f32x4 c[2][TN][4];
+      offsets(0, off[0]);
+      load_row(off[0], c[0]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if (i + 1 < TM) {
+          offsets(i + 1, off[(i + 1) & 1]);
+          load_row(off[(i + 1) & 1], c[(i + 1) & 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        store_row(i, off[i & 1], c[i & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        uint32_t off[TN][4];
+        offsets(i, off);
+        store_row(i, off, nullptr);
+      }
     }
   } else {
     __amdgpu_buffer_rsrc_t rrsrc = make_rsrc(EPI == EPI_RESID || EPI == EPI_DGELU ? p.R : p.C,
