@@ -49,6 +49,12 @@ INT_SHAPES = [
     (4096, 4096, 256),     # B picks 256x256 tiles
     (4096, 256, 4096),     # F picks 256x256 tiles
     (8, 8, 8),             # smallest legal shape
+    # More output tiles than CUs, so workgroups loop over tiles, with
+    # contractions shorter than the LDS ring (and ragged): the next tile's
+    # first copies go out before the current tile's epilogue.
+    (8192, 72, 4096),      # F: 512 tiles, two 64-deep k tiles, the second ragged
+    (8192, 4096, 40),      # B: 512 tiles, one ragged k tile
+    (40, 4096, 8192),      # W: 512 tiles, two 32-deep k tiles, the second ragged
 ]
 
 
