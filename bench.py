@@ -195,7 +195,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=12)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt_full_s4096")
     ap.add_argument("--order", default=None)
     ap.add_argument("--streams", type=int, default=2,
@@ -262,14 +262,24 @@ def main() -> int:
     flops = gpu_step_flops(w)
     torch.cuda.synchronize()
 
+    step_ev_ms = []
+
     def timed(pipe, o, steps, warmup):
+        # Wall time over `steps` back-to-back steps, synchronised only at both
+        # ends.  Each step also closes with a hipEvent on the caller's stream,
+        # which every stage stream joins at the end of a step: per-step times
+        # for the median and minimum, without a host wait between steps.
         for _ in range(warmup):
             pipe.run(o, X, DY, y, dx)
         torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         t = time.perf_counter()
-        for _ in range(steps):
+        ev[0].record()
+        for i in range(steps):
             pipe.run(o, X, DY, y, dx)
+            ev[i + 1].record()
         torch.cuda.synchronize()
+        step_ev_ms[:] = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
         return 1000.0 * (time.perf_counter() - t) / max(1, steps)
 
     def traced(pipe, o):
@@ -322,6 +332,9 @@ def main() -> int:
     if a.mode == "full":
         ms_per_step = timed(pipe, ops, a.steps, a.warmup)
         tflops = flops / (ms_per_step / 1000.0) / 1e12
+        ev_steps = sorted(step_ev_ms)
+        out_extra["step_ms_median"] = ev_steps[len(ev_steps) // 2] if ev_steps else None
+        out_extra["step_ms_min"] = ev_steps[0] if ev_steps else None
         log(f"{order}, {min(a.streams, P)} streams: {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s")
         short = ms_per_step < SHORT_STEP_MS
         tr_multi, _ = traced(pipe, ops)

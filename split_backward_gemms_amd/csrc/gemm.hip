@@ -498,19 +498,12 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
       else lb.template load<false>(b + AT, k0, p.K);
     }
   };
-  auto dma = [&](auto bi, int t) {
-    dma_op(bi, 0, t);
-    dma_op(bi, 1, t);
-  };
 
   // Ring: tiles t+1 .. t+NS-1 are in flight while tile t feeds the MFMAs;
-  // tile t+NS goes into tile t's stage once every wave has read it.
-  if (!pre) {  // else issued before the previous tile's epilogue
-    if (0 < nk) dma(std::integral_constant<int, 0>{}, 0);  // K == 0: no copies (none would be waited for)
-    if (NS > 1 && 1 < nk) dma(std::integral_constant<int, 1>{}, 1);
-    if (NS > 2 && 2 < nk) dma(std::integral_constant<int, (NS > 2 ? 2 : 0)>{}, 2);
-    if (NS > 3 && 3 < nk) dma(std::integral_constant<int, (NS > 3 ? 3 : 0)>{}, 3);
-  }
+  // tile t+NS goes into tile t's stage once every wave has read it.  The
+  // first NS tiles' copies (none when K == 0) come from tile_prologue: here,
+  // or before the previous tile's epilogue when `pre`.
+  if (!pre) tile_prologue<BM, BN, AK, BKC, OCC, BK, WV>(p, tile, split, s0, s1, s2, s3);
   if (nk > 0) {  // K == 0: empty sum
     if (nk >= NS) {
       if (pre) wait_vm_barrier<(NS - 1) * NI + EPN>();
