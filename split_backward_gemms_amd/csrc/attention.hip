@@ -106,6 +106,15 @@ __device__ __forceinline__ f32x16 zero16() {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt vmcnt(0) as an instruction the compiler tracks (gfx9 encoding:
+// expcnt 7 and lgkmcnt 15 mean no wait on those).  The block copies and the
+// ring's waits are inline assembly, which the compiler's wait insertion does
+// not see; without this, operands loaded into registers before a block loop
+// stay pending in its model, and it waits for them again inside the loop, where
+// the hardware counter also holds the next block's copies, so every block would
+// wait out its own prefetch.
+__device__ __forceinline__ void wait_vm_known() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---- LDS blocks ------------------------------------------------------------
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
@@ -241,6 +250,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
     dv.load(__builtin_amdgcn_readfirstlane(lds_addr(sv)), base_row + k0, p.seq - k0);
   };
   fetch(sK0, sV0, 0);
+  wait_vm_known();  // the register loads above, and block 0, which is needed first anyway
   if (nkb > 1) fetch(sK1, sV1, 1);
   if (nkb > 1) wait_vm_barrier<2 * BlockDma<4>::NI>();
   else wait_vm_barrier<0>();
@@ -386,6 +396,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
     dv.load(__builtin_amdgcn_readfirstlane(lds_addr(sv)), base_row + k0, p.seq - k0);
   };
   fetch(sK0, sV0, 0);
+  wait_vm_known();  // the register loads above, and block 0, which is needed first anyway
   if (nkb > 1) fetch(sK1, sV1, 1);
   if (nkb > 1) wait_vm_barrier<2 * BlockDma<4>::NI>();
   else wait_vm_barrier<0>();
@@ -610,6 +621,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NTP, NTP), amdgpu_wav
   fetch(I0{}, 0);
   if (nqb > 1) fetch(I1{}, 1);
   wait_vm_barrier<0>();
+  wait_vm_known();  // nothing is in flight here; the compiler learns that the K / V rows have landed
   // Step j (j % 6 == R): role P takes block j (slot j % 3, P buffer j % 2), role
   // dS block j - 1; then block j+1 has landed, P of block j is visible and
   // block j-1's slot, (j + 2) % 3, takes block j + 2.
