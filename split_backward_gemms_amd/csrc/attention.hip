@@ -261,10 +261,22 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
     const int k0 = kb * 64;
     if (k0 <= q_wave_max) {
       f32x16 s[2] = {zero16(), zero16()};
+      // Two independent chains, interleaved; each step's K fragments are
+      // requested one step ahead of their MFMAs.
+      bf16x8 kf[2][2];
+      kf[0][0] = rf.get(sk, 0, 0);
+      kf[0][1] = rf.get(sk, 1, 0);
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk)  // two independent chains, interleaved
+      for (int kk = 0; kk < 8; ++kk) {
+        if (kk + 1 < 8) {
+          kf[(kk + 1) & 1][0] = rf.get(sk, 0, kk + 1);
+          kf[(kk + 1) & 1][1] = rf.get(sk, 1, kk + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) s[b] = mfma(rf.get(sk, b, kk), qf[kk], s[b]);
+        for (int b = 0; b < 2; ++b) s[b] = mfma(kf[kk & 1][b], qf[kk], s[b]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (k0 + 63 > q_wave_min || k0 + 64 > p.seq) {  // diagonal or last block: mask
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -408,10 +420,20 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
 #pragma unroll
       for (int b = 0; b < 2; ++b) {  // two 32-key halves, one at a time
         f32x16 s = zero16(), dp = zero16();
+        // K and V fragments requested one step ahead of their MFMAs.
+        bf16x8 kf[2], vf[2];
+        kf[0] = rf.get(sk, b, 0);
+        vf[0] = rf.get(sv, b, 0);
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-          s = mfma(rf.get(sk, b, kk), qf[kk], s);     // S^T[kv][q]
-          dp = mfma(rf.get(sv, b, kk), dof[kk], dp);  // dP^T[kv][q]
+          if (kk + 1 < 8) {
+            kf[(kk + 1) & 1] = rf.get(sk, b, kk + 1);
+            vf[(kk + 1) & 1] = rf.get(sv, b, kk + 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          s = mfma(kf[kk & 1], qf[kk], s);     // S^T[kv][q]
+          dp = mfma(vf[kk & 1], dof[kk], dp);  // dP^T[kv][q]
+          __builtin_amdgcn_sched_barrier(0);
         }
         if (masked) {  // diagonal or last block (uniform branch: most blocks skip the index math)
 #pragma unroll
@@ -425,15 +447,25 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[r] = exp2_hw(fmaf(s[r], c, -lse)) * (dp[r] - dsum);
         }
-        // dQ^T[d][q] += sum_kv K^T[d][kv] dS^T[kv][q]
+        // dQ^T[d][q] += sum_kv K^T[d][kv] dS^T[kv][q]; the second step's K^T
+        // fragments are requested ahead of the first step's MFMAs.
+        bf16x8 ktf[2][4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) ktf[0][d] = tf.get(sk, d, 2 * b);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
+          if (st == 0) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) ktf[1][d] = tf.get(sk, d, 2 * b + 1);
+          }
           float v[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = s[8 * st + e];
           const bf16x8 f = to_frag(v);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int d = 0; d < 4; ++d) dq[d] = mfma(tf.get(sk, d, 2 * b + st), f, dq[d]);
+          for (int d = 0; d < 4; ++d) dq[d] = mfma(ktf[st][d], f, dq[d]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -546,10 +578,22 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NTP, NTP), amdgpu_wav
     const int q0 = (qb0 + j) * 64;
     const float* sL = reinterpret_cast<const float*>(sLDr + S * 1024);
     f32x16 x[2] = {zero16(), zero16()};
+    // The two halves are independent chains, interleaved; each step's Q
+    // fragments are requested one step ahead of their MFMAs.
+    bf16x8 qfr[2][2];
+    qfr[0][0] = rf.get(s, 0, 0);
+    qfr[0][1] = rf.get(s, 1, 0);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)  // the two halves are independent chains: interleave them
+    for (int kk = 0; kk < 8; ++kk) {
+      if (kk + 1 < 8) {
+        qfr[(kk + 1) & 1][0] = rf.get(s, 0, kk + 1);
+        qfr[(kk + 1) & 1][1] = rf.get(s, 1, kk + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) x[b] = mfma(rf.get(s, b, kk), xf[kk], x[b]);  // S[q][kv]
+      for (int b = 0; b < 2; ++b) x[b] = mfma(qfr[kk & 1][b], xf[kk], x[b]);  // S[q][kv]
+      __builtin_amdgcn_sched_barrier(0);
+    }
     const bool masked = q0 < kv_wave_max || q0 + 64 > p.seq;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -591,10 +635,20 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NTP, NTP), amdgpu_wav
     const char* sg = sGr + S * BLK;
     const float* sD = reinterpret_cast<const float*>(sLDr + S * 1024 + 256);
     f32x16 x[2] = {zero16(), zero16()};
+    bf16x8 gfr[2][2];  // dO fragments, one step ahead as in the S chain
+    gfr[0][0] = rf.get(sg, 0, 0);
+    gfr[0][1] = rf.get(sg, 1, 0);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
+    for (int kk = 0; kk < 8; ++kk) {
+      if (kk + 1 < 8) {
+        gfr[(kk + 1) & 1][0] = rf.get(sg, 0, kk + 1);
+        gfr[(kk + 1) & 1][1] = rf.get(sg, 1, kk + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) x[b] = mfma(rf.get(sg, b, kk), xf[kk], x[b]);  // dP[q][kv]
+      for (int b = 0; b < 2; ++b) x[b] = mfma(gfr[kk & 1][b], xf[kk], x[b]);  // dP[q][kv]
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
