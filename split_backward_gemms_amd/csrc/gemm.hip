@@ -575,6 +575,30 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
     if (t + 2 < nk) body(B2{}, t + 2);
   }
 
+  // The epilogue's residual / pre-activation values (every row of blocks,
+  // 16 bytes per lane: 8 columns) are requested and waited for before the
+  // next tile's first copies go out: vmcnt retires in order, so loads issued
+  // after those copies would wait for the whole ring fill.
+  const int sn = n0 + wn * WTN + 8 * (lane >> 5);  // this lane's stored column, before 32 j + 16 q
+  __amdgpu_buffer_rsrc_t rrsrc = make_rsrc(EPI == EPI_RESID || EPI == EPI_DGELU ? p.R : p.C,
+                                           (uint32_t)(((int64_t)(p.M - 1) * p.ldr + p.N) * 2));
+  u32x4 wr[TM][TN][2];
+  if constexpr (EPI == EPI_RESID || EPI == EPI_DGELU) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int m = em + i * 32, n = sn + j * 32 + 16 * q;
+          const uint32_t roff = (m < p.M && n < p.N) ? (uint32_t)(((int64_t)m * p.ldr + n) * 2) : kOOB;
+          wr[i][j][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rrsrc, (int)roff, 0, 0));
+        }
+  }
+  // s_waitcnt vmcnt(0) as an instruction the compiler tracks (gfx9 encoding; expcnt 7 and lgkmcnt 15
+  // mean no wait on those), so it places no further waits for these loads.
+  if constexpr (EPI == EPI_RESID || EPI == EPI_DGELU) __builtin_amdgcn_s_waitcnt(0x0F70);
+
   // Every wave is past its last read of the ring (and no copy is in flight):
   // the next tile's first copies go out before this tile's epilogue.
   if (has_next) {
@@ -661,8 +685,6 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
       }
     }
   } else {
-    __amdgpu_buffer_rsrc_t rrsrc = make_rsrc(EPI == EPI_RESID || EPI == EPI_DGELU ? p.R : p.C,
-                                             (uint32_t)(((int64_t)(p.M - 1) * p.ldr + p.N) * 2));
     __amdgpu_buffer_rsrc_t zrsrc = make_rsrc(EPI == EPI_GELU ? p.Z : p.C,
                                              (uint32_t)(((int64_t)(p.M - 1) * p.ldz + p.N) * 2));
     // The GeLU form is fixed per launch: one branch here, none per element.
@@ -671,8 +693,6 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
     // v_permlane32_swap gives lane l all eight columns of group 2q and lane
     // l+32 all eight of group 2q+1, so every store is 16 bytes per lane and 32
     // contiguous bytes per row.
-    const int h32 = lane >> 5;
-    const int sn = n0 + wn * WTN + 8 * h32;  // this lane's stored column, before 32 j + 16 q
     auto swap_store = [&](const __amdgpu_buffer_rsrc_t& rs, int64_t ld, int m, int n, u32x2 a, u32x2 b) {
       const auto s0 = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
       const auto s1 = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
@@ -682,24 +702,27 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
     };
     auto store_all = [&](auto kind_c) {
       constexpr int KIND = decltype(kind_c)::value;
-      // One row of 32x32 blocks at a time: its residual / pre-activation
-      // values (TN * 4 8-byte loads per lane) are all requested first, then
-      // used; the barriers keep rows from interleaving (shorter live ranges).
-      // With GeLU the row's pre-activation Z is stored before its activation,
-      // so each buffer's cache lines are completed by consecutive stores
+      // One row of 32x32 blocks at a time, its residual / pre-activation
+      // values already in registers (loaded before the hand-over); the
+      // barriers keep rows from interleaving (shorter live ranges).  With
+      // GeLU the row's pre-activation Z is stored before its activation, so
+      // each buffer's cache lines are completed by consecutive stores
       // (interleaving the two outputs wrote about 1.5x the bytes to memory).
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int m = em + i * 32;
         u32x2 rr[TN][4];
         if constexpr (EPI == EPI_RESID || EPI == EPI_DGELU) {
+          // The inverse of swap_store: lanes l and l + 32 swap halves so that
+          // lane l holds columns 8 g .. 8 g + 3 and lane l + 32 8 g + 4 .. + 7.
 #pragma unroll
           for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int n = en + j * 32 + 8 * g;
-              const uint32_t roff = (m < p.M && n < p.N) ? (uint32_t)(((int64_t)m * p.ldr + n) * 2) : kOOB;
-              rr[j][g] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rrsrc, (int)roff, 0, 0));
+            for (int q = 0; q < 2; ++q) {
+              const auto s = __builtin_amdgcn_permlane32_swap(wr[i][j][q][0], wr[i][j][q][2], false, false);
+              const auto t = __builtin_amdgcn_permlane32_swap(wr[i][j][q][1], wr[i][j][q][3], false, false);
+              rr[j][2 * q] = u32x2{s[0], t[0]};
+              rr[j][2 * q + 1] = u32x2{s[1], t[1]};
             }
         }
         if constexpr (EPI == EPI_GELU) {
