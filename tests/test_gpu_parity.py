@@ -576,6 +576,12 @@ FULL_SIZE = {
     "gpt_full_h4096": si.WORKLOADS["gpt_full_h4096"].replace(n_micro=1, n_stages=1, n_layers=1),
     "gpt_full_h6144": si.WORKLOADS["gpt_full_h6144"].replace(n_micro=1, n_stages=1, n_layers=1),
     "gpt_full_s4096": si.WORKLOADS["gpt_full_s4096"].replace(n_micro=1, n_stages=1, n_layers=1),
+    # ragged T (8 sequences of 1032) and h = 2176 (17 heads): every GEMM of the layer, the
+    # residual ones included, has more output tiles than the chip has CUs, so each epilogue
+    # runs with the workgroup's next tile already in flight
+    "persistent_ragged": si.WORKLOADS["gpt_full_h4096"].replace(
+        name="gpt_full_persistent_ragged", hidden=2176, ffn=4 * 2176, n_heads=17, seq=1032, micro_batch=8,
+        n_micro=1, n_stages=1, n_layers=1),
 }
 
 
