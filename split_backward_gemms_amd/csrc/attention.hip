@@ -84,6 +84,12 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 __device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
 }
+// 4 bytes per lane from rsrc at byte offset off (zero when out of range) into
+// LDS at lds + 4 * lane, lds wave-uniform: each lane's range check covers
+// exactly its own value.  Untracked by the compiler, like dev::dma16.
+__device__ __forceinline__ void dma4(const dev::u32x4& rsrc, uint32_t lds, uint32_t off) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc), "{m0}"(lds) : "memory");
+}
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -495,8 +501,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves
 // =============================================================== dK, dV
 // Workgroup: 128 key rows of one (sequence, head), four 32-key blocks;
 // (Q, dO) blocks of 64 queries, from the first query that can see the keys to
-// the end.  LSE2 and D of a block ride along: lanes 0-15 of one extra copy
-// fetch 64 LSE2 values, lanes 16-31 the 64 D values (the rest read as zero).
+// the end.  LSE2 and D of a block ride along: two more copies of 4 bytes per
+// lane, one row each (rows past the sequence read as zero).
 // Grid (heads x sequences, key blocks), heaviest first: key block 0 sees every
 // query block, and workgroups are handed out with x varying fastest.
 //
@@ -560,11 +566,11 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NTP, NTP), amdgpu_wav
     const int q0 = (qb0 + j) * 64;
     dmq.load(__builtin_amdgcn_readfirstlane(lds_addr(sQr + S * BLK)), base_row + q0, p.seq - q0);
     dmg.load(__builtin_amdgcn_readfirstlane(lds_addr(sGr + S * BLK)), base_row + q0, p.seq - q0);
-    if (w == 0) {
-      const int e = 4 * (lane & 15);
-      const uint32_t off = lane < 32 && q0 + e < p.seq ? (uint32_t)((q0 + e) * 4) : kOOB;
-      if (lane < 16) dma16(uniform4(rl), __builtin_amdgcn_readfirstlane(lds_addr(sLDr + S * 1024)), off);
-      else dma16(uniform4(rd), __builtin_amdgcn_readfirstlane(lds_addr(sLDr + S * 1024)), off);
+    if (w == 0) {  // one value per lane and row: a sequence of any length ends exactly
+      const uint32_t off = q0 + lane < p.seq ? (uint32_t)((q0 + lane) * 4) : kOOB;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(sLDr + S * 1024));
+      dma4(uniform4(rl), dst, off);
+      dma4(uniform4(rd), dst + 256, off);
     }
   };
   // some query of block j sees some key of the wave's block

@@ -305,6 +305,22 @@ def test_pipeline_matches_oracle(name, order):
     _pipeline_vs_oracle(name, order, 0)
 
 
+# Sequence lengths that are not multiples of 8 (only T = seq * micro_batch must be):
+# one token per sequence (softmax over one key), a sequence shorter than a 64-row
+# block, one row short of and one row past a block, and a third 64-row block of
+# a single row; eight sequences per microbatch.
+SHORT_SEQS = {
+    f"full_seq{s}": si.reduced(si.WORKLOADS["gpt_full_h4096"], hidden=256, heads=2, seq=s, n_micro=3,
+                               n_stages=2, n_layers=1).replace(micro_batch=8)
+    for s in (1, 7, 63, 65, 129)
+}
+
+
+@pytest.mark.parametrize("name", list(SHORT_SEQS))
+def test_short_and_odd_sequences_match_oracle(name):
+    _pipeline_vs_oracle_w(SHORT_SEQS[name], "zbh1", 0)
+
+
 # The stash layout that keeps only the MLP pre-activation and rebuilds A = GeLU(Z) for W.
 @pytest.mark.parametrize("name", ["tiny_bf16", "tiny_fp32", "mlp_linears_ragged", "full_reduced",
                                   "full_ragged_two_seqs"])
