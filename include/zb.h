@@ -34,8 +34,8 @@
  *  - On any error the call changes no state and enqueues no work; the text of
  *    the last error of the calling thread is returned by zb_last_error().
  *    Device faults surface as ZB_E_HIP at the next call that synchronises.
- *  - Shapes: hidden, ffn and seq*micro_batch must be multiples of 8; FULL needs
- *    hidden / n_heads == 128.
+ *  - Shapes: hidden, ffn and seq*micro_batch must be multiples of 8 (seq itself
+ *    may be any length from 1); FULL needs hidden / n_heads == 128.
  */
 #ifndef ZB_H
 #define ZB_H
