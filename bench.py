@@ -191,6 +191,51 @@ def counter_run(w0, a) -> int:
     return 0
 
 
+def sustained_run(a) -> int:
+    """One GEMM kind at n x n x n (bf16 operands) for a fixed wall time, back to back on one
+    stream: the library's F (store epilogue), B or W (fp32 accumulate, one launch) through the
+    C ABI, or torch.matmul (hipBLASLt) for reference.  Run beside a clock sampler (amd-smi) it
+    shows the clock the chip sustains under each dense load, and so the peak at that clock."""
+    import torch
+
+    import split_backward_gemms_amd as zb
+
+    n, kind = a.size, a.kind
+    torch.cuda.set_device(0)
+    g = torch.Generator(device="cuda:0").manual_seed(1)
+    x = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    w = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    y = torch.empty(n, n, device="cuda:0", dtype=torch.bfloat16)
+    dw = torch.zeros(n, n, device="cuda:0", dtype=torch.float32) if kind == "W" else None
+
+    def one():
+        if kind == "F":
+            zb.zb_linear_forward(x, w, y)
+        elif kind == "B":
+            zb.zb_linear_backward_input(x, w, y)
+        elif kind == "W":
+            zb.zb_linear_backward_weight(x, w, dw, True)
+        else:
+            torch.matmul(x, w, out=y)
+
+    one()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    calls, t0 = 0, time.perf_counter()
+    e0.record()
+    while time.perf_counter() - t0 < a.seconds:
+        for _ in range(20):
+            one()
+        calls += 20
+        torch.cuda.synchronize()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    print(json.dumps({"mode": "sustained", "kind": kind, "size": n, "calls": calls, "ms_per_call": ms,
+                      "tflops": 2.0 * n ** 3 / (ms * 1e-3) / 1e12}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,10 +250,15 @@ def main() -> int:
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-optim", action="store_true",
                     help="skip timing the optimizer step with post-update validation")
-    ap.add_argument("--mode", choices=["full", "kernels", "counters"], default="full",
+    ap.add_argument("--mode", choices=["full", "kernels", "counters", "sustained"], default="full",
                     help="kernels: only the one-stream kernel-timing phase (the phase a kernel profile covers); "
                          "counters: one full-size stage of the workload with two microbatches (F, F, B, B, W, W), "
-                         "two steps: the same kernels at the same shapes for counter passes, in a few GiB")
+                         "two steps: the same kernels at the same shapes for counter passes, in a few GiB; "
+                         "sustained: one GEMM kind (--kind) back to back for --seconds")
+    ap.add_argument("--kind", choices=["F", "B", "W", "matmul"], default="F",
+                    help="sustained mode: the library's F, B or W GEMM, or torch.matmul (hipBLASLt)")
+    ap.add_argument("--size", type=int, default=8192, help="sustained mode: n of the n x n x n product")
+    ap.add_argument("--seconds", type=float, default=15.0, help="sustained mode: wall time of the loop")
     ap.add_argument("--recompute-act", type=int, choices=[0, 1], default=None,
                     help="stash layout (zb_stage_desc.recompute_act); default: stash A when it fits")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -219,6 +269,11 @@ def main() -> int:
               f"supported (the pipeline stages are emulated on one device, and no run here uses a second GPU).",
               file=sys.stderr)
         return 2
+    if a.mode == "sustained":
+        if a.size < 8 or a.size % 8 or 4.0 * a.size * a.size >= 2147483648.0:
+            print("bench.py: --size must be a multiple of 8 with a dW below 2 GiB", file=sys.stderr)
+            return 2
+        return sustained_run(a)
     if a.calibrate_copy:
         import torch
         n = a.calibrate_copy // 4
