@@ -157,6 +157,65 @@ def roofline_of(kern, workload: str) -> dict:
     return r
 
 
+class ClockSampler:
+    """Samples the GPU's GFX clocks with `amd-smi metric -g 0 -c` (a child process, about three
+    times a second) on a background thread while a timed region runs.  Reports the mean of the
+    per-sample means over the eight XCDs, or None where the tool is missing or prints no clock."""
+
+    def __init__(self):
+        import threading
+
+        self.means, self._stop = [], threading.Event()
+        self._thread = threading.Thread(target=self._loop, daemon=True)
+
+    @staticmethod
+    def _sample():
+        import re
+        import subprocess
+
+        try:
+            out = subprocess.run(["amd-smi", "metric", "-g", "0", "-c"], capture_output=True, text=True,
+                                 timeout=10).stdout
+        except (OSError, subprocess.SubprocessError):
+            return None
+        clocks, in_gfx = [], False
+        for line in out.splitlines():
+            if re.match(r"\s+GFX_\d+:", line):
+                in_gfx = True
+                continue
+            m = re.match(r"\s+CLK: (\d+) MHz", line)
+            if m and in_gfx:
+                clocks.append(int(m.group(1)))
+                in_gfx = False
+            elif re.match(r"\s+[A-Z]+_?\d*:$", line):
+                in_gfx = False
+        return sum(clocks) / len(clocks) if clocks else None
+
+    def _loop(self):
+        while not self._stop.is_set():
+            v = self._sample()
+            if v is None:
+                return
+            self.means.append(v)
+            self._stop.wait(0.2)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=15)
+        return False
+
+    def report(self):
+        if len(self.means) < 3:
+            return None
+        m = self.means[1:]  # the first sample can predate the load
+        return {"mean": sum(m) / len(m), "min_sample": min(m), "max_sample": max(m), "samples": len(m),
+                "source": "amd-smi metric -g 0 -c during the timed steps; mean of the eight XCDs' GFX clocks"}
+
+
 def counter_run(w0, a) -> int:
     """One full-size stage of the workload, two microbatches, two steps, one stream."""
     import torch
@@ -385,8 +444,16 @@ def main() -> int:
     sim_measured = {}
     join = None
     if a.mode == "full":
-        ms_per_step = timed(pipe, ops, a.steps, a.warmup)
+        with ClockSampler() as clk:
+            ms_per_step = timed(pipe, ops, a.steps, a.warmup)
         tflops = flops / (ms_per_step / 1000.0) / 1e12
+        clock = clk.report()
+        out_extra["gfx_clock_mhz"] = clock
+        if clock is not None:
+            # the published bf16 dense peak assumes the 2400 MHz maximum clock
+            at_clock = PEAK_BF16_TFLOPS * clock["mean"] / 2400.0
+            out_extra["bf16_peak_at_sampled_clock_tflops"] = at_clock
+            out_extra["pct_of_bf16_peak_at_sampled_clock"] = 100.0 * tflops / at_clock
         ev_steps = sorted(step_ev_ms)
         out_extra["step_ms_median"] = ev_steps[len(ev_steps) // 2] if ev_steps else None
         out_extra["step_ms_min"] = ev_steps[0] if ev_steps else None
