@@ -19,7 +19,9 @@ width with ragged sequence lengths, through the two-stream executor (stages
 full depth in ZB-H1 with m = 16; one full-size layer of the h = 4096, seq 2048
 workload with two microbatches against the oracle, and the whole full-size
 4-layer stage with two microbatches against the fp32 sum of single-microbatch
-runs (the fp32 accumulation of W across microbatches at full shapes).
+runs (the fp32 accumulation of W across microbatches at full shapes); and at
+P = 8 devices, the orders searched at run time (the automatic scheduler at two
+budgets, the V placement over 16 chunk stages), each bit-identical to 1F1B.
 """
 import numpy as np
 import pytest
@@ -28,7 +30,7 @@ import torch
 import split_backward_gemms_amd as zb
 import synthetic_inputs as si
 from oracle import stage as ost
-from split_backward_gemms_amd.pipeline import EmulatedPipeline, upload
+from split_backward_gemms_amd.pipeline import EmulatedPipeline, heuristic_ops, upload, zbv_ops
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -50,7 +52,7 @@ def _run_tapped(w, order, n_streams):
     ws = [si.stage_weights(w, s) for s in range(w.n_stages)]
     xs = [si.stage_input(w, j) for j in range(w.n_micro)]
     dys = [si.last_stage_grad(w, j) for j in range(w.n_micro)]
-    ops, _ = zb.zb_schedule_build(order, w.n_stages, w.n_micro)
+    ops = zb.zb_schedule_build(order, w.n_stages, w.n_micro)[0] if isinstance(order, str) else order
     pipe = EmulatedPipeline(w, ws, ops=ops, stage_streams=n_streams is not None, n_streams=n_streams,
                             recompute_act=0)
     shape, dt = (w.tokens, w.hidden), torch.bfloat16
@@ -96,10 +98,13 @@ def _stagewise_errors(w, got, ws, xs, dys):
     return errs
 
 
-def _check_stagewise(w, order, n_streams):
+def _check_stagewise(w, order, n_streams, got=None):
     print(f"stagewise {w.name}: P={w.n_stages} m={w.n_micro} L={w.n_layers} h={w.hidden} T={w.tokens} "
-          f"{order} streams={n_streams}", flush=True)
-    got, ws, xs, dys = _run_tapped(w, order, n_streams)
+          f"{order if isinstance(order, str) else 'searched order'} streams={n_streams}", flush=True)
+    if got is None:
+        got, ws, xs, dys = _run_tapped(w, order, n_streams)
+    else:
+        got, ws, xs, dys = got
     # The taps hold exactly what the executor handed on: the last stage's
     # outputs and the first stage's input gradients are the same bits.
     for j in range(w.n_micro):
@@ -287,3 +292,57 @@ def test_debug_sync_mode_runs_clean_and_keeps_bits():
     for s in range(w.n_stages):
         for nm in outs[0][2][s][0]:
             assert np.array_equal(outs[0][2][s][0][nm].view(np.uint32), outs[1][2][s][0][nm].view(np.uint32))
+
+
+def _same_bits(a, b, w):
+    for s in range(w.n_stages):
+        for j in range(w.n_micro):
+            assert np.array_equal(a["y"][s][j], b["y"][s][j]), ("Y", s, j)
+            assert np.array_equal(a["dx"][s][j], b["dx"][s][j]), ("dX", s, j)
+        for l in range(w.n_layers):
+            for nm in a["dw"][s][l]:
+                assert np.array_equal(a["dw"][s][l][nm].view(np.uint32), b["dw"][s][l][nm].view(np.uint32)), \
+                    ("dW", s, l, nm)
+
+
+def _stash_handles(w):
+    """Stage objects of the workload, for the stash sizes the searched orders budget with."""
+    ws = [si.stage_weights(w, s) for s in range(w.n_stages)]
+    return EmulatedPipeline(w, ws, ops=None, recompute_act=0)
+
+
+# The orders searched at run time at the depth of the P = 8 workloads, through
+# the two-stream executor: the automatic scheduler with budgets of P and 2P
+# stashes ("The Heuristic Scheduling Algorithm" of "Zero Bubble Pipeline
+# Parallelism") and the V placement over 2P chunk stages ("Innovation 3: The
+# V-Shaped Interleaving Pattern").  Every stage issues its W passes in
+# ascending microbatch order, so each order gives 1F1B's bits on every stage
+# boundary and in every dW; 1F1B itself is checked stage by stage.
+def test_p8_searched_orders_stagewise_and_1f1b_bits():
+    w = si.reduced(si.WORKLOADS["gpt_full_s4096"], hidden=256, heads=2, seq=136, n_micro=16, n_stages=8,
+                   n_layers=2)
+    ref, ws, xs, dys = _run_tapped(w, "1f1b", 2)
+    _check_stagewise(w, "1f1b", 2, got=(ref, ws, xs, dys))
+    probe = _stash_handles(w)
+    cases = []
+    for budget in (w.n_stages, 2 * w.n_stages):
+        for times in ((1, 1, 1), (2, 3, 1)):
+            ops, stats, choice, _ = heuristic_ops(probe.handles, w.n_stages, w.n_micro, times, budget)
+            assert zb.zb_schedule_validate(w.n_stages, w.n_micro, ops) == (zb.ZB_OK, -1)
+            cases.append((f"budget {budget} times {times} choice {choice} bubble {stats['bubble']}", ops))
+    probe.close()
+    for label, ops in cases:
+        print(f"P=8 searched order: {label}", flush=True)
+        got, _, _, _ = _run_tapped(w, ops, 2)
+        _same_bits(got, ref, w)
+
+    wv = si.v_chunks(w)  # 16 chunk stages of one layer
+    ref_v, ws_v, xs_v, dys_v = _run_tapped(wv, "1f1b", 2)
+    _check_stagewise(wv, "1f1b", 2, got=(ref_v, ws_v, xs_v, dys_v))
+    probe = _stash_handles(wv)
+    ops_v, stats_v, _ = zbv_ops(probe.handles, wv.n_micro, (1, 1, 1))
+    probe.close()
+    assert zb.zb_schedule_validate(wv.n_stages, wv.n_micro, ops_v) == (zb.ZB_OK, -1)
+    print(f"P=8 ZB-V over {wv.n_stages} chunk stages: bubble {stats_v['bubble']}", flush=True)
+    got, _, _, _ = _run_tapped(wv, ops_v, 2)
+    _same_bits(got, ref_v, wv)
