@@ -382,6 +382,10 @@ __device__ __forceinline__ void gemm_tile(const Params& p, int tile, int split, 
                                           char* s3, bool pre, bool has_next, const Params& np, int ntile,
                                           int nsplit) {
   constexpr int WTM = BM / 2, WTN = BN / (WV / 2);  // waves in a 2 x (WV / 2) grid
+  // Fragments alternate between two register buffers over a tile's 16-deep k
+  // steps; the last step's are in buffer 1 while the next tile's first go to
+  // buffer 0, which needs an even number of steps per tile.
+  static_assert(BK % 32 == 0, "k tiles of an even number of 16-deep steps");
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int NS = Ring<BM, BN, OCC, BK>::NS;
   constexpr int AT = BM * BK * 2;  // bytes of the A tile in a ring stage (the B tile follows)
