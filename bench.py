@@ -209,7 +209,7 @@ class ClockSampler:
         return False
 
     def report(self):
-        if len(self.means) < 3:
+        if len(self.means) < 9:  # under ~2 s of samples: too few to stand for the timed region
             return None
         m = self.means[1:]  # the first sample can predate the load
         return {"mean": sum(m) / len(m), "min_sample": min(m), "max_sample": max(m), "samples": len(m),
